@@ -1,0 +1,313 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each test checks the oracle against something fixed by the pages or by mathematics: a brute-force
+sort, the dense-merge form of LoRA the pages compare against, a per-token loop with no grouping,
+fp64 central finite differences, closed forms and invariants, and the page's gate/up order.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+rng0 = np.random.default_rng(1234)
+
+
+def _rand_layer(rng, s, m, n, E, k, r, scale_w=0.3):
+    W = {
+        "W_gu": rng.normal(0, scale_w, (E, m, 2 * n)),
+        "W_d": rng.normal(0, scale_w, (E, n, m)),
+        "A_g": rng.normal(0, 0.5, (E, m, r)), "B_g": rng.normal(0, 0.5, (E, r, n)),
+        "A_u": rng.normal(0, 0.5, (E, m, r)), "B_u": rng.normal(0, 0.5, (E, r, n)),
+        "A_d": rng.normal(0, 0.5, (E, n, r)), "B_d": rng.normal(0, 0.5, (E, r, m)),
+    }
+    X = rng.normal(0, 1, (s, m))
+    W_r = rng.normal(0, 1, (m, E))
+    dY = rng.normal(0, 1, (s, m))
+    return X, W_r, W, dY
+
+
+def _silu(v):
+    return v / (1.0 + np.exp(-v))
+
+
+def _merged(W, e, c):
+    """Dense-merged expert weights W + c * A B (the materialised PEFT form)."""
+    n = W["W_d"].shape[1]
+    Wg = W["W_gu"][e][:, :n] + c * W["A_g"][e] @ W["B_g"][e]
+    Wu = W["W_gu"][e][:, n:] + c * W["A_u"][e] @ W["B_u"][e]
+    Wd = W["W_d"][e] + c * W["A_d"][e] @ W["B_d"][e]
+    return Wg, Wu, Wd
+
+
+def _min_gap(z, k):
+    zs = -np.sort(-z, axis=1)
+    return float(np.min(zs[:, k - 1] - zs[:, k])) if z.shape[1] > k else np.inf
+
+
+# ------------------------------------------------------------------------------- routing
+
+def test_topk_matches_bruteforce_sort():
+    rng = np.random.default_rng(7)
+    z = rng.integers(-2, 3, size=(300, 12)).astype(np.float64)  # many ties
+    k = 5
+    idx = oracle.topk_experts(z, k)
+    for t in range(z.shape[0]):
+        order = sorted(range(z.shape[1]), key=lambda e: (-z[t, e], e))
+        assert list(idx[t]) == order[:k]
+
+
+def test_topk_negative_zero_ties_with_zero():
+    z = np.array([[0.0, -0.0, 1.0, -0.0]])
+    assert list(oracle.topk_experts(z, 3)[0]) == [2, 0, 1]
+
+
+def test_all_equal_logits_pick_first_experts_with_equal_weights():
+    s, E, k = 5, 8, 4
+    z = np.full((s, E), 0.37)
+    rt = oracle.route(z, k, E, "softmax")
+    assert np.all(rt["idx"] == np.arange(k))
+    assert np.all(rt["w"] == 1.0 / k)
+    rt = oracle.route(z, k, E, "sigmoid")
+    assert np.all(rt["w"] == 1.0 / k)
+
+
+def test_k_equals_E_renormalisation_is_identity_for_softmax():
+    rng = np.random.default_rng(3)
+    z = rng.normal(size=(40, 6))
+    rt = oracle.route(z, 6, 6, "softmax")
+    np.testing.assert_allclose(rt["w"], rt["p_sel"], rtol=1e-14, atol=0)
+    # softmax restricted to the k selected logits equals the renormalised weights
+    zs = np.take_along_axis(z, rt["idx"].astype(np.int64), 1)
+    ref = np.exp(zs) / np.exp(zs).sum(1, keepdims=True)
+    np.testing.assert_allclose(rt["w"], ref, rtol=1e-13)
+
+
+def test_sigmoid_scores_closed_form():
+    z = np.array([[0.0, math.log(3.0), -1.0, 2.0]])
+    rt = oracle.route(z, 2, 4, "sigmoid", renormalize=False)
+    assert list(rt["idx"][0]) == [3, 1]
+    np.testing.assert_allclose(rt["w"][0], [1 / (1 + math.exp(-2.0)), 0.75], rtol=1e-15)
+
+
+def test_grouping_invariants():
+    rng = np.random.default_rng(11)
+    s, E, k = 257, 13, 3
+    z = rng.normal(size=(s, E))
+    z[:, 4] -= 10.0  # expert 4 never selected
+    rt = oracle.route(z, k, E)
+    idx, cnt, off, perm, inv = rt["idx"], rt["cnt"], rt["off"], rt["perm"], rt["inv"]
+    P = s * k
+    assert cnt.sum() == P and off[0] == 0 and off[E] == P and cnt[4] == 0
+    assert np.all(np.diff(off) == cnt)
+    assert sorted(perm.tolist()) == list(range(P))
+    for i in range(P):
+        assert inv[perm[i]] == i
+    for e in range(E):
+        rows = perm[off[e]:off[e + 1]]
+        assert all(idx.reshape(-1)[p] == e for p in rows)
+        toks = [p // k for p in rows]
+        assert all(a < b for a, b in zip(toks, toks[1:]))
+    for t in range(s):
+        assert len(set(idx[t].tolist())) == k
+    assert np.max(np.abs(rt["w"].sum(1) - 1.0)) <= k * 2.0 ** -52
+
+
+# ------------------------------------------------------------------------------- forward
+
+def test_gate_up_order_closed_form():
+    fx = json.load(open(os.path.join(GOLDEN, "swiglu_gate_first.json")))
+    m = n = 64
+    r = 8
+    W = {key: np.zeros(shape) for key, shape in
+         (("W_gu", (1, m, 2 * n)), ("W_d", (1, n, m)), ("A_g", (1, m, r)), ("B_g", (1, r, n)),
+          ("A_u", (1, m, r)), ("B_u", (1, r, n)), ("A_d", (1, n, r)), ("B_d", (1, r, m)))}
+    W["W_gu"][0, 0, :n] = fx["gate"]
+    W["W_gu"][0, 0, n:] = fx["up"]
+    W["W_d"][0] = np.eye(n, m)
+    X = np.zeros((1, m))
+    X[0, 0] = 1.0
+    rt = oracle.route(np.zeros((1, 1)), 1, 1)
+    Y, saved = oracle.forward(X, W, rt, alpha=16.0, r=r)
+    np.testing.assert_allclose(saved["h"][0], fx["expected_h"], rtol=1e-15)
+    np.testing.assert_allclose(Y[0, :n], fx["expected_h"], rtol=1e-15)
+
+
+@pytest.mark.parametrize("score", ["softmax", "sigmoid"])
+def test_split_lora_equals_dense_merge_and_per_token_loop(score):
+    """Split LoRA (X W + c (X A) B) against the materialised form X (W + c A B), evaluated one
+    token at a time over its k experts with no grouping (the per-expert loop semantics)."""
+    rng = np.random.default_rng(5)
+    s, m, n, E, k, r, alpha = 37, 16, 8, 5, 2, 3, 6.0
+    X, W_r, W, _ = _rand_layer(rng, s, m, n, E, k, r)
+    c = alpha / r
+    rt = oracle.route(oracle.router_logits(X, W_r), k, E, score)
+    Y, _ = oracle.forward(X, W, rt, alpha, r)
+    ref = np.zeros((s, m))
+    for t in range(s):
+        for j in range(k):
+            Wg, Wu, Wd = _merged(W, int(rt["idx"][t, j]), c)
+            x = X[t]
+            ref[t] += rt["w"][t, j] * ((_silu(x @ Wg) * (x @ Wu)) @ Wd)
+    np.testing.assert_allclose(Y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def test_single_expert_is_a_dense_swiglu_mlp():
+    rng = np.random.default_rng(9)
+    s, m, n, r, alpha = 11, 12, 6, 2, 4.0
+    X, W_r, W, _ = _rand_layer(rng, s, m, n, 1, 1, r)
+    rt = oracle.route(oracle.router_logits(X, W_r), 1, 1)
+    assert np.all(rt["w"] == 1.0)
+    Y, _ = oracle.forward(X, W, rt, alpha, r)
+    Wg, Wu, Wd = _merged(W, 0, alpha / r)
+    np.testing.assert_allclose(Y, (_silu(X @ Wg) * (X @ Wu)) @ Wd, rtol=1e-12, atol=1e-13)
+
+
+def test_alpha_zero_is_plain_moe_and_freezes_lora():
+    rng = np.random.default_rng(10)
+    s, m, n, E, k, r = 20, 8, 4, 4, 2, 2
+    X, W_r, W, dY = _rand_layer(rng, s, m, n, E, k, r)
+    rt = oracle.route(oracle.router_logits(X, W_r), k, E)
+    Y0, sv = oracle.forward(X, W, rt, 0.0, r)
+    Wz = dict(W)
+    for key in ("B_g", "B_u", "B_d"):
+        Wz[key] = np.zeros_like(W[key])
+    Yb, _ = oracle.forward(X, Wz, rt, 5.0, r)
+    np.testing.assert_allclose(Y0, Yb, rtol=1e-14, atol=0)
+    g = oracle.backward(dY, X, W_r, W, rt, 0.0, r, saved=sv)
+    for key in ("dA_g", "dB_g", "dA_u", "dB_u", "dA_d", "dB_d"):
+        assert np.all(g[key] == 0.0)
+
+
+def test_zero_B_gives_zero_dA_but_nonzero_dB():
+    rng = np.random.default_rng(12)
+    s, m, n, E, k, r = 20, 8, 4, 3, 2, 2
+    X, W_r, W, dY = _rand_layer(rng, s, m, n, E, k, r)
+    for key in ("B_g", "B_u", "B_d"):
+        W[key] = np.zeros_like(W[key])
+    rt = oracle.route(oracle.router_logits(X, W_r), k, E)
+    g = oracle.backward(dY, X, W_r, W, rt, 4.0, r)
+    for key in ("dA_g", "dA_u", "dA_d"):
+        assert np.all(g[key] == 0.0)
+    for key in ("dB_g", "dB_u", "dB_d"):
+        assert np.abs(g[key]).max() > 1e-3
+
+
+def test_zero_token_expert_has_exact_zero_gradients():
+    rng = np.random.default_rng(13)
+    s, m, n, E, k, r = 30, 8, 4, 5, 2, 2
+    X, W_r, W, dY = _rand_layer(rng, s, m, n, E, k, r)
+    z = oracle.router_logits(X, W_r)
+    z[:, 2] = -1e3
+    rt = oracle.route(z, k, E)
+    assert rt["cnt"][2] == 0
+    g = oracle.backward(dY, X, W_r, W, rt, 2.0, r)
+    for key in ("dA_g", "dB_g", "dA_u", "dB_u", "dA_d", "dB_d"):
+        assert np.all(g[key][2] == 0.0)
+
+
+# ------------------------------------------------------------------------------- backward
+
+def _loss(X, W_r, W, dY, k, E, alpha, r, score, renorm, frozen_rt=None):
+    rt = frozen_rt if frozen_rt is not None else oracle.route(oracle.router_logits(X, W_r), k, E,
+                                                               score, renorm)
+    Y, _ = oracle.forward(X, W, rt, alpha, r, keep=False)
+    return float(np.sum(dY * Y)), rt
+
+
+@pytest.mark.parametrize("score,renorm", [("softmax", True), ("sigmoid", True), ("sigmoid", False)])
+def test_gradients_match_central_finite_differences(score, renorm):
+    rng = np.random.default_rng(21)
+    s, m, n, E, k, r, alpha = 6, 8, 4, 4, 2, 2, 3.0
+    for _ in range(50):
+        X, W_r, W, dY = _rand_layer(rng, s, m, n, E, k, r)
+        if _min_gap(oracle.router_logits(X, W_r), k) > 1e-2:
+            break
+    base_rt = oracle.route(oracle.router_logits(X, W_r), k, E, score, renorm)
+    g = oracle.backward(dY, X, W_r, W, base_rt, alpha, r, score, renorm, router_grad=True)
+    g0 = oracle.backward(dY, X, W_r, W, base_rt, alpha, r, score, renorm, router_grad=False)
+    h = 1e-6
+
+    def fd(arr, frozen):
+        out = np.zeros_like(arr)
+        for i in np.ndindex(arr.shape):
+            old = arr[i]
+            arr[i] = old + h
+            lp, rtp = _loss(X, W_r, W, dY, k, E, alpha, r, score, renorm, frozen)
+            arr[i] = old - h
+            lm, rtm = _loss(X, W_r, W, dY, k, E, alpha, r, score, renorm, frozen)
+            arr[i] = old
+            if frozen is None:
+                assert np.array_equal(rtp["idx"], base_rt["idx"])
+                assert np.array_equal(rtm["idx"], base_rt["idx"])
+            out[i] = (lp - lm) / (2 * h)
+        return out
+
+    def close(a, b):
+        return np.max(np.abs(a - b)) <= 1e-6 * max(np.max(np.abs(b)), 1e-3)
+
+    assert close(g["dX"], fd(X, None)), "dX with the router path"
+    assert close(g0["dX"], fd(X, base_rt)), "dX through the experts only"
+    for key in ("A_g", "B_g", "A_u", "B_u", "A_d", "B_d"):
+        assert close(g["d" + key], fd(W[key], base_rt)), key
+
+
+def test_lora_grads_equal_projected_dense_weight_gradient():
+    """With W' = W + c A B, dA = c (dL/dW') B^T and dB = c A^T (dL/dW'); dL/dW' = X_e^T dG_e."""
+    rng = np.random.default_rng(31)
+    s, m, n, E, k, r, alpha = 25, 8, 6, 3, 2, 2, 5.0
+    c = alpha / r
+    X, W_r, W, dY = _rand_layer(rng, s, m, n, E, k, r)
+    rt = oracle.route(oracle.router_logits(X, W_r), k, E)
+    g = oracle.backward(dY, X, W_r, W, rt, alpha, r)
+    Xp = X[rt["perm"] // k]
+    tok, slot = rt["perm"] // k, rt["perm"] % k
+    dO = rt["w"][tok, slot][:, None] * dY[tok]
+    for e in range(E):
+        a, b = rt["off"][e], rt["off"][e + 1]
+        ew = oracle._expert(W, e)
+        f = oracle.expert_rows_forward(Xp[a:b], ew, c)
+        res = oracle.expert_rows_backward(Xp[a:b], dO[a:b], ew, c, f)
+        dWg = Xp[a:b].T @ res["dg"]
+        dWd = f["h"].T @ dO[a:b]
+        np.testing.assert_allclose(g["dA_g"][e], c * dWg @ W["B_g"][e].T, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(g["dB_g"][e], c * W["A_g"][e].T @ dWg, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(g["dA_d"][e], c * dWd @ W["B_d"][e].T, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(g["dB_d"][e], c * W["A_d"][e].T @ dWd, rtol=1e-12, atol=1e-14)
+
+
+def test_softmax_router_gradient_sums_to_zero_per_token():
+    rng = np.random.default_rng(41)
+    s, m, n, E, k, r = 40, 8, 4, 6, 3, 2
+    X, W_r, W, dY = _rand_layer(rng, s, m, n, E, k, r)
+    rt = oracle.route(oracle.router_logits(X, W_r), k, E)
+    g = oracle.backward(dY, X, W_r, W, rt, 2.0, r)
+    assert np.max(np.abs(g["dz"].sum(1))) <= 1e-14 * np.abs(g["dz"]).max() * k
+
+
+# ------------------------------------------------------------------------------- sampled outputs
+
+def test_sampled_outputs_equal_full_layer():
+    rng = np.random.default_rng(51)
+    s, m, n, E, k, r, alpha = 30, 8, 4, 5, 2, 2, 4.0
+    X, W_r, W, dY = _rand_layer(rng, s, m, n, E, k, r)
+    for score in ("softmax", "sigmoid"):
+        rt = oracle.route(oracle.router_logits(X, W_r), k, E, score)
+        Y, sv = oracle.forward(X, W, rt, alpha, r)
+        g = oracle.backward(dY, X, W_r, W, rt, alpha, r, score, True, True, sv)
+        toks = [0, 7, 29]
+        np.testing.assert_allclose(oracle.forward_tokens(toks, X, W, rt, alpha, r), Y[toks],
+                                   rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(
+            oracle.backward_tokens(toks, dY, X, W_r, W, rt, alpha, r, score), g["dX"][toks],
+            rtol=1e-12, atol=1e-14)
+        for e in range(E):
+            ge = oracle.backward_expert(e, dY, X, W, rt, alpha, r)
+            for key, v in ge.items():
+                np.testing.assert_allclose(v, g[key][e], rtol=1e-12, atol=1e-14)
