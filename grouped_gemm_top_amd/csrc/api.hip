@@ -1,0 +1,472 @@
+// C ABI of libmoelora: argument checks, buffer layout and the launch sequence of the MoE-LoRA
+// layer (routing, forward, backward). See include/moelora.h for the contract of each call.
+#include <cmath>
+#include <cstring>
+
+#include "../../include/moelora.h"
+#include "gemm.h"
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int kTileIdxForMFMA = 2;  // row tile 128 (kTileSizes[2])
+
+// Bump allocator over a caller buffer; with base == nullptr it only measures.
+struct Carve {
+  char* base;
+  size_t off = 0;
+  explicit Carve(void* b) : base((char*)b) {}
+  template <typename T> T* take(size_t count) {
+    off = align_up(off, 256);
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+  void* bytes(size_t n) { return take<char>(n); }
+};
+
+struct RouteState {
+  float* logits;
+  float* psel;
+  int* row_tok;
+  int* rank;
+  int* blk_hist;
+  int* blk_base;
+  int* tiles;
+};
+
+struct FwdBufs {
+  void *Xp, *gu, *h, *Tgu, *Td, *o;
+};
+
+struct BwdBufs {
+  void* dO;
+  float* ds;
+  float* dz;
+  void* WrT;
+  void *Ud, *dgu, *Ugu, *dXp;
+};
+
+inline size_t esize(const moe_shape& s) { return s.dtype == MOE_DTYPE_BF16 ? 2 : 4; }
+inline long pairs(const moe_shape& s) { return (long)s.s * s.k; }
+inline int nblocks(const moe_shape& s) { return (s.s + kRouteBlockTokens - 1) / kRouteBlockTokens; }
+
+size_t route_layout(const moe_shape& s, void* base, RouteState* rs) {
+  Carve c(base);
+  const long P = pairs(s);
+  const int nb = nblocks(s);
+  RouteState r;
+  r.logits = c.take<float>((size_t)s.s * s.E);
+  r.psel = c.take<float>((size_t)P);
+  r.row_tok = c.take<int>((size_t)P);
+  r.rank = c.take<int>((size_t)P);
+  r.blk_hist = c.take<int>((size_t)nb * s.E);
+  r.blk_base = c.take<int>((size_t)nb * s.E);
+  r.tiles = c.take<int>((size_t)kNumTileSizes * (s.E + 1));
+  if (rs) *rs = r;
+  return align_up(c.off, 256);
+}
+
+size_t fwd_layout(const moe_shape& s, void* base, FwdBufs* fb) {
+  Carve c(base);
+  const size_t P = (size_t)pairs(s), es = esize(s);
+  FwdBufs f;
+  f.Xp = c.bytes(P * s.m * es);
+  f.gu = c.bytes(P * 2 * s.n * es);
+  f.h = c.bytes(P * s.n * es);
+  f.Tgu = c.bytes(P * 2 * s.r * es);
+  f.Td = c.bytes(P * s.r * es);
+  f.o = c.bytes(P * s.m * es);
+  if (fb) *fb = f;
+  return align_up(c.off, 256);
+}
+
+size_t bwd_layout(const moe_shape& s, void* base, BwdBufs* bb) {
+  Carve c(base);
+  const size_t P = (size_t)pairs(s), es = esize(s);
+  BwdBufs b;
+  b.dO = c.bytes(P * s.m * es);
+  b.ds = c.take<float>(P);
+  b.dz = c.take<float>(P);
+  b.WrT = c.bytes((size_t)s.E * s.m * es);
+  b.Ud = c.bytes(P * s.r * es);
+  b.dgu = c.bytes(P * 2 * s.n * es);
+  b.Ugu = c.bytes(P * 2 * s.r * es);
+  b.dXp = c.bytes(P * s.m * es);
+  if (bb) *bb = b;
+  return align_up(c.off, 256);
+}
+
+moe_status check_shape(const moe_shape* sp) {
+  if (!sp) return MOE_ERR_INVALID_ARG;
+  const moe_shape& s = *sp;
+  if (s.s < 0 || s.m <= 0 || s.n <= 0 || s.E <= 0 || s.k <= 0 || s.r <= 0) return MOE_ERR_INVALID_ARG;
+  if (s.k > s.E) return MOE_ERR_INVALID_ARG;
+  if (s.dtype != MOE_DTYPE_F32 && s.dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
+  if (s.score != MOE_SCORE_SOFTMAX && s.score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if ((s.renormalize != 0 && s.renormalize != 1) || (s.router_grad != 0 && s.router_grad != 1))
+    return MOE_ERR_INVALID_ARG;
+  if (s.flags & ~MOE_FLAG_REFERENCE_GEMM) return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(s.alpha)) return MOE_ERR_INVALID_ARG;
+  if (s.m % 64 || s.n % 64) return MOE_ERR_UNSUPPORTED;
+  if (s.E > 1024 || s.r > 64) return MOE_ERR_UNSUPPORTED;
+  if (s.dtype == MOE_DTYPE_BF16 && (s.r % 8 || s.E % 8)) return MOE_ERR_UNSUPPORTED;
+  const long wide = s.m > 2L * s.n ? s.m : 2L * s.n;
+  if ((long)s.s * s.k * wide >= (1L << 31)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// A device pointer argument holding `count` elements: required and 16-byte aligned when count > 0.
+inline bool ptr_ok(const void* p, size_t count) {
+  if (count == 0) return true;
+  return p != nullptr && ((uintptr_t)p & 15u) == 0;
+}
+
+#define HIP_TRY(x)                           \
+  do {                                       \
+    if ((x) != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+
+GemmArgs gemm_args() {
+  GemmArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.scale = 1.0f;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(moe_status st) {
+  switch (st) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+int32_t moe_abi_version(void) { return 1; }
+
+moe_status moe_check_shape(const moe_shape* shape) { return check_shape(shape); }
+
+size_t moe_route_state_bytes(const moe_shape* shape) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  return route_layout(*shape, nullptr, nullptr);
+}
+
+size_t moe_fwd_saved_bytes(const moe_shape* shape) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  return fwd_layout(*shape, nullptr, nullptr);
+}
+
+size_t moe_fwd_ws_bytes(const moe_shape* shape, int32_t with_saved) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  return with_saved ? 0 : fwd_layout(*shape, nullptr, nullptr);
+}
+
+size_t moe_bwd_ws_bytes(const moe_shape* shape) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  return bwd_layout(*shape, nullptr, nullptr);
+}
+
+moe_status moe_route(const moe_shape* shape, const void* X, const void* W_r,
+                     const float* router_bias, float* logits, int32_t* topk_idx, float* topk_w,
+                     int32_t* expert_off, int32_t* perm, int32_t* inv_perm, void* route_state,
+                     size_t route_state_bytes, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape& s = *shape;
+  const long P = pairs(s);
+  if (!ptr_ok(X, (size_t)s.s * s.m) || !ptr_ok(W_r, (size_t)s.m * s.E) ||
+      !ptr_ok(topk_idx, P) || !ptr_ok(topk_w, P) || !ptr_ok(expert_off, s.E + 1) ||
+      !ptr_ok(perm, P) || !ptr_ok(inv_perm, P))
+    return MOE_ERR_INVALID_ARG;
+  if ((router_bias && ((uintptr_t)router_bias & 15u)) || (logits && ((uintptr_t)logits & 15u)))
+    return MOE_ERR_INVALID_ARG;
+  const size_t need = route_layout(s, nullptr, nullptr);
+  if (!route_state || ((uintptr_t)route_state & 255u)) return MOE_ERR_INVALID_ARG;
+  if (route_state_bytes < need) return MOE_ERR_WORKSPACE;
+  hipStream_t hs = (hipStream_t)stream;
+  RouteState rs;
+  route_layout(s, route_state, &rs);
+  if (s.s == 0) {
+    HIP_TRY(launch_zero(expert_off, s.E + 1, hs));
+    HIP_TRY(launch_zero(rs.tiles, (size_t)kNumTileSizes * (s.E + 1), hs));
+    return MOE_OK;
+  }
+  float* z = logits ? logits : rs.logits;
+  GemmArgs a = gemm_args();
+  a.M = s.s;
+  a.N = s.E;
+  a.K = s.m;
+  a.G = 1;
+  a.A = X;
+  a.lda = s.m;
+  a.B = W_r;
+  a.ldb = s.E;
+  a.C = z;
+  a.ldc = s.E;
+  a.bias = router_bias;
+  const int ref = (s.flags & MOE_FLAG_REFERENCE_GEMM) ? 1 : 0;
+  HIP_TRY(gemm_gm_launch(a, LAYOUT_KX, EPI_STORE, 1, s.dtype, s.s, ref, hs));
+  HIP_TRY(launch_topk(z, s.s, s.E, s.k, s.score, s.renormalize, topk_idx, topk_w, rs.psel, hs));
+  HIP_TRY(launch_hist_rank(topk_idx, s.s, s.k, s.E, rs.blk_hist, rs.rank, hs));
+  HIP_TRY(launch_scan(rs.blk_hist, nblocks(s), s.E, (int)P, rs.blk_base, expert_off, rs.tiles, hs));
+  HIP_TRY(launch_scatter(topk_idx, rs.rank, rs.blk_base, s.s, s.k, s.E, perm, inv_perm, rs.row_tok, hs));
+  return MOE_OK;
+}
+
+moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t* topk_idx,
+                            const float* topk_w, const int32_t* expert_off, const int32_t* perm,
+                            const int32_t* inv_perm, const void* route_state, const void* W_gu,
+                            const void* W_d, const void* A_g, const void* B_g, const void* A_u,
+                            const void* B_u, const void* A_d, const void* B_d, void* Y, void* saved,
+                            size_t saved_bytes, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape& s = *shape;
+  const long P = pairs(s);
+  const size_t E = s.E, m = s.m, n = s.n, r = s.r;
+  if (!ptr_ok(X, (size_t)s.s * m) || !ptr_ok(topk_idx, P) || !ptr_ok(topk_w, P) ||
+      !ptr_ok(expert_off, E + 1) || !ptr_ok(perm, P) || !ptr_ok(inv_perm, P) ||
+      !ptr_ok(W_gu, E * m * 2 * n) || !ptr_ok(W_d, E * n * m) || !ptr_ok(A_g, E * m * r) ||
+      !ptr_ok(B_g, E * r * n) || !ptr_ok(A_u, E * m * r) || !ptr_ok(B_u, E * r * n) ||
+      !ptr_ok(A_d, E * n * r) || !ptr_ok(B_d, E * r * m) || !ptr_ok(Y, (size_t)s.s * m))
+    return MOE_ERR_INVALID_ARG;
+  if (!route_state || ((uintptr_t)route_state & 255u)) return MOE_ERR_INVALID_ARG;
+  const size_t need_saved = fwd_layout(s, nullptr, nullptr);
+  void* inter = saved;
+  if (saved) {
+    if ((uintptr_t)saved & 255u) return MOE_ERR_INVALID_ARG;
+    if (saved_bytes < need_saved) return MOE_ERR_WORKSPACE;
+  } else {
+    if (ws_bytes < need_saved) return MOE_ERR_WORKSPACE;
+    if (need_saved && (!ws || ((uintptr_t)ws & 255u))) return MOE_ERR_INVALID_ARG;
+    inter = ws;
+  }
+  if (s.s == 0) return MOE_OK;
+  hipStream_t hs = (hipStream_t)stream;
+  RouteState rs;
+  route_layout(s, const_cast<void*>(route_state), &rs);
+  FwdBufs f;
+  fwd_layout(s, inter, &f);
+  const int ref = (s.flags & MOE_FLAG_REFERENCE_GEMM) ? 1 : 0;
+  const float c = s.alpha / (float)s.r;
+  const int Pi = (int)P;
+
+  // permute: Xp[row] = X[perm[row] / k]
+  HIP_TRY(launch_gather_rows(s.dtype, X, f.Xp, perm, s.k, Pi, s.m, hs));
+
+  GemmArgs base = gemm_args();
+  base.G = s.E;
+  base.goff = expert_off;
+  base.toff_all = rs.tiles;
+
+  // Tc_gu = c * Xp [A_g | A_u]
+  {
+    GemmArgs a = base;
+    a.N = s.r; a.K = s.m;
+    a.A = f.Xp; a.lda = s.m;
+    a.B = A_g; a.Bu = A_u; a.ldb = s.r; a.bstride = (long)m * r;
+    a.C = f.Tgu; a.ldc = 2 * s.r; a.cup = s.r; a.scale = c;
+    HIP_TRY(gemm_gm_launch(a, LAYOUT_KX, EPI_DUAL, 0, s.dtype, Pi, ref, hs));
+  }
+  // [g | u] = Xp W_gu + [Tc_g B_g | Tc_u B_u];  h = silu(g) * u
+  {
+    GemmArgs a = base;
+    a.N = s.n; a.K = s.m;
+    a.A = f.Xp; a.lda = s.m;
+    a.B = W_gu; a.Bu = (const char*)W_gu + n * esize(s); a.ldb = 2 * s.n; a.bstride = (long)m * 2 * n;
+    a.tail = TAIL_BLOCKDIAG; a.r2a = s.r;
+    a.TA = f.Tgu; a.lda2 = 2 * s.r;
+    a.TB0 = B_g; a.TB1 = B_u; a.ldtb = s.n; a.tbstride = (long)r * n;
+    a.C = f.gu; a.ldc = 2 * s.n; a.cup = s.n;
+    a.H = f.h; a.ldh = s.n;
+    HIP_TRY(gemm_gm_launch(a, LAYOUT_KX, EPI_SWIGLU, 0, s.dtype, Pi, ref, hs));
+  }
+  // Tc_d = c * h A_d
+  {
+    GemmArgs a = base;
+    a.N = s.r; a.K = s.n;
+    a.A = f.h; a.lda = s.n;
+    a.B = A_d; a.ldb = s.r; a.bstride = (long)n * r;
+    a.C = f.Td; a.ldc = s.r; a.scale = c;
+    HIP_TRY(gemm_gm_launch(a, LAYOUT_KX, EPI_STORE, 0, s.dtype, Pi, ref, hs));
+  }
+  // o = h W_d + Tc_d B_d
+  {
+    GemmArgs a = base;
+    a.N = s.m; a.K = s.n;
+    a.A = f.h; a.lda = s.n;
+    a.B = W_d; a.ldb = s.m; a.bstride = (long)n * m;
+    a.tail = TAIL_SINGLE; a.r2a = s.r;
+    a.TA = f.Td; a.lda2 = s.r;
+    a.TB0 = B_d; a.ldtb = s.m; a.tbstride = (long)r * m;
+    a.C = f.o; a.ldc = s.m;
+    HIP_TRY(gemm_gm_launch(a, LAYOUT_KX, EPI_STORE, 0, s.dtype, Pi, ref, hs));
+  }
+  // combine
+  HIP_TRY(launch_combine(s.dtype, f.o, inv_perm, topk_w, Y, s.s, s.k, s.m, hs));
+  return MOE_OK;
+}
+
+moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void* X,
+                             const void* W_r, const int32_t* topk_idx, const float* topk_w,
+                             const int32_t* expert_off, const int32_t* perm,
+                             const int32_t* inv_perm, const void* route_state, const void* W_gu,
+                             const void* W_d, const void* A_g, const void* B_g, const void* A_u,
+                             const void* B_u, const void* A_d, const void* B_d, const void* saved,
+                             size_t saved_bytes, void* dX, float* dA_g, float* dB_g, float* dA_u,
+                             float* dB_u, float* dA_d, float* dB_d, void* ws, size_t ws_bytes,
+                             void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape& s = *shape;
+  if (s.router_grad && s.score == MOE_SCORE_SOFTMAX && !s.renormalize) return MOE_ERR_UNSUPPORTED;
+  const long P = pairs(s);
+  const size_t E = s.E, m = s.m, n = s.n, r = s.r;
+  if (!ptr_ok(dY, (size_t)s.s * m) || !ptr_ok(X, (size_t)s.s * m) || !ptr_ok(W_r, m * E) ||
+      !ptr_ok(topk_idx, P) || !ptr_ok(topk_w, P) || !ptr_ok(expert_off, E + 1) ||
+      !ptr_ok(perm, P) || !ptr_ok(inv_perm, P) || !ptr_ok(W_gu, E * m * 2 * n) ||
+      !ptr_ok(W_d, E * n * m) || !ptr_ok(A_g, E * m * r) || !ptr_ok(B_g, E * r * n) ||
+      !ptr_ok(A_u, E * m * r) || !ptr_ok(B_u, E * r * n) || !ptr_ok(A_d, E * n * r) ||
+      !ptr_ok(B_d, E * r * m) || !ptr_ok(dX, (size_t)s.s * m) || !ptr_ok(dA_g, E * m * r) ||
+      !ptr_ok(dB_g, E * r * n) || !ptr_ok(dA_u, E * m * r) || !ptr_ok(dB_u, E * r * n) ||
+      !ptr_ok(dA_d, E * n * r) || !ptr_ok(dB_d, E * r * m))
+    return MOE_ERR_INVALID_ARG;
+  if (!route_state || ((uintptr_t)route_state & 255u)) return MOE_ERR_INVALID_ARG;
+  if (!saved || ((uintptr_t)saved & 255u)) return MOE_ERR_INVALID_ARG;
+  if (saved_bytes < fwd_layout(s, nullptr, nullptr)) return MOE_ERR_WORKSPACE;
+  const size_t need_ws = bwd_layout(s, nullptr, nullptr);
+  if (ws_bytes < need_ws) return MOE_ERR_WORKSPACE;
+  if (!ws || ((uintptr_t)ws & 255u)) return MOE_ERR_INVALID_ARG;
+  hipStream_t hs = (hipStream_t)stream;
+  if (s.s == 0) {
+    HIP_TRY(launch_zero(dA_g, E * m * r, hs));
+    HIP_TRY(launch_zero(dA_u, E * m * r, hs));
+    HIP_TRY(launch_zero(dB_g, E * r * n, hs));
+    HIP_TRY(launch_zero(dB_u, E * r * n, hs));
+    HIP_TRY(launch_zero(dA_d, E * n * r, hs));
+    HIP_TRY(launch_zero(dB_d, E * r * m, hs));
+    return MOE_OK;
+  }
+  RouteState rs;
+  route_layout(s, const_cast<void*>(route_state), &rs);
+  FwdBufs f;
+  fwd_layout(s, const_cast<void*>(saved), &f);
+  BwdBufs b;
+  bwd_layout(s, ws, &b);
+  const int ref = (s.flags & MOE_FLAG_REFERENCE_GEMM) ? 1 : 0;
+  const float c = s.alpha / (float)s.r;
+  const int Pi = (int)P;
+  const size_t es = esize(s);
+
+  // combine backward: dO = s_{t,j} dY_t, ds_{t,j} = dY_t . o_{t,j}
+  HIP_TRY(launch_combine_bwd(s.dtype, dY, f.o, perm, topk_w, b.dO, b.ds, Pi, s.k, s.m, hs));
+  // router backward: dz on the selected logits; W_r^T rows for the unpermute
+  if (s.router_grad) {
+    HIP_TRY(launch_router_bwd(b.ds, topk_w, rs.psel, s.s, s.k, s.score, s.renormalize, b.dz, hs));
+    HIP_TRY(launch_transpose(s.dtype, W_r, b.WrT, s.m, s.E, hs));
+  }
+
+  GemmArgs base = gemm_args();
+  base.G = s.E;
+  base.goff = expert_off;
+  base.toff_all = rs.tiles;
+
+  // Uc_d = c * dO B_d^T
+  {
+    GemmArgs a = base;
+    a.N = s.r; a.K = s.m;
+    a.A = b.dO; a.lda = s.m;
+    a.B = B_d; a.ldb = s.m; a.bstride = (long)r * m;
+    a.C = b.Ud; a.ldc = s.r; a.scale = c;
+    HIP_TRY(gemm_gm_launch(a, LAYOUT_XK, EPI_STORE, 0, s.dtype, Pi, ref, hs));
+  }
+  // dh = dO W_d^T + Uc_d A_d^T, then SwiGLU backward -> dgu = [dg | du]
+  {
+    GemmArgs a = base;
+    a.N = s.n; a.K = s.m;
+    a.A = b.dO; a.lda = s.m;
+    a.B = W_d; a.ldb = s.m; a.bstride = (long)n * m;
+    a.tail = TAIL_SINGLE; a.r2a = s.r;
+    a.TA = b.Ud; a.lda2 = s.r;
+    a.TB0 = A_d; a.ldtb = s.r; a.tbstride = (long)n * r;
+    a.GU = f.gu; a.ldgu = 2 * s.n; a.guup = s.n;
+    a.C = b.dgu; a.ldc = 2 * s.n; a.cup = s.n;
+    HIP_TRY(gemm_gm_launch(a, LAYOUT_XK, EPI_SWIGLU_BWD, 0, s.dtype, Pi, ref, hs));
+  }
+  // dA_d = h^T Uc_d ;  dB_d = Tc_d^T dO  (computed as (dO^T Tc_d)^T)
+  {
+    GemmArgs a = base;
+    a.toff_all = nullptr;
+    a.M = s.n; a.N = s.r;
+    a.A = f.h; a.lda = s.n;
+    a.B = b.Ud; a.ldb = s.r;
+    a.C = dA_d; a.ldc = s.r; a.cstride = (long)n * r;
+    HIP_TRY(gemm_gk_launch(a, s.dtype, ref, hs));
+    a.M = s.m; a.N = s.r;
+    a.A = b.dO; a.lda = s.m;
+    a.B = f.Td; a.ldb = s.r;
+    a.C = dB_d; a.ldc = s.m; a.cstride = (long)r * m; a.ctrans = 1;
+    HIP_TRY(gemm_gk_launch(a, s.dtype, ref, hs));
+  }
+  // Uc_gu = c * [dg B_g^T | du B_u^T]
+  {
+    GemmArgs a = base;
+    a.N = s.r; a.K = s.n;
+    a.A = b.dgu; a.lda = 2 * s.n;
+    a.B = B_g; a.ldb = s.n; a.bstride = (long)r * n;
+    a.C = b.Ugu; a.ldc = 2 * s.r; a.scale = c;
+    HIP_TRY(gemm_gm_launch(a, LAYOUT_XK, EPI_STORE, 0, s.dtype, Pi, ref, hs));
+    a.A = (const char*)b.dgu + n * es;
+    a.B = B_u;
+    a.C = (char*)b.Ugu + r * es;
+    HIP_TRY(gemm_gm_launch(a, LAYOUT_XK, EPI_STORE, 0, s.dtype, Pi, ref, hs));
+  }
+  // dXp = dgu W_gu^T + Uc_g A_g^T + Uc_u A_u^T
+  {
+    GemmArgs a = base;
+    a.N = s.m; a.K = 2 * s.n;
+    a.A = b.dgu; a.lda = 2 * s.n;
+    a.B = W_gu; a.ldb = 2 * s.n; a.bstride = (long)m * 2 * n;
+    a.tail = TAIL_STACKED; a.r2a = s.r;
+    a.TA = b.Ugu; a.lda2 = 2 * s.r;
+    a.TB0 = A_g; a.TB1 = A_u; a.ldtb = s.r; a.tbstride = (long)m * r;
+    a.C = b.dXp; a.ldc = s.m;
+    HIP_TRY(gemm_gm_launch(a, LAYOUT_XK, EPI_STORE, 0, s.dtype, Pi, ref, hs));
+  }
+  // dA_g | dA_u = Xp^T [Uc_g | Uc_u] ;  dB_g = Tc_g^T dg, dB_u = Tc_u^T du
+  {
+    GemmArgs a = base;
+    a.toff_all = nullptr;
+    a.M = s.m; a.N = 2 * s.r;
+    a.A = f.Xp; a.lda = s.m;
+    a.B = b.Ugu; a.ldb = 2 * s.r;
+    a.C = dA_g; a.C1 = dA_u; a.nsplit = s.r; a.ldc = s.r; a.cstride = (long)m * r;
+    HIP_TRY(gemm_gk_launch(a, s.dtype, ref, hs));
+    GemmArgs bg = base;
+    bg.toff_all = nullptr;
+    bg.M = s.n; bg.N = s.r;
+    bg.A = b.dgu; bg.lda = 2 * s.n;
+    bg.B = f.Tgu; bg.ldb = 2 * s.r;
+    bg.C = dB_g; bg.ldc = s.n; bg.cstride = (long)r * n; bg.ctrans = 1;
+    HIP_TRY(gemm_gk_launch(bg, s.dtype, ref, hs));
+    bg.A = (const char*)b.dgu + n * es;
+    bg.B = (const char*)f.Tgu + r * es;
+    bg.C = dB_u;
+    HIP_TRY(gemm_gk_launch(bg, s.dtype, ref, hs));
+  }
+  // unpermute: dX[t] = sum_j dXp[inv[t k + j]] (+ sum_j dz[t,j] W_r[:, idx[t,j]])
+  HIP_TRY(launch_unpermute(s.dtype, b.dXp, inv_perm, s.router_grad ? b.dz : nullptr, topk_idx,
+                           b.WrT, dX, s.s, s.k, s.m, hs));
+  return MOE_OK;
+}
+
+}  // extern "C"

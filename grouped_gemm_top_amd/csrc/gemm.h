@@ -1,0 +1,91 @@
+// Grouped GEMM descriptions shared by the MFMA kernels and the plain SIMT kernels.
+//
+// Two problem kinds:
+//  * row-grouped ("GM"): the rows of the output are split into expert groups
+//    [goff[e], goff[e+1]); group e computes C[rows_e, :] = A[rows_e, :] . B_e  (+ a LoRA tail
+//    A2[rows_e, :] . B2_e), followed by an epilogue. K is shared by all groups.
+//  * K-grouped ("GK"): group e computes C_e = scale * L[rows_e, :]^T . R[rows_e, :]; the group
+//    rows are the reduction axis (LoRA-factor gradients).
+#pragma once
+#include "common.h"
+
+namespace moe {
+
+// Operand storage: element (x, kk) of an operand, x the output-side index, kk the reduction index.
+enum OperandLayout : int {
+  LAYOUT_XK = 0,  // base[x * ld + kk]   (reduction axis contiguous)
+  LAYOUT_KX = 1,  // base[kk * ld + x]   (output axis contiguous)
+};
+
+enum Epilogue : int {
+  EPI_STORE = 0,       // C = scale * acc (+ bias[col])
+  EPI_DUAL = 1,        // two column halves: C[:, j] = scale*acc_gate, C[:, cup + j] = scale*acc_up
+  EPI_SWIGLU = 2,      // dual, plus H = silu(gate) * up; C holds [gate | up]
+  EPI_SWIGLU_BWD = 3,  // acc = dh; reads GU = [g | u]; C[:, j] = dg, C[:, cup + j] = du
+};
+
+enum TailMode : int {
+  TAIL_NONE = 0,
+  TAIL_SINGLE = 1,     // K2 = r2a from source 0
+  TAIL_BLOCKDIAG = 2,  // dual: tail rows [0, r2a) feed gate columns from source 0,
+                       //       rows [r2a, 2 r2a) feed up columns from source 1
+  TAIL_STACKED = 3,    // tail rows [0, r2a) from source 0, [r2a, 2 r2a) from source 1
+};
+
+struct GemmArgs {
+  // ---- problem
+  int M;             // rows of a single ungrouped problem (goff == nullptr); GK: output rows
+  int N;             // output columns (per half for dual epilogues)
+  int K;             // reduction length (GM)
+  int G;             // number of groups
+  const int* goff;   // [G+1] group offsets, or nullptr for one group [0, M)
+  const int* toff_all;  // GM: kNumTileSizes tables of [G+1] row-tile prefix sums (one per BM)
+  // ---- A operand (GM: layout XK with optional row gather; GK: layout KX over group rows)
+  const void* A;
+  long lda;
+  const int* arow;   // GM gather: A row of output row i is arow[i] / arow_div
+  int arow_div;
+  // ---- B operand
+  const void* B;
+  long ldb;
+  long bstride;      // elements between consecutive groups' B
+  const void* Bu;    // dual: base of the up half (same layout, ld and group stride as B)
+  // ---- LoRA tail (GM only)
+  int tail;          // TailMode
+  int r2a;           // rows of the reduction tail taken from each source
+  const void* TA;    // [rows][lda2] tail A operand (layout XK, same row space as the output)
+  long lda2;
+  const void* TB0;   // tail B sources (layout of B), per-group stride tbstride
+  const void* TB1;
+  long ldtb;
+  long tbstride;
+  // ---- epilogue
+  void* C;
+  void* C1;          // GK: columns >= nsplit go to C1 (column index minus nsplit); nullptr: none
+  int nsplit;
+  int ctrans;        // GK: store C[col * ldc + row] instead of C[row * ldc + col]
+  long ldc;
+  long cup;          // dual epilogues: column offset of the up half in C
+  long cstride;      // GK: elements between groups' outputs
+  float scale;
+  const float* bias; // EPI_STORE: per-column bias (fp32) or nullptr
+  void* H;           // EPI_SWIGLU: silu(gate)*up output
+  long ldh;
+  const void* GU;    // EPI_SWIGLU_BWD: saved [g | u]
+  long ldgu;
+  long guup;         // column offset of u in GU
+};
+
+// Launchers (hipStream_t passed as void* to keep this header light). Each returns a HIP error.
+// dtype: 0 fp32, 1 bf16. For bf16 the MFMA kernels run unless reference is set.
+// GM: rows_bound = upper bound on the total number of rows over all groups (sizes the grid).
+hipError_t gemm_gm_launch(const GemmArgs& a, int b_layout, int epi, int out_f32, int dtype,
+                          int rows_bound, int reference, hipStream_t stream);
+hipError_t gemm_gk_launch(const GemmArgs& a, int dtype, int reference, hipStream_t stream);
+
+// Row-tile tables for the MFMA row tile sizes used by gemm_gm_launch.
+constexpr int kNumTileSizes = 3;
+constexpr int kTileSizes[kNumTileSizes] = {32, 64, 128};
+int tile_table_index(int bm);
+
+}  // namespace moe

@@ -1,0 +1,45 @@
+// Launchers for the routing and data-movement kernels of the MoE-LoRA layer.
+#pragma once
+#include "common.h"
+
+namespace moe {
+
+constexpr int kRouteBlockTokens = 256;  // tokens per block in the histogram/rank pass
+
+// Per token: top-k logits (ties -> lower expert id), routing weights, raw scores.
+hipError_t launch_topk(const float* z, int s, int E, int k, int score, int renorm, int* idx,
+                       float* w, float* psel, hipStream_t st);
+// Per block of 256 tokens: expert histogram and each pair's rank among the block's pairs of the
+// same expert (token order).
+hipError_t launch_hist_rank(const int* idx, int s, int k, int E, int* blk_hist, int* rank,
+                            hipStream_t st);
+// Expert offsets, per-block bases and row-tile tables from the block histograms (one workgroup).
+hipError_t launch_scan(const int* blk_hist, int nb, int E, int P, int* blk_base, int* off,
+                       int* tile_tables, hipStream_t st);
+// perm / inv / row token from the bases and ranks.
+hipError_t launch_scatter(const int* idx, const int* rank, const int* blk_base, int s, int k, int E,
+                          int* perm, int* inv, int* row_tok, hipStream_t st);
+
+// dst[i, :] = src[map[i] / div, :] for i < rows (row of `row_elems` elements).
+hipError_t launch_gather_rows(int dtype, const void* src, void* dst, const int* map, int div,
+                              int rows, int row_elems, hipStream_t st);
+// Y[t] = sum_j w[t,j] o[inv[t k + j]] (fp32 accumulate, slot order).
+hipError_t launch_combine(int dtype, const void* o, const int* inv, const float* w, void* Y, int s,
+                          int k, int m, hipStream_t st);
+// dO[i] = w[p] dY[t], ds[p] = dY[t] . o[i] for row i holding pair p = perm[i], t = p / k.
+hipError_t launch_combine_bwd(int dtype, const void* dY, const void* o, const int* perm,
+                              const float* w, void* dO, float* ds, int P, int k, int m,
+                              hipStream_t st);
+// dz[t, j] from ds, w, p_sel (softmax or sigmoid, renormalised or not).
+hipError_t launch_router_bwd(const float* ds, const float* w, const float* psel, int s, int k,
+                             int score, int renorm, float* dz, hipStream_t st);
+// WT[e, a] = W[a, e]
+hipError_t launch_transpose(int dtype, const void* W, void* WT, int rows, int cols, hipStream_t st);
+// dX[t] = sum_j dXp[inv[t k + j]] (+ sum_j dz[t,j] WrT[idx[t,j]] when dz != nullptr)
+hipError_t launch_unpermute(int dtype, const void* dXp, const int* inv, const float* dz,
+                            const int* idx, const void* WrT, void* dX, int s, int k, int m,
+                            hipStream_t st);
+// zero-fill n 32-bit words
+hipError_t launch_zero(void* p, size_t words, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,493 @@
+// Routing and data-movement kernels of the MoE-LoRA layer.
+//
+// Routing follows the routing equation of the ailinkdeeptech cookbook page "Accelerating
+// Mixture-of-Experts Fine-Tuning" (section "The Dynamic Dispatch Bottleneck"): top-k over the
+// router scores of x_t W_r, weights s_{t,i} on the selected experts. Grouping of the token-expert
+// pairs into contiguous per-expert runs is a counting sort: an LDS bitmask histogram per block of
+// 256 tokens gives each pair its rank among earlier tokens of the same expert, a single-workgroup
+// scan turns block histograms into bases, and a scatter writes perm/inv. The result is the stable
+// order (expert ascending, token ascending) and is independent of thread timing.
+#include "kernels.h"
+#include "gemm.h"
+#include <algorithm>
+
+namespace moe {
+namespace {
+
+// ---------------------------------------------------------------------------------------- top-k
+constexpr int kMaxPerLane = 16;  // E <= 1024
+
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ z, int s, int E, int k,
+                                                   int score, int renorm, int* __restrict__ idx,
+                                                   float* __restrict__ w, float* __restrict__ psel) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= s) return;
+  const float* zt = z + (long)t * E;
+  float v[kMaxPerLane];
+  unsigned taken = 0;
+  const int npl = (E + 63) >> 6;
+#pragma unroll
+  for (int q = 0; q < kMaxPerLane; q++) {
+    const int e = lane + 64 * q;
+    v[q] = (q < npl && e < E) ? zt[e] : -INFINITY;
+    if (!(q < npl && e < E)) taken |= 1u << q;
+  }
+  float selv[kMaxPerLane];  // lane L keeps the values of slots j with j % 64 == L
+  for (int j = 0; j < k; j++) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < kMaxPerLane; q++) {
+      if (taken & (1u << q)) continue;
+      const int e = lane + 64 * q;
+      if (v[q] > bv || (v[q] == bv && e < bi)) { bv = v[q]; bi = e; }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    }
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if ((j & 63) == lane) {
+      idx[(long)t * k + j] = bi;
+      selv[j >> 6] = bv;
+    }
+  }
+  // scores of the selected experts
+  float denom = 1.0f;
+  if (score == 0) {  // softmax over all E, max-subtracted (the max is the first selection)
+    const float zmax = __shfl(selv[0], 0, 64);
+    float part = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kMaxPerLane; q++) {
+      const int e = lane + 64 * q;
+      if (q < npl && e < E) part += expf(v[q] - zmax);
+    }
+    denom = wave_sum(part);
+    float p[kMaxPerLane];
+    float ps = 0.0f;
+    for (int jj = 0; (jj << 6) + lane < k; jj++) {
+      p[jj] = expf(selv[jj] - zmax) / denom;
+      ps += p[jj];
+    }
+    ps = wave_sum(ps);
+    for (int jj = 0; (jj << 6) + lane < k; jj++) {
+      const long o = (long)t * k + (jj << 6) + lane;
+      psel[o] = p[jj];
+      w[o] = renorm ? p[jj] / ps : p[jj];
+    }
+  } else {  // sigmoid
+    float p[kMaxPerLane];
+    float ps = 0.0f;
+    for (int jj = 0; (jj << 6) + lane < k; jj++) {
+      p[jj] = 1.0f / (1.0f + expf(-selv[jj]));
+      ps += p[jj];
+    }
+    ps = wave_sum(ps);
+    for (int jj = 0; (jj << 6) + lane < k; jj++) {
+      const long o = (long)t * k + (jj << 6) + lane;
+      psel[o] = p[jj];
+      w[o] = renorm ? p[jj] / ps : p[jj];
+    }
+  }
+}
+
+// ------------------------------------------------------------------------- histogram and ranks
+__global__ __launch_bounds__(256) void hist_rank_kernel(const int* __restrict__ idx, int s, int k,
+                                                        int E, int* __restrict__ blk_hist,
+                                                        int* __restrict__ rank) {
+  extern __shared__ unsigned long long lds_masks[];      // [4][E] token bitmasks per wave
+  int* wpre = reinterpret_cast<int*>(lds_masks + 4 * E);  // [4][E] per-wave prefix counts
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int t = blockIdx.x * kRouteBlockTokens + tid;
+  for (int i = tid; i < 4 * E; i += 256) lds_masks[i] = 0ull;
+  __syncthreads();
+  if (t < s)
+    for (int j = 0; j < k; j++) atomicOr(&lds_masks[wv * E + idx[(long)t * k + j]], 1ull << lane);
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) {
+    int acc = 0;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      wpre[q * E + e] = acc;
+      acc += __popcll(lds_masks[q * E + e]);
+    }
+    blk_hist[(long)blockIdx.x * E + e] = acc;
+  }
+  __syncthreads();
+  if (t < s) {
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int j = 0; j < k; j++) {
+      const int e = idx[(long)t * k + j];
+      rank[(long)t * k + j] = wpre[wv * E + e] + __popcll(lds_masks[wv * E + e] & below);
+    }
+  }
+}
+
+// Exclusive scan over a 1024-thread block; returns the exclusive prefix, *total the sum.
+__device__ int block_exscan_1024(int v, int* sh, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh[wv] = x;
+  __syncthreads();
+  if (wv == 0) {
+    int s2 = lane < 16 ? sh[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const int y = __shfl_up(s2, o, 64);
+      if (lane >= o) s2 += y;
+    }
+    if (lane < 16) sh[16 + lane] = s2;
+  }
+  __syncthreads();
+  const int base = wv > 0 ? sh[16 + wv - 1] : 0;
+  *total = sh[16 + 15];
+  const int r = base + x - v;
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ blk_hist, int nb, int E,
+                                                    int P, int* __restrict__ blk_base,
+                                                    int* __restrict__ off,
+                                                    int* __restrict__ tile_tables) {
+  __shared__ int sh[32];
+  const int e = threadIdx.x;
+  int cnt = 0;
+  if (e < E)
+    for (int b = 0; b < nb; b++) cnt += blk_hist[(long)b * E + e];
+  int total;
+  const int start = block_exscan_1024(e < E ? cnt : 0, sh, &total);
+  if (e < E) {
+    off[e] = start;
+    int run = start;
+    for (int b = 0; b < nb; b++) {
+      blk_base[(long)b * E + e] = run;
+      run += blk_hist[(long)b * E + e];
+    }
+  }
+  if (e == 0) off[E] = total;
+  for (int i = 0; i < kNumTileSizes; i++) {
+    const int bm = kTileSizes[i];
+    const int tiles = e < E ? (cnt + bm - 1) / bm : 0;
+    int ttot;
+    const int ts = block_exscan_1024(tiles, sh, &ttot);
+    if (e < E) tile_tables[i * (E + 1) + e] = ts;
+    if (e == 0) tile_tables[i * (E + 1) + E] = ttot;
+  }
+  (void)P;
+}
+
+__global__ void scatter_kernel(const int* __restrict__ idx, const int* __restrict__ rank,
+                               const int* __restrict__ blk_base, int s, int k, int E,
+                               int* __restrict__ perm, int* __restrict__ inv,
+                               int* __restrict__ row_tok) {
+  const long p = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= (long)s * k) return;
+  const int t = (int)(p / k);
+  const int e = idx[p];
+  const int pos = blk_base[(long)(t / kRouteBlockTokens) * E + e] + rank[p];
+  perm[pos] = (int)p;
+  inv[p] = pos;
+  row_tok[pos] = t;
+}
+
+// --------------------------------------------------------------------------- data movement
+// Rows are moved as 16-byte chunks; row_elems * sizeof(T) is a multiple of 16.
+template <typename T>
+__global__ __launch_bounds__(256) void gather_rows_kernel(const T* __restrict__ src, T* __restrict__ dst,
+                                                          const int* __restrict__ map, int div, int rows,
+                                                          int row_elems) {
+  constexpr int V = 16 / sizeof(T);
+  const int cpr = row_elems / V;
+  const long total = (long)rows * cpr;
+  for (long c = (long)blockIdx.x * blockDim.x + threadIdx.x; c < total; c += (long)gridDim.x * blockDim.x) {
+    const long i = c / cpr;
+    const int q = (int)(c - i * cpr);
+    const long srow = map[i] / div;
+    *reinterpret_cast<i32x4_t*>(dst + i * row_elems + q * V) =
+        *reinterpret_cast<const i32x4_t*>(src + srow * row_elems + q * V);
+  }
+}
+
+template <typename T> struct Vec8;
+template <> struct Vec8<bf16_t> {
+  static constexpr int N = 8;
+  __device__ static void load(const bf16_t* p, float* f) {
+    const i32x4_t r = *reinterpret_cast<const i32x4_t*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      f[2 * i] = bf16_to_f32((bf16_t)(r[i] & 0xffff));
+      f[2 * i + 1] = bf16_to_f32((bf16_t)((unsigned)r[i] >> 16));
+    }
+  }
+  __device__ static void store(bf16_t* p, const float* f) {
+    i32x4_t r;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      r[i] = (int)((unsigned)f32_to_bf16(f[2 * i]) | ((unsigned)f32_to_bf16(f[2 * i + 1]) << 16));
+    *reinterpret_cast<i32x4_t*>(p) = r;
+  }
+};
+template <> struct Vec8<float> {
+  static constexpr int N = 4;
+  __device__ static void load(const float* p, float* f) {
+    const f32x4_t r = *reinterpret_cast<const f32x4_t*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; i++) f[i] = r[i];
+  }
+  __device__ static void store(float* p, const float* f) {
+    f32x4_t r;
+#pragma unroll
+    for (int i = 0; i < 4; i++) r[i] = f[i];
+    *reinterpret_cast<f32x4_t*>(p) = r;
+  }
+};
+
+// One block per token; threads walk the row in 16-byte chunks.
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ o, const int* __restrict__ inv,
+                                                      const float* __restrict__ w, T* __restrict__ Y,
+                                                      int k, int m) {
+  constexpr int V = Vec8<T>::N;
+  const long t = blockIdx.x;
+  for (int c = threadIdx.x; c * V < m; c += blockDim.x) {
+    float acc[V] = {};
+    for (int j = 0; j < k; j++) {
+      const float wj = w[t * k + j];
+      float f[V];
+      Vec8<T>::load(o + (long)inv[t * k + j] * m + c * V, f);
+#pragma unroll
+      for (int i = 0; i < V; i++) acc[i] += wj * f[i];
+    }
+    Vec8<T>::store(Y + t * m + c * V, acc);
+  }
+}
+
+// One block per group row.
+template <typename T>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ dY, const T* __restrict__ o,
+                                                          const int* __restrict__ perm,
+                                                          const float* __restrict__ w, T* __restrict__ dO,
+                                                          float* __restrict__ ds, int k, int m) {
+  constexpr int V = Vec8<T>::N;
+  __shared__ float red[4];
+  const long i = blockIdx.x;
+  const int p = perm[i];
+  const long t = p / k;
+  const float wp = w[p];
+  float dot = 0.0f;
+  for (int c = threadIdx.x; c * V < m; c += blockDim.x) {
+    float fy[V], fo[V], out[V];
+    Vec8<T>::load(dY + t * m + c * V, fy);
+    Vec8<T>::load(o + i * m + c * V, fo);
+#pragma unroll
+    for (int q = 0; q < V; q++) {
+      dot += fy[q] * fo[q];
+      out[q] = wp * fy[q];
+    }
+    Vec8<T>::store(dO + i * m + c * V, out);
+  }
+  dot = wave_sum(dot);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = dot;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float sum = 0.0f;
+    for (int q = 0; q < (int)(blockDim.x >> 6); q++) sum += red[q];
+    ds[p] = sum;
+  }
+}
+
+__global__ void router_bwd_kernel(const float* __restrict__ ds, const float* __restrict__ w,
+                                  const float* __restrict__ psel, int s, int k, int score, int renorm,
+                                  float* __restrict__ dz) {
+  const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= s) return;
+  const float* dst = ds + t * k;
+  const float* wt = w + t * k;
+  const float* pt = psel + t * k;
+  float wds = 0.0f, S = 0.0f;
+  for (int j = 0; j < k; j++) {
+    wds += wt[j] * dst[j];
+    S += pt[j];
+  }
+  for (int j = 0; j < k; j++) {
+    float g;
+    if (score == 0) g = wt[j] * (dst[j] - wds);  // softmax + renormalise
+    else if (renorm) g = pt[j] * (1.0f - pt[j]) / S * (dst[j] - wds);
+    else g = pt[j] * (1.0f - pt[j]) * dst[j];
+    dz[t * k + j] = g;
+  }
+}
+
+template <typename T>
+__global__ void transpose_kernel(const T* __restrict__ W, T* __restrict__ WT, int rows, int cols) {
+  __shared__ T tile[32][33];
+  const int bx = blockIdx.x * 32, by = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+  for (int yy = ty; yy < 32; yy += 8) {
+    const int r = by + yy, c = bx + tx;
+    if (r < rows && c < cols) tile[yy][tx] = W[(long)r * cols + c];
+  }
+  __syncthreads();
+  for (int yy = ty; yy < 32; yy += 8) {
+    const int r = bx + yy, c = by + tx;  // output row = input column
+    if (r < cols && c < rows) WT[(long)r * rows + c] = tile[tx][yy];
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void unpermute_kernel(const T* __restrict__ dXp, const int* __restrict__ inv,
+                                                        const float* __restrict__ dz,
+                                                        const int* __restrict__ idx,
+                                                        const T* __restrict__ WrT, T* __restrict__ dX,
+                                                        int k, int m) {
+  constexpr int V = Vec8<T>::N;
+  const long t = blockIdx.x;
+  for (int c = threadIdx.x; c * V < m; c += blockDim.x) {
+    float acc[V] = {};
+    for (int j = 0; j < k; j++) {
+      float f[V];
+      Vec8<T>::load(dXp + (long)inv[t * k + j] * m + c * V, f);
+#pragma unroll
+      for (int i = 0; i < V; i++) acc[i] += f[i];
+    }
+    if (dz) {
+      for (int j = 0; j < k; j++) {
+        const float g = dz[t * k + j];
+        float f[V];
+        Vec8<T>::load(WrT + (long)idx[t * k + j] * m + c * V, f);
+#pragma unroll
+        for (int i = 0; i < V; i++) acc[i] += g * f[i];
+      }
+    }
+    Vec8<T>::store(dX + t * m + c * V, acc);
+  }
+}
+
+__global__ void zero_kernel(int* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_topk(const float* z, int s, int E, int k, int score, int renorm, int* idx,
+                       float* w, float* psel, hipStream_t st) {
+  if (s <= 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_kernel, dim3((s + 3) / 4), dim3(256), 0, st, z, s, E, k, score, renorm,
+                     idx, w, psel);
+  return hipGetLastError();
+}
+
+hipError_t launch_hist_rank(const int* idx, int s, int k, int E, int* blk_hist, int* rank,
+                            hipStream_t st) {
+  if (s <= 0) return hipSuccess;
+  const int nb = (s + kRouteBlockTokens - 1) / kRouteBlockTokens;
+  const size_t lds = (size_t)4 * E * sizeof(unsigned long long) + (size_t)4 * E * sizeof(int);
+  hipLaunchKernelGGL(hist_rank_kernel, dim3(nb), dim3(256), lds, st, idx, s, k, E, blk_hist, rank);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(const int* blk_hist, int nb, int E, int P, int* blk_base, int* off,
+                       int* tile_tables, hipStream_t st) {
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, blk_hist, nb, E, P, blk_base, off,
+                     tile_tables);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(const int* idx, const int* rank, const int* blk_base, int s, int k, int E,
+                          int* perm, int* inv, int* row_tok, hipStream_t st) {
+  const long P = (long)s * k;
+  if (P <= 0) return hipSuccess;
+  hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, st, idx, rank,
+                     blk_base, s, k, E, perm, inv, row_tok);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(int dtype, const void* src, void* dst, const int* map, int div,
+                              int rows, int row_elems, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  const long chunks = (long)rows * row_elems * (dtype ? 2 : 4) / 16;
+  const long blocks = std::min<long>((chunks + 255) / 256, 256L * 64);
+  if (dtype)
+    hipLaunchKernelGGL(gather_rows_kernel<bf16_t>, dim3((unsigned)blocks), dim3(256), 0, st,
+                       (const bf16_t*)src, (bf16_t*)dst, map, div, rows, row_elems);
+  else
+    hipLaunchKernelGGL(gather_rows_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st,
+                       (const float*)src, (float*)dst, map, div, rows, row_elems);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(int dtype, const void* o, const int* inv, const float* w, void* Y, int s,
+                          int k, int m, hipStream_t st) {
+  if (s <= 0) return hipSuccess;
+  if (dtype)
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(s), dim3(256), 0, st, (const bf16_t*)o, inv, w,
+                       (bf16_t*)Y, k, m);
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(s), dim3(256), 0, st, (const float*)o, inv, w,
+                       (float*)Y, k, m);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bwd(int dtype, const void* dY, const void* o, const int* perm,
+                              const float* w, void* dO, float* ds, int P, int k, int m,
+                              hipStream_t st) {
+  if (P <= 0) return hipSuccess;
+  if (dtype)
+    hipLaunchKernelGGL(combine_bwd_kernel<bf16_t>, dim3(P), dim3(256), 0, st, (const bf16_t*)dY,
+                       (const bf16_t*)o, perm, w, (bf16_t*)dO, ds, k, m);
+  else
+    hipLaunchKernelGGL(combine_bwd_kernel<float>, dim3(P), dim3(256), 0, st, (const float*)dY,
+                       (const float*)o, perm, w, (float*)dO, ds, k, m);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_bwd(const float* ds, const float* w, const float* psel, int s, int k,
+                             int score, int renorm, float* dz, hipStream_t st) {
+  if (s <= 0) return hipSuccess;
+  hipLaunchKernelGGL(router_bwd_kernel, dim3((s + 255) / 256), dim3(256), 0, st, ds, w, psel, s, k,
+                     score, renorm, dz);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(int dtype, const void* W, void* WT, int rows, int cols, hipStream_t st) {
+  dim3 grid((cols + 31) / 32, (rows + 31) / 32);
+  if (dtype)
+    hipLaunchKernelGGL(transpose_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)W, (bf16_t*)WT,
+                       rows, cols);
+  else
+    hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, st, (const float*)W, (float*)WT,
+                       rows, cols);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpermute(int dtype, const void* dXp, const int* inv, const float* dz,
+                            const int* idx, const void* WrT, void* dX, int s, int k, int m,
+                            hipStream_t st) {
+  if (s <= 0) return hipSuccess;
+  if (dtype)
+    hipLaunchKernelGGL(unpermute_kernel<bf16_t>, dim3(s), dim3(256), 0, st, (const bf16_t*)dXp, inv,
+                       dz, idx, (const bf16_t*)WrT, (bf16_t*)dX, k, m);
+  else
+    hipLaunchKernelGGL(unpermute_kernel<float>, dim3(s), dim3(256), 0, st, (const float*)dXp, inv, dz,
+                       idx, (const float*)WrT, (float*)dX, k, m);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(void* p, size_t words, hipStream_t st) {
+  if (words == 0) return hipSuccess;
+  const size_t blocks = std::min<size_t>((words + 255) / 256, 4096);
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (int*)p, words);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,151 @@
+/*
+ * moelora.h -- C ABI of libmoelora, the MoE expert-MLP layer with Split LoRA on one MI355X
+ * (gfx950). Forward and backward of
+ *
+ *     y_t = sum_{i in TopK(score(x_t W_r))} s_{t,i} * Expert_i(x_t),
+ *     Expert_e(x) = (silu(x Wg_e + c (x Ag_e) Bg_e) * (x Wu_e + c (x Au_e) Bu_e)) Wd_e
+ *                   + c ((...) Ad_e) Bd_e,                          c = alpha / r,
+ *
+ * the routing equation of the ailinkdeeptech.com cookbook page "Accelerating Mixture-of-Experts
+ * Fine-Tuning: Unsloth Faster MoE, Split LoRA, and Grouped GEMM" (section "The Dynamic Dispatch
+ * Bottleneck in Mixture-of-Experts Architectures") with every expert projection evaluated as
+ * Split LoRA, Y = XW + (alpha/r)(XA)B (same page, section "2. Split LoRA Associative
+ * Transformation"), never forming the m x n product of the LoRA factors. The expert weights are
+ * one fused tensor per projection, gate and up concatenated along the output axis, gate first
+ * (unsloth.ai "Faster MoE" documentation page, section on torch._grouped_mm).
+ *
+ * Conventions (all calls):
+ *  - Tensors are caller-owned DEVICE pointers, dense row-major, 16-byte aligned. The library never
+ *    allocates device memory, keeps no state between calls, never prints and never aborts.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream). Buffers must
+ *    stay valid until the work on `stream` has finished.
+ *  - All argument checks run on the host before anything is enqueued; on any error nothing is
+ *    enqueued and a status other than MOE_OK is returned. MOE_ERR_HIP reports a failed launch.
+ *  - Outputs are overwritten, never accumulated into.
+ *  - Element type of X, W_r, weights, LoRA factors, Y, dY, dX: `shape->dtype` (fp32 or bf16).
+ *    Routing weights, logits and LoRA-factor gradients are fp32; indices are int32.
+ *  - Weights use the x.W orientation: W_r [m, E]; W_gu [E, m, 2n] (columns [0,n) gate, [n,2n) up);
+ *    W_d [E, n, m]; A_g, A_u [E, m, r]; B_g, B_u [E, r, n]; A_d [E, n, r]; B_d [E, r, m].
+ *  - Pair id p = t*k + j (token t, slot j of its selection order); P = s*k pairs.
+ *
+ * Supported shapes: s >= 0; m and n multiples of 64; 1 <= k <= E <= 1024; 1 <= r <= 64, and for
+ * bf16 r a multiple of 8 and E a multiple of 8; s*k*max(m, 2n) < 2^31. Anything else returns
+ * MOE_ERR_UNSUPPORTED (there is no fallback path).
+ */
+#ifndef MOELORA_H
+#define MOELORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status;
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG 1 /* null or misaligned pointer, bad enum, inconsistent sizes */
+#define MOE_ERR_UNSUPPORTED 2 /* a shape or mode the kernels do not implement */
+#define MOE_ERR_WORKSPACE 3   /* a state/saved/workspace buffer smaller than its size query */
+#define MOE_ERR_HIP 4         /* a kernel launch failed */
+
+#define MOE_DTYPE_F32 0
+#define MOE_DTYPE_BF16 1
+
+#define MOE_SCORE_SOFTMAX 0 /* softmax over all E logits */
+#define MOE_SCORE_SIGMOID 1 /* 1 / (1 + exp(-z)) per logit */
+
+/* flags */
+#define MOE_FLAG_REFERENCE_GEMM 1 /* run every GEMM with the plain one-thread-per-output kernels */
+
+typedef struct moe_shape {
+  int32_t s;           /* tokens */
+  int32_t m;           /* hidden size */
+  int32_t n;           /* expert intermediate size */
+  int32_t E;           /* experts */
+  int32_t k;           /* experts per token */
+  int32_t r;           /* LoRA rank */
+  float alpha;         /* LoRA alpha; the LoRA scale is c = alpha / r */
+  int32_t dtype;       /* MOE_DTYPE_* */
+  int32_t score;       /* MOE_SCORE_* */
+  int32_t renormalize; /* 1: s_{t,j} = p_j / sum of the token's k selected p; 0: s_{t,j} = p_j */
+  int32_t router_grad; /* 1: dX includes the path through the routing weights (top-k set fixed) */
+  int32_t flags;       /* MOE_FLAG_* */
+} moe_shape;
+
+/* Name of a status code (static string). */
+const char* moe_status_str(moe_status st);
+/* ABI version of this header (incremented on any incompatible change). */
+int32_t moe_abi_version(void);
+/* Checks a shape without enqueuing anything: MOE_OK or the status any call would return. */
+moe_status moe_check_shape(const moe_shape* shape);
+
+/* Size queries (bytes). Return 0 for an invalid or unsupported shape. */
+size_t moe_route_state_bytes(const moe_shape* shape);
+size_t moe_fwd_saved_bytes(const moe_shape* shape);
+/* Forward scratch; with_saved = 0 (inference, saved == NULL) also covers the intermediates that
+ * would otherwise live in `saved`. */
+size_t moe_fwd_ws_bytes(const moe_shape* shape, int32_t with_saved);
+size_t moe_bwd_ws_bytes(const moe_shape* shape);
+
+/*
+ * moe_route -- router logits, top-k selection, routing weights and grouping of the P pairs into
+ * contiguous per-expert runs.
+ *   logits z = X W_r (+ router_bias), fp32 accumulate. Per token the k largest logits are selected
+ *   (equal logits: lower expert id first); slot j is the j-th selection. Scores: softmax over all E
+ *   (MOE_SCORE_SOFTMAX) or sigmoid; weights s_{t,j} renormalised over the k selected when
+ *   shape->renormalize. Grouping: expert_off[e] = number of pairs routed to experts < e
+ *   (expert_off[E] = P); perm[row] = pair id, ordered by expert then token; inv_perm[pair] = row.
+ * In:  X [s, m], W_r [m, E], router_bias [E] fp32 or NULL (a fixed per-expert logit bias).
+ * Out: logits [s, E] fp32 (may be NULL), topk_idx [s, k] int32, topk_w [s, k] fp32,
+ *      expert_off [E + 1] int32, perm [P] int32, inv_perm [P] int32.
+ * route_state: >= moe_route_state_bytes(shape) bytes; keeps per-pair scores and the row tables the
+ *      forward and backward calls read; must stay untouched until the backward has run.
+ */
+moe_status moe_route(const moe_shape* shape, const void* X, const void* W_r,
+                     const float* router_bias, float* logits, int32_t* topk_idx, float* topk_w,
+                     int32_t* expert_off, int32_t* perm, int32_t* inv_perm, void* route_state,
+                     size_t route_state_bytes, void* stream);
+
+/*
+ * moe_lora_forward -- Y [s, m] = sum_j topk_w[t, j] * Expert_{topk_idx[t, j]}(X[t]).
+ * The pairs are gathered into per-expert runs (Xp[row] = X[perm[row] / k]); per expert, one
+ * grouped GEMM computes [g | u] = Xp W_gu + c [(Xp A_g) B_g | (Xp A_u) B_u] and h = silu(g) * u,
+ * a second computes o = h W_d + c (h A_d) B_d; the combine sums the k rows of each token weighted
+ * by topk_w in slot order (fp32 accumulate).
+ * Routing arguments and route_state come from moe_route on the same X and shape.
+ * saved: >= moe_fwd_saved_bytes bytes, receives what moe_lora_backward needs; NULL for inference.
+ * ws: >= moe_fwd_ws_bytes(shape, saved != NULL) bytes of scratch (may be NULL if that is 0).
+ */
+moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t* topk_idx,
+                            const float* topk_w, const int32_t* expert_off, const int32_t* perm,
+                            const int32_t* inv_perm, const void* route_state, const void* W_gu,
+                            const void* W_d, const void* A_g, const void* B_g, const void* A_u,
+                            const void* B_u, const void* A_d, const void* B_d, void* Y, void* saved,
+                            size_t saved_bytes, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_lora_backward -- gradients of the layer for upstream gradient dY [s, m]. The base weights
+ * and the router are frozen; only the LoRA factors train (unsloth.ai "Faster MoE" page, section
+ * "Implementation details").
+ * Out: dX [s, m] (dtype): through the experts, plus through the routing weights when
+ *      shape->router_grad (softmax without renormalisation is then MOE_ERR_UNSUPPORTED);
+ *      dA_g, dA_u [E, m, r], dB_g, dB_u [E, r, n], dA_d [E, n, r], dB_d [E, r, m], all fp32.
+ *      Experts that received no pair get exact zeros.
+ * In: the routing outputs and route_state of moe_route, the same weights as the forward, and the
+ *     `saved` buffer that moe_lora_forward filled. ws >= moe_bwd_ws_bytes bytes of scratch.
+ */
+moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void* X,
+                             const void* W_r, const int32_t* topk_idx, const float* topk_w,
+                             const int32_t* expert_off, const int32_t* perm,
+                             const int32_t* inv_perm, const void* route_state, const void* W_gu,
+                             const void* W_d, const void* A_g, const void* B_g, const void* A_u,
+                             const void* B_u, const void* A_d, const void* B_d, const void* saved,
+                             size_t saved_bytes, void* dX, float* dA_g, float* dB_g, float* dA_u,
+                             float* dB_u, float* dA_d, float* dB_d, void* ws, size_t ws_bytes,
+                             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOELORA_H */

@@ -1,0 +1,117 @@
+"""GPU parity: libmoelora (through the C ABI) against the CPU oracle on reduced layers.
+
+Routing protocol: GPU logits must match the oracle's to LOGIT_TOL; the oracle then selects,
+weights and groups on the GPU's own logits, and ids / offsets / perm / inv must be bit-equal and
+weights within WEIGHT_TOL. The layer outputs and gradients are compared per tensor with
+max|gpu - ref| / max|ref| <= 1e-5 (fp32) or 2e-2 (bf16).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import (LOGIT_TOL, TOL, VARIANTS, WEIGHT_TOL, host_weights, np64, oracle_route_from,
+                     rel_err)
+from synth import make_inputs
+
+pytestmark = pytest.mark.gpu
+
+GRAD_KEYS = ("dA_g", "dB_g", "dA_u", "dB_u", "dA_d", "dB_d")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def run_gpu(cfg, device, flags=0, router_grad=True):
+    from grouped_gemm_top_amd import layer
+    inp = make_inputs(cfg, seed=0, device="cpu", with_grad_output=cfg.backward)
+    d = {k: (v.to(device) if v is not None else None) for k, v in inp.items()}
+    shape = layer.shape_of(cfg, router_grad=router_grad, flags=flags)
+    rt = layer.route(shape, d["X"], d["W_r"], d["router_bias"])
+    Y, saved = layer.forward(shape, d["X"], rt, d, training=cfg.backward)
+    out = {"rt": rt, "Y": Y}
+    if cfg.backward:
+        dX, grads = layer.backward(shape, d["dY"], d["X"], d["W_r"], rt, d, saved)
+        out["dX"] = dX
+        out.update(grads)
+    torch.cuda.synchronize()
+    return inp, out
+
+
+def check_routing(cfg, inp, rt):
+    X, Wr = np64(inp["X"]), np64(inp["W_r"])
+    bias = np64(inp["router_bias"]) if inp["router_bias"] is not None else None
+    z_ref = oracle.router_logits(X, Wr, bias)
+    z_gpu = rt["logits"].cpu().numpy().astype(np.float64)
+    assert rel_err(z_gpu, z_ref) <= LOGIT_TOL
+    ort = oracle_route_from(z_gpu, cfg)
+    np.testing.assert_array_equal(rt["topk_idx"].cpu().numpy(), ort["idx"])
+    np.testing.assert_array_equal(rt["expert_off"].cpu().numpy(), ort["off"])
+    np.testing.assert_array_equal(rt["perm"].cpu().numpy(), ort["perm"])
+    np.testing.assert_array_equal(rt["inv_perm"].cpu().numpy(), ort["inv"])
+    assert rel_err(rt["topk_w"].cpu().numpy(), ort["w"]) <= WEIGHT_TOL
+    # selections that would differ under the oracle's own logits (near ties); reported only
+    diff = int(np.sum(np.any(np.sort(oracle.topk_experts(z_ref, cfg.k), 1) !=
+                             np.sort(ort["idx"], 1), axis=1)))
+    _say(f"  tokens whose top-k set differs under the oracle's own logits: {diff}")
+    return ort
+
+
+@pytest.mark.parametrize("flags", [0, 1], ids=["mfma", "reference"])
+@pytest.mark.parametrize("name", list(VARIANTS))
+def test_layer_parity(name, flags, cuda):
+    cfg = VARIANTS[name]
+    _say(f"[parity] {name} flags={flags} s={cfg.s} m={cfg.m} n={cfg.n} E={cfg.E} k={cfg.k} "
+         f"r={cfg.r} {cfg.dtype} {cfg.score} backward={cfg.backward}")
+    inp, out = run_gpu(cfg, cuda, flags=flags)
+    ort = check_routing(cfg, inp, out["rt"])
+    W = host_weights(inp)
+    X = np64(inp["X"])
+    Y_ref, saved = oracle.forward(X, W, ort, cfg.alpha, cfg.r)
+    tol = TOL[cfg.dtype]
+    errs = {"Y": rel_err(np64(out["Y"]), Y_ref)}
+    if cfg.backward:
+        g = oracle.backward(np64(inp["dY"]), X, np64(inp["W_r"]), W, ort, cfg.alpha, cfg.r,
+                            cfg.score, cfg.renormalize, True, saved)
+        errs["dX"] = rel_err(np64(out["dX"]), g["dX"])
+        for key in GRAD_KEYS:
+            errs[key] = rel_err(np64(out[key]), g[key])
+    _say("  rel errors: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"over tolerance {tol}: {bad}"
+
+
+def test_router_grad_off(cuda):
+    cfg = VARIANTS["qwen3_small"]
+    _say("[parity] router_grad=0 qwen3_small")
+    inp, out = run_gpu(cfg, cuda, router_grad=False)
+    ort = check_routing(cfg, inp, out["rt"])
+    W = host_weights(inp)
+    X = np64(inp["X"])
+    _, saved = oracle.forward(X, W, ort, cfg.alpha, cfg.r)
+    g = oracle.backward(np64(inp["dY"]), X, np64(inp["W_r"]), W, ort, cfg.alpha, cfg.r,
+                        cfg.score, cfg.renormalize, False, saved)
+    assert rel_err(np64(out["dX"]), g["dX"]) <= TOL[cfg.dtype]
+
+
+def test_zero_token_experts_get_zero_grads(cuda):
+    cfg = VARIANTS["qwen3_zipf_small"]
+    _say("[parity] zero-token experts")
+    inp, out = run_gpu(cfg, cuda)
+    off = out["rt"]["expert_off"].cpu().numpy()
+    empty = np.where(off[1:] == off[:-1])[0]
+    assert empty.size > 0, "the skewed layer should leave some experts without tokens"
+    for key in GRAD_KEYS:
+        assert torch.all(out[key][torch.as_tensor(empty, device=cuda)] == 0)
+
+
+def test_determinism(cuda):
+    cfg = VARIANTS["qwen3_small"]
+    _say("[parity] determinism qwen3_small")
+    _, a = run_gpu(cfg, cuda)
+    _, b = run_gpu(cfg, cuda)
+    for key in ("Y", "dX") + GRAD_KEYS:
+        assert torch.equal(a[key], b[key]), key
