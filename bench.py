@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""MoE-LoRA expert layer benchmark on one MI355X.
+
+One step = moe_route + moe_lora_forward (training, saving what the backward needs) +
+moe_lora_backward on one batch of seeded synthetic input already resident in HBM. Prints one JSON
+line: tokens/s of the whole step (value), TFLOP/s of the algorithmic work, the roofline of the
+dominant kernel (from per-stage HIP events recorded on the launch stream during a second timed
+pass), and the CPU oracle's rate on a bounded token sample of the same layer.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-LoRA layer fwd+bwd tokens/s and TFLOP/s (% bf16 MFMA peak), Qwen3-30B-A3B shape"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+GEMM_STAGES = ("fwd_gate_up", "fwd_down", "bwd_down", "bwd_gate_up")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def stage_work(stage, cfg, cnt, b):
+    """Algorithmic FLOPs and unique HBM bytes of one launch of a GEMM stage."""
+    P, m, n, r = cfg.s * cfg.k, cfg.m, cfg.n, cfg.r
+    used = int((cnt > 0).sum())   # experts whose weights are read
+    if stage == "fwd_gate_up":
+        fl = 2 * P * m * 2 * n + 2 * P * r * 2 * n
+        by = (P * m + used * m * 2 * n + P * 2 * r + 2 * used * r * n + P * 2 * n + P * n) * b
+    elif stage == "fwd_down":
+        fl = 2 * P * n * m + 2 * P * r * m
+        by = (P * n + used * n * m + P * r + used * r * m + P * m) * b
+    elif stage == "bwd_down":
+        fl = 2 * P * m * n + 2 * P * r * n
+        by = (P * m + used * n * m + P * r + used * n * r + P * 2 * n + P * 2 * n) * b
+    elif stage == "bwd_gate_up":
+        fl = 2 * P * 2 * n * m + 2 * P * 2 * r * m
+        by = (P * 2 * n + used * m * 2 * n + P * 2 * r + 2 * used * m * r + P * m) * b
+    else:
+        raise KeyError(stage)
+    return fl, by
+
+
+def traffic_for(stage, workload):
+    """HBM bytes per launch measured by rocprofv3 counters (profiles/traffic.json), or None when
+    absent or taken on a different build of the GEMM kernels."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    src = hashlib.sha256(open(os.path.join(ROOT, "grouped_gemm_top_amd", "csrc", "gemm.hip"), "rb").read()).hexdigest()
+    try:
+        entries = json.load(open(path))
+    except ValueError:
+        return None
+    for ent in entries.get("entries", []):
+        if ent.get("stage") == stage and ent.get("workload") == workload and ent.get("gemm_hip_sha256") == src:
+            return ent.get("bytes_per_launch")
+    return None
+
+
+def cpu_baseline(cfg, inp, tokens, min_seconds=10.0, max_passes=8):
+    """The oracle, untuned, on the first `tokens` tokens of the same layer (route + fwd + bwd)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    S = min(tokens, cfg.s)
+    f64 = lambda t: t.detach().to("cpu", torch.float32).numpy().astype(np.float64)
+    X = f64(inp["X"][:S])
+    dY = f64(inp["dY"][:S])
+    Wr = f64(inp["W_r"])
+    bias = f64(inp["router_bias"]) if inp["router_bias"] is not None else None
+    W = {k: inp[k].detach().to("cpu", torch.float32).numpy() for k in
+         ("W_gu", "W_d", "A_g", "B_g", "A_u", "B_u", "A_d", "B_d")}
+    passes, t0 = 0, time.perf_counter()
+    while True:   # whole passes until at least min_seconds of CPU work
+        z = oracle.router_logits(X, Wr, bias)
+        rt = oracle.route(z, cfg.k, cfg.E, cfg.score, cfg.renormalize)
+        _, saved = oracle.forward(X, W, rt, cfg.alpha, cfg.r)
+        oracle.backward(dY, X, Wr, W, rt, cfg.alpha, cfg.r, cfg.score, cfg.renormalize, True, saved)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or passes >= max_passes:
+            break
+    return {"value": round(passes * S / dt, 3), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {S} of {cfg.s} tokens of the same layer, route + forward + backward "
+                      f"(fp64 numpy), {passes} pass(es) in {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_30b_a3b")
+    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--reference-gemm", action="store_true",
+                    help="run every GEMM with the plain SIMT kernels (diagnostics)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the layer is benchmarked on a single MI355X and multi-GPU runs are not part of "
+              "this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import grouped_gemm_top_amd as g
+    from grouped_gemm_top_amd import accounting, layer
+    from synth import config, make_inputs
+
+    g.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    cfg = config(args.workload)
+    log(f"[bench] workload {cfg.name}: s={cfg.s} m={cfg.m} n={cfg.n} E={cfg.E} k={cfg.k} r={cfg.r} "
+        f"{cfg.dtype} {cfg.score}")
+    inp = make_inputs(cfg, seed=0, device=dev, with_grad_output=True)
+    flags = g.MOE_FLAG_REFERENCE_GEMM if args.reference_gemm else 0
+    shape = layer.shape_of(cfg, flags=flags)
+    X, Wr, bias, dY = inp["X"], inp["W_r"], inp["router_bias"], inp["dY"]
+    rt = layer.alloc_route(shape, dev)
+    saved = torch.empty(g.moe_fwd_saved_bytes(shape), dtype=torch.uint8, device=dev)
+    bws = torch.empty(g.moe_bwd_ws_bytes(shape), dtype=torch.uint8, device=dev)
+    Y = torch.empty_like(X)
+    dX = torch.empty_like(X)
+    grads = layer.alloc_grads(shape, dev)
+
+    def step():
+        layer.route(shape, X, Wr, bias, bufs=rt)
+        layer.forward(shape, X, rt, inp, Y=Y, saved=saved)
+        layer.backward(shape, dY, X, Wr, rt, inp, saved, dX=dX, grads=grads, ws=bws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    log(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step")
+
+    # second pass: per-stage HIP events on the launch stream
+    g.moe_timing_enable(True)
+    g.moe_timing_read()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    stages = g.moe_timing_read()
+    g.moe_timing_enable(False)
+    avg = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in stages.items()}
+    per_step = {k: v[0] / args.steps for k, v in stages.items() if v[1]}
+    for k, v in sorted(per_step.items(), key=lambda kv: -kv[1]):
+        log(f"[bench]   {k:24s} {v * 1e3:9.1f} us/step")
+
+    flops = accounting.gemm_flops(cfg.s, cfg.m, cfg.n, cfg.E, cfg.k, cfg.r, backward=True)
+    tflops = flops["total"] / (ms * 1e-3) / 1e12
+    cnt = np.diff(rt["expert_off"].cpu().numpy())
+    b = 2 if cfg.dtype == "bf16" else 4
+    dom = max(GEMM_STAGES, key=lambda st: per_step.get(st, 0.0))
+    fl, by = stage_work(dom, cfg, cnt, b)
+    t_s = avg[dom] * 1e-3
+    t_mfma = fl / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = by / (PEAK_HBM_GBS * 1e9)
+    if t_hbm > t_mfma:
+        roof = {"bound": "hbm", "achieved": round(by / t_s / 1e9, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(by / t_s / 1e9 / PEAK_HBM_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(fl / t_s / 1e12, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(fl / t_s / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    roof["traffic"] = traffic_for(dom, cfg.name)
+    roof["kernel"] = dom
+    roof["avg_launch_ms"] = round(avg[dom], 4)
+    roof["mfma_frac"] = round(fl / t_s / 1e12 / PEAK_BF16_TFLOPS, 4)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle on {args.cpu_tokens} tokens ...")
+        cpu = cpu_baseline(cfg, inp, args.cpu_tokens)
+        log(f"[bench] CPU oracle: {cpu['value']} tokens/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": METRIC,
+        "value": round(cfg.s / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "s": cfg.s, "m": cfg.m, "n": cfg.n, "E": cfg.E,
+                   "k": cfg.k, "r": cfg.r, "alpha": cfg.alpha, "router": cfg.score,
+                   "step": "route+forward+backward",
+                   "gemm": "reference-simt" if args.reference_gemm else "mfma"},
+        "tflops": round(tflops, 2),
+        "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "stage_us_per_step": {k: round(v * 1e3, 1) for k, v in per_step.items()},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -17,7 +17,7 @@ __all__ = [
     "moe_check_shape", "moe_route_state_bytes", "moe_fwd_saved_bytes", "moe_fwd_ws_bytes",
     "moe_bwd_ws_bytes", "moe_route", "moe_lora_forward", "moe_lora_backward",
     "MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP",
-    "MOE_FLAG_REFERENCE_GEMM",
+    "MOE_FLAG_REFERENCE_GEMM", "moe_timing_enable", "moe_timing_read",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoelora.so")
@@ -59,6 +59,10 @@ _SIGNATURES = {
     "moe_route": (_I32, [_SHAPE] + [_P] * 10 + [_SZ, _P]),
     "moe_lora_forward": (_I32, [_SHAPE] + [_P] * 17 + [_SZ, _P, _SZ, _P]),
     "moe_lora_backward": (_I32, [_SHAPE] + [_P] * 18 + [_SZ] + [_P] * 8 + [_SZ, _P]),
+    "moe_timing_enable": (_I32, [_I32]),
+    "moe_timing_stage_count": (_I32, []),
+    "moe_timing_stage_name": (ctypes.c_char_p, [_I32]),
+    "moe_timing_read": (_I32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), _I32]),
 }
 
 
@@ -168,3 +172,16 @@ def moe_lora_backward(shape, dY, X, W_r, topk_idx, topk_w, expert_off, perm, inv
         _nbytes(saved), _ptr(dX), _ptr(dA_g), _ptr(dB_g), _ptr(dA_u), _ptr(dB_u), _ptr(dA_d),
         _ptr(dB_d), _ptr(ws), _nbytes(ws), _stream(stream))
     _check(st, "moe_lora_backward")
+
+
+def moe_timing_enable(on: bool) -> None:
+    _check(lib().moe_timing_enable(int(bool(on))), "moe_timing_enable")
+
+
+def moe_timing_read() -> dict:
+    """{stage name: (summed ms, count)} since the last read; waits for the recorded events."""
+    n = int(lib().moe_timing_stage_count())
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    _check(lib().moe_timing_read(ms, cnt, n), "moe_timing_read")
+    return {lib().moe_timing_stage_name(i).decode(): (ms[i], int(cnt[i])) for i in range(n)}

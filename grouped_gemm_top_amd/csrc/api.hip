@@ -2,6 +2,8 @@
 // layer (routing, forward, backward). See include/moelora.h for the contract of each call.
 #include <cmath>
 #include <cstring>
+#include <mutex>
+#include <vector>
 
 #include "../../include/moelora.h"
 #include "gemm.h"
@@ -10,8 +12,6 @@
 using namespace moe;
 
 namespace {
-
-constexpr int kTileIdxForMFMA = 2;  // row tile 128 (kTileSizes[2])
 
 // Bump allocator over a caller buffer; with base == nullptr it only measures.
 struct Carve {
@@ -129,6 +129,76 @@ inline bool ptr_ok(const void* p, size_t count) {
     if ((x) != hipSuccess) return MOE_ERR_HIP; \
   } while (0)
 
+
+// ------------------------------------------------------------------------------------------------
+// Optional per-stage timing (diagnostics): hipEvent pairs recorded on the call's stream around each
+// stage while enabled, resolved and summed by moe_timing_read.
+enum Stage {
+  ST_ROUTE_LOGITS, ST_ROUTE_TOPK, ST_ROUTE_HIST, ST_ROUTE_SCAN, ST_ROUTE_SCATTER,
+  ST_FWD_PERMUTE, ST_FWD_T_GU, ST_FWD_GATE_UP, ST_FWD_T_D, ST_FWD_DOWN, ST_FWD_COMBINE,
+  ST_BWD_COMBINE, ST_BWD_ROUTER, ST_BWD_U_D, ST_BWD_DOWN, ST_BWD_GRAD_D, ST_BWD_U_GU,
+  ST_BWD_GATE_UP, ST_BWD_GRAD_GU, ST_BWD_UNPERMUTE, ST_COUNT
+};
+const char* const kStageNames[ST_COUNT] = {
+  "route_logits", "route_topk", "route_hist_rank", "route_scan", "route_scatter",
+  "fwd_permute", "fwd_lora_t_gate_up", "fwd_gate_up", "fwd_lora_t_down", "fwd_down", "fwd_combine",
+  "bwd_combine", "bwd_router", "bwd_lora_u_down", "bwd_down", "bwd_lora_grads_down",
+  "bwd_lora_u_gate_up", "bwd_gate_up", "bwd_lora_grads_gate_up", "bwd_unpermute"};
+
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  struct Pending { int stage; hipEvent_t b, e; };
+  std::vector<Pending> pending;
+  std::vector<hipEvent_t> pool;
+  double total_ms[ST_COUNT] = {};
+  long long count[ST_COUNT] = {};
+};
+Timing g_timing;
+
+hipEvent_t timing_event() {
+  if (!g_timing.pool.empty()) {
+    hipEvent_t ev = g_timing.pool.back();
+    g_timing.pool.pop_back();
+    return ev;
+  }
+  hipEvent_t ev = nullptr;
+  if (hipEventCreate(&ev) != hipSuccess) return nullptr;
+  return ev;
+}
+
+struct StageScope {
+  int stage;
+  hipStream_t st;
+  hipEvent_t b = nullptr;
+  StageScope(int s_, hipStream_t st_) : stage(s_), st(st_) {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    if (!g_timing.on) return;
+    b = timing_event();
+    if (b && hipEventRecord(b, st) != hipSuccess) {
+      g_timing.pool.push_back(b);
+      b = nullptr;
+    }
+  }
+  ~StageScope() {
+    if (!b) return;
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    hipEvent_t e = timing_event();
+    if (e && hipEventRecord(e, st) == hipSuccess) {
+      g_timing.pending.push_back({stage, b, e});
+    } else {
+      g_timing.pool.push_back(b);
+      if (e) g_timing.pool.push_back(e);
+    }
+  }
+};
+
+#define STAGE(id, x)                  \
+  do {                                \
+    StageScope stage_scope_((id), hs); \
+    HIP_TRY(x);                       \
+  } while (0)
+
 GemmArgs gemm_args() {
   GemmArgs a;
   std::memset(&a, 0, sizeof(a));
@@ -214,11 +284,11 @@ moe_status moe_route(const moe_shape* shape, const void* X, const void* W_r,
   a.ldc = s.E;
   a.bias = router_bias;
   const int ref = (s.flags & MOE_FLAG_REFERENCE_GEMM) ? 1 : 0;
-  HIP_TRY(gemm_gm_launch(a, LAYOUT_KX, EPI_STORE, 1, s.dtype, s.s, ref, hs));
-  HIP_TRY(launch_topk(z, s.s, s.E, s.k, s.score, s.renormalize, topk_idx, topk_w, rs.psel, hs));
-  HIP_TRY(launch_hist_rank(topk_idx, s.s, s.k, s.E, rs.blk_hist, rs.rank, hs));
-  HIP_TRY(launch_scan(rs.blk_hist, nblocks(s), s.E, (int)P, rs.blk_base, expert_off, rs.tiles, hs));
-  HIP_TRY(launch_scatter(topk_idx, rs.rank, rs.blk_base, s.s, s.k, s.E, perm, inv_perm, rs.row_tok, hs));
+  STAGE(ST_ROUTE_LOGITS, gemm_gm_launch(a, LAYOUT_KX, EPI_STORE, 1, s.dtype, s.s, ref, hs));
+  STAGE(ST_ROUTE_TOPK, launch_topk(z, s.s, s.E, s.k, s.score, s.renormalize, topk_idx, topk_w, rs.psel, hs));
+  STAGE(ST_ROUTE_HIST, launch_hist_rank(topk_idx, s.s, s.k, s.E, rs.blk_hist, rs.rank, hs));
+  STAGE(ST_ROUTE_SCAN, launch_scan(rs.blk_hist, nblocks(s), s.E, (int)P, rs.blk_base, expert_off, rs.tiles, hs));
+  STAGE(ST_ROUTE_SCATTER, launch_scatter(topk_idx, rs.rank, rs.blk_base, s.s, s.k, s.E, perm, inv_perm, rs.row_tok, hs));
   return MOE_OK;
 }
 
@@ -261,7 +331,7 @@ moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t
   const int Pi = (int)P;
 
   // permute: Xp[row] = X[perm[row] / k]
-  HIP_TRY(launch_gather_rows(s.dtype, X, f.Xp, perm, s.k, Pi, s.m, hs));
+  STAGE(ST_FWD_PERMUTE, launch_gather_rows(s.dtype, X, f.Xp, perm, s.k, Pi, s.m, hs));
 
   GemmArgs base = gemm_args();
   base.G = s.E;
@@ -275,7 +345,7 @@ moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t
     a.A = f.Xp; a.lda = s.m;
     a.B = A_g; a.Bu = A_u; a.ldb = s.r; a.bstride = (long)m * r;
     a.C = f.Tgu; a.ldc = 2 * s.r; a.cup = s.r; a.scale = c;
-    HIP_TRY(gemm_gm_launch(a, LAYOUT_KX, EPI_DUAL, 0, s.dtype, Pi, ref, hs));
+    STAGE(ST_FWD_T_GU, gemm_gm_launch(a, LAYOUT_KX, EPI_DUAL, 0, s.dtype, Pi, ref, hs));
   }
   // [g | u] = Xp W_gu + [Tc_g B_g | Tc_u B_u];  h = silu(g) * u
   {
@@ -288,7 +358,7 @@ moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t
     a.TB0 = B_g; a.TB1 = B_u; a.ldtb = s.n; a.tbstride = (long)r * n;
     a.C = f.gu; a.ldc = 2 * s.n; a.cup = s.n;
     a.H = f.h; a.ldh = s.n;
-    HIP_TRY(gemm_gm_launch(a, LAYOUT_KX, EPI_SWIGLU, 0, s.dtype, Pi, ref, hs));
+    STAGE(ST_FWD_GATE_UP, gemm_gm_launch(a, LAYOUT_KX, EPI_SWIGLU, 0, s.dtype, Pi, ref, hs));
   }
   // Tc_d = c * h A_d
   {
@@ -297,7 +367,7 @@ moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t
     a.A = f.h; a.lda = s.n;
     a.B = A_d; a.ldb = s.r; a.bstride = (long)n * r;
     a.C = f.Td; a.ldc = s.r; a.scale = c;
-    HIP_TRY(gemm_gm_launch(a, LAYOUT_KX, EPI_STORE, 0, s.dtype, Pi, ref, hs));
+    STAGE(ST_FWD_T_D, gemm_gm_launch(a, LAYOUT_KX, EPI_STORE, 0, s.dtype, Pi, ref, hs));
   }
   // o = h W_d + Tc_d B_d
   {
@@ -309,10 +379,10 @@ moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t
     a.TA = f.Td; a.lda2 = s.r;
     a.TB0 = B_d; a.ldtb = s.m; a.tbstride = (long)r * m;
     a.C = f.o; a.ldc = s.m;
-    HIP_TRY(gemm_gm_launch(a, LAYOUT_KX, EPI_STORE, 0, s.dtype, Pi, ref, hs));
+    STAGE(ST_FWD_DOWN, gemm_gm_launch(a, LAYOUT_KX, EPI_STORE, 0, s.dtype, Pi, ref, hs));
   }
   // combine
-  HIP_TRY(launch_combine(s.dtype, f.o, inv_perm, topk_w, Y, s.s, s.k, s.m, hs));
+  STAGE(ST_FWD_COMBINE, launch_combine(s.dtype, f.o, inv_perm, topk_w, Y, s.s, s.k, s.m, hs));
   return MOE_OK;
 }
 
@@ -368,11 +438,11 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
   const size_t es = esize(s);
 
   // combine backward: dO = s_{t,j} dY_t, ds_{t,j} = dY_t . o_{t,j}
-  HIP_TRY(launch_combine_bwd(s.dtype, dY, f.o, perm, topk_w, b.dO, b.ds, Pi, s.k, s.m, hs));
+  STAGE(ST_BWD_COMBINE, launch_combine_bwd(s.dtype, dY, f.o, perm, topk_w, b.dO, b.ds, Pi, s.k, s.m, hs));
   // router backward: dz on the selected logits; W_r^T rows for the unpermute
   if (s.router_grad) {
-    HIP_TRY(launch_router_bwd(b.ds, topk_w, rs.psel, s.s, s.k, s.score, s.renormalize, b.dz, hs));
-    HIP_TRY(launch_transpose(s.dtype, W_r, b.WrT, s.m, s.E, hs));
+    STAGE(ST_BWD_ROUTER, launch_router_bwd(b.ds, topk_w, rs.psel, s.s, s.k, s.score, s.renormalize, b.dz, hs));
+    STAGE(ST_BWD_ROUTER, launch_transpose(s.dtype, W_r, b.WrT, s.m, s.E, hs));
   }
 
   GemmArgs base = gemm_args();
@@ -387,7 +457,7 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
     a.A = b.dO; a.lda = s.m;
     a.B = B_d; a.ldb = s.m; a.bstride = (long)r * m;
     a.C = b.Ud; a.ldc = s.r; a.scale = c;
-    HIP_TRY(gemm_gm_launch(a, LAYOUT_XK, EPI_STORE, 0, s.dtype, Pi, ref, hs));
+    STAGE(ST_BWD_U_D, gemm_gm_launch(a, LAYOUT_XK, EPI_STORE, 0, s.dtype, Pi, ref, hs));
   }
   // dh = dO W_d^T + Uc_d A_d^T, then SwiGLU backward -> dgu = [dg | du]
   {
@@ -400,7 +470,7 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
     a.TB0 = A_d; a.ldtb = s.r; a.tbstride = (long)n * r;
     a.GU = f.gu; a.ldgu = 2 * s.n; a.guup = s.n;
     a.C = b.dgu; a.ldc = 2 * s.n; a.cup = s.n;
-    HIP_TRY(gemm_gm_launch(a, LAYOUT_XK, EPI_SWIGLU_BWD, 0, s.dtype, Pi, ref, hs));
+    STAGE(ST_BWD_DOWN, gemm_gm_launch(a, LAYOUT_XK, EPI_SWIGLU_BWD, 0, s.dtype, Pi, ref, hs));
   }
   // dA_d = h^T Uc_d ;  dB_d = Tc_d^T dO  (computed as (dO^T Tc_d)^T)
   {
@@ -410,12 +480,12 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
     a.A = f.h; a.lda = s.n;
     a.B = b.Ud; a.ldb = s.r;
     a.C = dA_d; a.ldc = s.r; a.cstride = (long)n * r;
-    HIP_TRY(gemm_gk_launch(a, s.dtype, ref, hs));
+    STAGE(ST_BWD_GRAD_D, gemm_gk_launch(a, s.dtype, ref, hs));
     a.M = s.m; a.N = s.r;
     a.A = b.dO; a.lda = s.m;
     a.B = f.Td; a.ldb = s.r;
     a.C = dB_d; a.ldc = s.m; a.cstride = (long)r * m; a.ctrans = 1;
-    HIP_TRY(gemm_gk_launch(a, s.dtype, ref, hs));
+    STAGE(ST_BWD_GRAD_D, gemm_gk_launch(a, s.dtype, ref, hs));
   }
   // Uc_gu = c * [dg B_g^T | du B_u^T]
   {
@@ -424,11 +494,11 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
     a.A = b.dgu; a.lda = 2 * s.n;
     a.B = B_g; a.ldb = s.n; a.bstride = (long)r * n;
     a.C = b.Ugu; a.ldc = 2 * s.r; a.scale = c;
-    HIP_TRY(gemm_gm_launch(a, LAYOUT_XK, EPI_STORE, 0, s.dtype, Pi, ref, hs));
+    STAGE(ST_BWD_U_GU, gemm_gm_launch(a, LAYOUT_XK, EPI_STORE, 0, s.dtype, Pi, ref, hs));
     a.A = (const char*)b.dgu + n * es;
     a.B = B_u;
     a.C = (char*)b.Ugu + r * es;
-    HIP_TRY(gemm_gm_launch(a, LAYOUT_XK, EPI_STORE, 0, s.dtype, Pi, ref, hs));
+    STAGE(ST_BWD_U_GU, gemm_gm_launch(a, LAYOUT_XK, EPI_STORE, 0, s.dtype, Pi, ref, hs));
   }
   // dXp = dgu W_gu^T + Uc_g A_g^T + Uc_u A_u^T
   {
@@ -440,7 +510,7 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
     a.TA = b.Ugu; a.lda2 = 2 * s.r;
     a.TB0 = A_g; a.TB1 = A_u; a.ldtb = s.r; a.tbstride = (long)m * r;
     a.C = b.dXp; a.ldc = s.m;
-    HIP_TRY(gemm_gm_launch(a, LAYOUT_XK, EPI_STORE, 0, s.dtype, Pi, ref, hs));
+    STAGE(ST_BWD_GATE_UP, gemm_gm_launch(a, LAYOUT_XK, EPI_STORE, 0, s.dtype, Pi, ref, hs));
   }
   // dA_g | dA_u = Xp^T [Uc_g | Uc_u] ;  dB_g = Tc_g^T dg, dB_u = Tc_u^T du
   {
@@ -450,23 +520,60 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
     a.A = f.Xp; a.lda = s.m;
     a.B = b.Ugu; a.ldb = 2 * s.r;
     a.C = dA_g; a.C1 = dA_u; a.nsplit = s.r; a.ldc = s.r; a.cstride = (long)m * r;
-    HIP_TRY(gemm_gk_launch(a, s.dtype, ref, hs));
+    STAGE(ST_BWD_GRAD_GU, gemm_gk_launch(a, s.dtype, ref, hs));
     GemmArgs bg = base;
     bg.toff_all = nullptr;
     bg.M = s.n; bg.N = s.r;
     bg.A = b.dgu; bg.lda = 2 * s.n;
     bg.B = f.Tgu; bg.ldb = 2 * s.r;
     bg.C = dB_g; bg.ldc = s.n; bg.cstride = (long)r * n; bg.ctrans = 1;
-    HIP_TRY(gemm_gk_launch(bg, s.dtype, ref, hs));
+    STAGE(ST_BWD_GRAD_GU, gemm_gk_launch(bg, s.dtype, ref, hs));
     bg.A = (const char*)b.dgu + n * es;
     bg.B = (const char*)f.Tgu + r * es;
     bg.C = dB_u;
-    HIP_TRY(gemm_gk_launch(bg, s.dtype, ref, hs));
+    STAGE(ST_BWD_GRAD_GU, gemm_gk_launch(bg, s.dtype, ref, hs));
   }
   // unpermute: dX[t] = sum_j dXp[inv[t k + j]] (+ sum_j dz[t,j] W_r[:, idx[t,j]])
-  HIP_TRY(launch_unpermute(s.dtype, b.dXp, inv_perm, s.router_grad ? b.dz : nullptr, topk_idx,
+  STAGE(ST_BWD_UNPERMUTE, launch_unpermute(s.dtype, b.dXp, inv_perm, s.router_grad ? b.dz : nullptr, topk_idx,
                            b.WrT, dX, s.s, s.k, s.m, hs));
   return MOE_OK;
+}
+
+moe_status moe_timing_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  g_timing.on = on != 0;
+  return MOE_OK;
+}
+
+int32_t moe_timing_stage_count(void) { return ST_COUNT; }
+
+const char* moe_timing_stage_name(int32_t stage) {
+  return (stage >= 0 && stage < ST_COUNT) ? kStageNames[stage] : nullptr;
+}
+
+moe_status moe_timing_read(double* total_ms, int64_t* counts, int32_t nstages) {
+  if (!total_ms || !counts || nstages < ST_COUNT) return MOE_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  moe_status st = MOE_OK;
+  for (auto& p : g_timing.pending) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(p.e) != hipSuccess || hipEventElapsedTime(&ms, p.b, p.e) != hipSuccess) {
+      st = MOE_ERR_HIP;
+    } else {
+      g_timing.total_ms[p.stage] += ms;
+      g_timing.count[p.stage] += 1;
+    }
+    g_timing.pool.push_back(p.b);
+    g_timing.pool.push_back(p.e);
+  }
+  g_timing.pending.clear();
+  for (int i = 0; i < ST_COUNT; i++) {
+    total_ms[i] = g_timing.total_ms[i];
+    counts[i] = g_timing.count[i];
+    g_timing.total_ms[i] = 0.0;
+    g_timing.count[i] = 0;
+  }
+  return st;
 }
 
 }  // extern "C"

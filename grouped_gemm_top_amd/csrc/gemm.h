@@ -84,8 +84,8 @@ hipError_t gemm_gm_launch(const GemmArgs& a, int b_layout, int epi, int out_f32,
 hipError_t gemm_gk_launch(const GemmArgs& a, int dtype, int reference, hipStream_t stream);
 
 // Row-tile tables for the MFMA row tile sizes used by gemm_gm_launch.
-constexpr int kNumTileSizes = 3;
-constexpr int kTileSizes[kNumTileSizes] = {32, 64, 128};
+constexpr int kNumTileSizes = 4;
+constexpr int kTileSizes[kNumTileSizes] = {32, 64, 128, 256};
 int tile_table_index(int bm);
 
 }  // namespace moe

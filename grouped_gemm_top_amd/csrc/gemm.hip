@@ -13,6 +13,7 @@
 // and as a reference for the MFMA kernels.
 #include "gemm.h"
 #include <algorithm>
+#include <type_traits>
 
 namespace moe {
 
@@ -51,6 +52,15 @@ __device__ inline bf16x8_t frag_kx(const bf16_t* tile, int LD, int x0, int k0, i
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [0, N).
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
 __device__ inline i32x4_t ld16(const bf16_t* p) { return *reinterpret_cast<const i32x4_t*>(p); }
 
 __device__ inline float silu_f(float g) { return g / (1.0f + __expf(-g)); }
@@ -68,24 +78,87 @@ __device__ inline int xcd_unit(int total) {
 
 // ------------------------------------------------------------------------------------------------
 // Row-grouped MFMA GEMM.
-template <int WM, int WN, int TM, int TN, int BL, int EPI, typename OutT>
+//
+// LDS tiles are unpadded and XOR-swizzled at 16-byte-chunk granularity so that global->LDS copies
+// can use gfx950's direct-to-LDS loads (global_load_lds_dwordx4: lane L of a wave instruction
+// writes the L-th 16-byte chunk of a contiguous 1 KB LDS span, so each lane fetches whichever global
+// chunk belongs at that position). Tiles whose reduction axis is contiguous hold 8 chunks per row
+// (BK = 64) with chunk q of row x at q ^ swz_xk(x); tiles whose output axis is contiguous hold
+// BN/8 chunks per row with chunk q of row k at q ^ swz_kx(k).
+// XOR swizzles (measured conflict-free on gfx950, whose LDS serves 256 bytes per clock: 16 lanes per
+// cycle for ds_read_b128, 32 lanes per cycle for ds_read_b64_tr_b16).
+// XK tiles (CPR chunks per row): the 16 rows read together by one MFMA fragment must land on
+// distinct 16-byte bank groups of each 256-byte window.
+template <int CPR>
+__host__ __device__ constexpr int swz_xk(int x) { return CPR >= 8 ? ((x >> 1) & 7) : ((x >> 2) & 3); }
+// KX tiles: one transposing read covers 4 rows x 4 chunks per 32 lanes; those 16 chunks must be
+// distinct modulo 16.
+template <int CPR>
+__host__ __device__ constexpr int swz_kx(int k) {
+  return CPR >= 16 ? 4 * (k & 3) : (CPR == 8 ? 4 * ((k >> 1) & 1) : 0);
+}
+
+// Fragment from an XK tile with BKT elements per row (chunk q of row x at q ^ swz_xk(x)).
+template <int BKT>
+__device__ inline bf16x8_t frag_xk_s(const bf16_t* tile, int x0, int k0, int lane) {
+  const int x = x0 + (lane & 31);
+  const int q = (k0 >> 3) + (lane >> 5);
+  return *reinterpret_cast<const bf16x8_t*>(tile + x * BKT + ((q ^ swz_xk<BKT / 8>(x)) << 3));
+}
+
+// Fragment from a KX tile with X elements per row (chunk q of row k at q ^ swz_kx(k)).
+template <int X>
+__device__ inline bf16x8_t frag_kx_s(const bf16_t* tile, int x0, int k0, int lane) {
+  constexpr int CPR = X / 8;
+  const int g = lane >> 4, b = (lane >> 2) & 3, c = lane & 3;
+  const int k = k0 + 8 * (g >> 1) + b;
+  const int x = x0 + 16 * (g & 1) + 4 * c;
+  const int off = (((x >> 3) ^ swz_kx<CPR>(k)) << 3) + (x & 7);  // same swizzle for rows k, k + 4
+  bf16x4_t lo = lds_read_tr(tile + k * X + off);
+  bf16x4_t hi = lds_read_tr(tile + (k + 4) * X + off);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+typedef __attribute__((address_space(1))) void gbl_void_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One 16-byte chunk per lane straight into LDS at lds_wave_base + 16 * lane.
+__device__ inline void dma16(const bf16_t* src, bf16_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)(lds_bf16_t*)lds_wave_base, 16, 0, 0);
+}
+
+// Wait until at most N of this wave's vector-memory operations are outstanding.
+template <int N>
+__device__ inline void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+// Row-grouped MFMA GEMM.
+//
+// K tiles of BKT stream through two LDS stages with gfx950's direct-to-LDS loads
+// (global_load_lds_dwordx4: lane L of a wave instruction writes the L-th 16-byte chunk of a
+// contiguous 1 KB LDS span, so each lane fetches whichever global chunk belongs at that position):
+// the loads of tile kt+1 run while tile kt is multiplied. LDS tiles are unpadded and XOR-swizzled at
+// 16-byte chunk granularity against bank conflicts of the fragment reads.
+template <int WM, int WN, int TM, int TN, int BKT, int S, int BL, int EPI, typename OutT, bool TAIL>
 __global__ __launch_bounds__(WM * WN * 64) void gm_mfma(GemmArgs a, int tidx) {
   constexpr bool DUAL = (EPI == EPI_DUAL || EPI == EPI_SWIGLU);
-  constexpr int BM = WM * TM * 32, BN = WN * TN * 32, NT = WM * WN * 64;
+  constexpr int BM = WM * TM * 32, BN = WN * TN * 32, NW = WM * WN;
   constexpr int BNH = DUAL ? BN / 2 : BN;
-  constexpr int LDA = BK + PADE;
-  constexpr int LDB = (BL == LAYOUT_XK) ? BK + PADE : BN + PADE;
-  constexpr int A_ELEMS = BM * LDA;
-  constexpr int B_ELEMS = (BL == LAYOUT_XK) ? BN * LDB : BK * LDB;
-  constexpr int STAGE = A_ELEMS + B_ELEMS;
-  constexpr int A_PT = BM * BK / 8 / NT;
-  constexpr int B_PT = BN * BK / 8 / NT;
-  constexpr int CPR_B = BN / 8;  // chunks per KX B row
-  static_assert((BM * BK / 8) % NT == 0 && (BN * BK / 8) % NT == 0, "tile/thread mismatch");
+  constexpr int CPR_A = BKT / 8;                                 // chunks per XK row
+  constexpr int CPR_B = BN / 8;                                  // chunks per KX B row
+  constexpr int A_ELEMS = BM * BKT, B_ELEMS = BN * BKT, STAGE = A_ELEMS + B_ELEMS;
+  constexpr int A_IPW = BM * BKT / 8 / 64 / NW;                  // DMA instructions per wave
+  constexpr int B_IPW = BN * BKT / 8 / 64 / NW;
+  constexpr int IPW = A_IPW + B_IPW;
+  constexpr int TAIL_STEPS = 64 / BKT;                           // LoRA tail: up to 64 reduction rows
+  static_assert(A_IPW * 64 * NW * 8 == BM * BKT && B_IPW * 64 * NW * 8 == BN * BKT, "tile/wave mismatch");
   static_assert(!DUAL || (TN % 2 == 0), "dual epilogue needs an even TN");
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * STAGE];
+  static_assert(BL == LAYOUT_XK || CPR_B >= 4, "KX tiles need >= 4 chunks per row");
+  static_assert(S == 2, "two LDS stages");
+  static_assert(!TAIL || TAIL_STEPS <= S, "tail tiles reuse the ring stages");
+  extern __shared__ __attribute__((aligned(16))) bf16_t smem[];  // S * STAGE elements
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
   // ---- which (group, row tile, column tile)
@@ -115,37 +188,40 @@ __global__ __launch_bounds__(WM * WN * 64) void gm_mfma(GemmArgs a, int tidx) {
   }
   const int j0 = nt * BNH;
 
-  // ---- per-thread global chunk pointers
-  const bf16_t* aptr[A_PT];
-  int arowc[A_PT];
+  // ---- per-lane source offsets of the chunks this lane moves (32-bit; the shape limits keep them
+  //      below 2^31)
+  const bf16_t* Ab = (const bf16_t*)a.A;
+  int aoff[A_IPW];
 #pragma unroll
-  for (int u = 0; u < A_PT; u++) {
-    const int c = tid + u * NT;
-    const int row = min(row0 + (c >> 3), row_end - 1);
-    arowc[u] = row;
-    const long src = a.arow ? (long)(a.arow[row] / a.arow_div) : (long)row;
-    aptr[u] = (const bf16_t*)a.A + src * a.lda + (c & 7) * 8;
+  for (int i = 0; i < A_IPW; i++) {
+    const int P = (wave * A_IPW + i) * 64 + lane;
+    const int x = P / CPR_A, q = (P % CPR_A) ^ swz_xk<CPR_A>(x);
+    const int row = min(row0 + x, row_end - 1);
+    const int src = a.arow ? a.arow[row] / a.arow_div : row;
+    aoff[i] = src * (int)a.lda + q * 8;
   }
   const bf16_t* Bg = (const bf16_t*)a.B + (long)e * a.bstride;
   const bf16_t* Bug = DUAL ? (const bf16_t*)a.Bu + (long)e * a.bstride : nullptr;
-  const bf16_t* bptr[B_PT];
+  int boff[B_IPW];
+  bool bup[B_IPW];
 #pragma unroll
-  for (int u = 0; u < B_PT; u++) {
-    const int c = tid + u * NT;
+  for (int i = 0; i < B_IPW; i++) {
+    const int P = (wave * B_IPW + i) * 64 + lane;
     if (BL == LAYOUT_KX) {
-      const int kk = c / CPR_B, x = (c % CPR_B) * 8;
+      const int k = P / CPR_B, x = ((P % CPR_B) ^ swz_kx<CPR_B>(k)) * 8;
       const int half = DUAL ? (x >= BNH) : 0;
       const int jj = min(j0 + x - half * BNH, a.N - 8);
-      bptr[u] = (half ? Bug : Bg) + (long)kk * a.ldb + jj;
+      bup[i] = half;
+      boff[i] = k * (int)a.ldb + jj;
     } else {
-      const int x = c >> 3, q = c & 7;
+      const int x = P / CPR_A, q = (P % CPR_A) ^ swz_xk<CPR_A>(x);
       const int half = DUAL ? (x >= BNH) : 0;
       const int jj = min(j0 + x - half * BNH, a.N - 1);
-      bptr[u] = (half ? Bug : Bg) + (long)jj * a.ldb + q * 8;
+      bup[i] = half;
+      boff[i] = jj * (int)a.ldb + q * 8;
     }
   }
 
-  i32x4_t ra[A_PT], rb[B_PT];
   f32x16_t acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; i++)
@@ -154,29 +230,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gm_mfma(GemmArgs a, int tidx) {
 #pragma unroll
       for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
 
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int u = 0; u < A_PT; u++) ra[u] = ld16(aptr[u] + k0);
-#pragma unroll
-    for (int u = 0; u < B_PT; u++)
-      rb[u] = ld16(bptr[u] + (BL == LAYOUT_KX ? (long)k0 * a.ldb : (long)k0));
-  };
-  auto sstore = [&](int buf) {
-    bf16_t* sA = smem + buf * STAGE;
+  // DMA of one K tile into the stage at sA (A tile) / sA + A_ELEMS (B tile)
+  auto issue = [&](bf16_t* sA, int k0) {
     bf16_t* sB = sA + A_ELEMS;
 #pragma unroll
-    for (int u = 0; u < A_PT; u++) {
-      const int c = tid + u * NT;
-      *reinterpret_cast<i32x4_t*>(sA + (c >> 3) * LDA + (c & 7) * 8) = ra[u];
-    }
+    for (int i = 0; i < A_IPW; i++) dma16(Ab + aoff[i] + k0, sA + (wave * A_IPW + i) * 512);
+    const int kb = (BL == LAYOUT_KX) ? k0 * (int)a.ldb : k0;
 #pragma unroll
-    for (int u = 0; u < B_PT; u++) {
-      const int c = tid + u * NT;
-      if (BL == LAYOUT_KX)
-        *reinterpret_cast<i32x4_t*>(sB + (c / CPR_B) * LDB + (c % CPR_B) * 8) = rb[u];
-      else
-        *reinterpret_cast<i32x4_t*>(sB + (c >> 3) * LDB + (c & 7) * 8) = rb[u];
-    }
+    for (int i = 0; i < B_IPW; i++)
+      dma16((bup[i] ? Bug : Bg) + boff[i] + kb, sB + (wave * B_IPW + i) * 512);
   };
   auto wcol = [&](int tn) {
     if constexpr (DUAL) {
@@ -186,130 +248,167 @@ __global__ __launch_bounds__(WM * WN * 64) void gm_mfma(GemmArgs a, int tidx) {
       return wn * TN * 32 + tn * 32;
     }
   };
-  auto compute = [&](int buf) {
-    const bf16_t* sA = smem + buf * STAGE;
+  auto frags = [&](const bf16_t* sA, const bf16_t* sB, int ks, bf16x8_t* fa, bf16x8_t* fb) {
+#pragma unroll
+    for (int tm = 0; tm < TM; tm++) fa[tm] = frag_xk_s<BKT>(sA, wm * TM * 32 + tm * 32, ks * 16, lane);
+#pragma unroll
+    for (int tn = 0; tn < TN; tn++)
+      fb[tn] = (BL == LAYOUT_XK) ? frag_xk_s<BKT>(sB, wcol(tn), ks * 16, lane)
+                                 : frag_kx_s<BN>(sB, wcol(tn), ks * 16, lane);
+  };
+  auto mma = [&](const bf16x8_t* fa, const bf16x8_t* fb) {
+    static_for<TM>([&](auto tmc) {
+      constexpr int tm = decltype(tmc)::value;
+      static_for<TN>([&](auto tnc) {
+        constexpr int tn = decltype(tnc)::value;
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[tm], fb[tn], acc[tm][tn], 0, 0, 0);
+      });
+    });
+  };
+  // fragments of k16 step ks+1 are read while the MFMAs of step ks run
+  auto compute = [&](const bf16_t* sA) {
     const bf16_t* sB = sA + A_ELEMS;
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ks++) {
-      bf16x8_t fa[TM], fb[TN];
-#pragma unroll
-      for (int tm = 0; tm < TM; tm++) fa[tm] = frag_xk(sA, LDA, wm * TM * 32 + tm * 32, ks * 16, lane);
-#pragma unroll
-      for (int tn = 0; tn < TN; tn++)
-        fb[tn] = (BL == LAYOUT_XK) ? frag_xk(sB, LDB, wcol(tn), ks * 16, lane)
-                                   : frag_kx(sB, LDB, wcol(tn), ks * 16, lane);
-#pragma unroll
-      for (int tm = 0; tm < TM; tm++)
-#pragma unroll
-        for (int tn = 0; tn < TN; tn++)
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[tm], fb[tn], acc[tm][tn], 0, 0, 0);
-    }
+    bf16x8_t fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+    frags(sA, sB, 0, fa0, fb0);
+    static_for<BKT / 32>([&](auto kc) {
+      constexpr int ks = 2 * decltype(kc)::value;
+      frags(sA, sB, ks + 1, fa1, fb1);
+      mma(fa0, fb0);
+      if constexpr (ks + 2 < BKT / 16) frags(sA, sB, ks + 2, fa0, fb0);
+      mma(fa1, fb1);
+    });
+  };
+  // One pipeline step: DMA of the next tile into `next` while the tile in `cur` is multiplied. The
+  // two stages are distinct, and saying so (__restrict__) lets the compiler keep the DMA in flight
+  // across the LDS fragment reads instead of draining it first.
+  auto step = [&](bf16_t* __restrict__ next, const bf16_t* __restrict__ cur, int k0_next) {
+    if (k0_next >= 0) issue(next, k0_next);
+    compute(cur);
   };
 
-  const int nk = a.K / BK;
-  gload(0);
-  sstore(0);
+  // ---- main K loop: loads of tile kt+1 in flight while tile kt is multiplied
+  const int nk = a.K / BKT;
+  bf16_t* const stage0 = smem;
+  bf16_t* const stage1 = smem + STAGE;
+  issue(stage0, 0);
+  wait_vm<0>();
   __syncthreads();
-  for (int kt = 0; kt < nk; kt++) {
-    if (kt + 1 < nk) gload((kt + 1) * BK);
-    compute(kt & 1);
-    if (kt + 1 < nk) sstore((kt + 1) & 1);
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(stage1, stage0, kt + 1 < nk ? (kt + 1) * BKT : -1);
+    wait_vm<0>();
     __syncthreads();
+    if (kt + 1 < nk) {
+      step(stage0, stage1, kt + 2 < nk ? (kt + 2) * BKT : -1);
+      wait_vm<0>();
+      __syncthreads();
+    }
   }
 
-  // ---- Split-LoRA tail: one more K tile [TA | 0] . [TB ; 0]
-  if (a.tail != TAIL_NONE) {
+  // ---- Split-LoRA tail: TAIL_STEPS more K tiles [TA | 0] . [TB ; 0], zero-filled via registers
+  if constexpr (TAIL) {
     const int r2 = a.r2a;
     const int K2 = (a.tail == TAIL_SINGLE) ? r2 : 2 * r2;
     const i32x4_t zero = {0, 0, 0, 0};
-#pragma unroll
-    for (int u = 0; u < A_PT; u++) {
-      const int q = (tid + u * NT) & 7;
-      ra[u] = (q * 8 < K2) ? ld16((const bf16_t*)a.TA + (long)arowc[u] * a.lda2 + q * 8) : zero;
-    }
     const bf16_t* T0 = (const bf16_t*)a.TB0 + (long)e * a.tbstride;
     const bf16_t* T1 = a.TB1 ? (const bf16_t*)a.TB1 + (long)e * a.tbstride : nullptr;
+    static_for<TAIL_STEPS>([&](auto tc) {
+      constexpr int ts = decltype(tc)::value;
+      bf16_t* sA = smem + ts * STAGE;
+      bf16_t* sB = sA + A_ELEMS;
 #pragma unroll
-    for (int u = 0; u < B_PT; u++) {
-      const int c = tid + u * NT;
-      const bf16_t* src = nullptr;
-      if (BL == LAYOUT_KX) {
-        const int kk = c / CPR_B, x = (c % CPR_B) * 8;
-        const int half = DUAL ? (x >= BNH) : 0;
-        const int jj = min(j0 + x - half * BNH, a.N - 8);
-        if (a.tail == TAIL_SINGLE) {
-          if (kk < r2) src = T0 + (long)kk * a.ldtb + jj;
-        } else if (a.tail == TAIL_BLOCKDIAG) {
-          if (half == 0 && kk < r2) src = T0 + (long)kk * a.ldtb + jj;
-          else if (half == 1 && kk >= r2 && kk < 2 * r2) src = T1 + (long)(kk - r2) * a.ldtb + jj;
-        } else {
-          if (kk < r2) src = T0 + (long)kk * a.ldtb + jj;
-          else if (kk < 2 * r2) src = T1 + (long)(kk - r2) * a.ldtb + jj;
-        }
-      } else {
-        const int x = c >> 3, k8 = (c & 7) * 8;
-        const int half = DUAL ? (x >= BNH) : 0;
-        const int jj = min(j0 + x - half * BNH, a.N - 1);
-        if (a.tail == TAIL_SINGLE) {
-          if (k8 < r2) src = T0 + (long)jj * a.ldtb + k8;
-        } else if (a.tail == TAIL_BLOCKDIAG) {
-          if (half == 0 && k8 < r2) src = T0 + (long)jj * a.ldtb + k8;
-          else if (half == 1 && k8 >= r2 && k8 < 2 * r2) src = T1 + (long)jj * a.ldtb + (k8 - r2);
-        } else {
-          if (k8 < r2) src = T0 + (long)jj * a.ldtb + k8;
-          else if (k8 < 2 * r2) src = T1 + (long)jj * a.ldtb + (k8 - r2);
-        }
+      for (int i = 0; i < A_IPW; i++) {
+        const int P = (wave * A_IPW + i) * 64 + lane;
+        const int x = P / CPR_A, q = ((P % CPR_A) ^ swz_xk<CPR_A>(x)) + ts * CPR_A;
+        const int row = min(row0 + x, row_end - 1);
+        *reinterpret_cast<i32x4_t*>(sA + P * 8) =
+            (q * 8 < K2) ? ld16((const bf16_t*)a.TA + (long)row * a.lda2 + q * 8) : zero;
       }
-      rb[u] = src ? ld16(src) : zero;
-    }
-    sstore(nk & 1);
+#pragma unroll
+      for (int i = 0; i < B_IPW; i++) {
+        const int P = (wave * B_IPW + i) * 64 + lane;
+        const bf16_t* src = nullptr;
+        if (BL == LAYOUT_KX) {
+          const int kk = P / CPR_B + ts * BKT, x = ((P % CPR_B) ^ swz_kx<CPR_B>(P / CPR_B)) * 8;
+          const int half = DUAL ? (x >= BNH) : 0;
+          const int jj = min(j0 + x - half * BNH, a.N - 8);
+          if (a.tail == TAIL_SINGLE) {
+            if (kk < r2) src = T0 + (long)kk * a.ldtb + jj;
+          } else if (a.tail == TAIL_BLOCKDIAG) {
+            if (half == 0 && kk < r2) src = T0 + (long)kk * a.ldtb + jj;
+            else if (half == 1 && kk >= r2 && kk < 2 * r2) src = T1 + (long)(kk - r2) * a.ldtb + jj;
+          } else {
+            if (kk < r2) src = T0 + (long)kk * a.ldtb + jj;
+            else if (kk < 2 * r2) src = T1 + (long)(kk - r2) * a.ldtb + jj;
+          }
+        } else {
+          const int x = P / CPR_A;
+          const int k8 = (((P % CPR_A) ^ swz_xk<CPR_A>(x)) + ts * CPR_A) * 8;
+          const int half = DUAL ? (x >= BNH) : 0;
+          const int jj = min(j0 + x - half * BNH, a.N - 1);
+          if (a.tail == TAIL_SINGLE) {
+            if (k8 < r2) src = T0 + (long)jj * a.ldtb + k8;
+          } else if (a.tail == TAIL_BLOCKDIAG) {
+            if (half == 0 && k8 < r2) src = T0 + (long)jj * a.ldtb + k8;
+            else if (half == 1 && k8 >= r2 && k8 < 2 * r2) src = T1 + (long)jj * a.ldtb + (k8 - r2);
+          } else {
+            if (k8 < r2) src = T0 + (long)jj * a.ldtb + k8;
+            else if (k8 < 2 * r2) src = T1 + (long)jj * a.ldtb + (k8 - r2);
+          }
+        }
+        *reinterpret_cast<i32x4_t*>(sB + P * 8) = src ? ld16(src) : zero;
+      }
+    });
     __syncthreads();
-    compute(nk & 1);
+    static_for<TAIL_STEPS>([&](auto tc) { compute(smem + decltype(tc)::value * STAGE); });
   }
 
-  // ---- epilogue
+  // ---- epilogue (compile-time accumulator indices; one 32-row MFMA tile row at a time)
   OutT* C = (OutT*)a.C;
-#pragma unroll
-  for (int tm = 0; tm < TM; tm++) {
-#pragma unroll
-    for (int v = 0; v < 16; v++) {
+  static_for<TM>([&](auto tmc) {
+    constexpr int tm = decltype(tmc)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<16>([&](auto vc) {
+      constexpr int v = decltype(vc)::value;
       const int row = row0 + wm * TM * 32 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (row >= row_end) continue;
-      if constexpr (DUAL) {
-#pragma unroll
-        for (int t2 = 0; t2 < TN / 2; t2++) {
-          const int jj = j0 + wn * (TN / 2) * 32 + t2 * 32 + (lane & 31);
-          if (jj >= a.N) continue;
-          const float g = acc[tm][t2][v], uu = acc[tm][t2 + TN / 2][v];
-          if (EPI == EPI_DUAL) {
-            C[(long)row * a.ldc + jj] = from_f<OutT>(a.scale * g);
-            C[(long)row * a.ldc + a.cup + jj] = from_f<OutT>(a.scale * uu);
-          } else {
-            C[(long)row * a.ldc + jj] = from_f<OutT>(g);
-            C[(long)row * a.ldc + a.cup + jj] = from_f<OutT>(uu);
-            ((OutT*)a.H)[(long)row * a.ldh + jj] = from_f<OutT>(silu_f(g) * uu);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int tn = 0; tn < TN; tn++) {
-          const int jj = j0 + wn * TN * 32 + tn * 32 + (lane & 31);
-          if (jj >= a.N) continue;
-          const float val = a.scale * acc[tm][tn][v];
-          if (EPI == EPI_STORE) {
-            C[(long)row * a.ldc + jj] = from_f<OutT>(val + (a.bias ? a.bias[jj] : 0.0f));
-          } else {  // EPI_SWIGLU_BWD
-            const OutT* GU = (const OutT*)a.GU;
-            const float g = to_f(GU[(long)row * a.ldgu + jj]);
-            const float uu = to_f(GU[(long)row * a.ldgu + a.guup + jj]);
-            const float sg = 1.0f / (1.0f + __expf(-g));
-            C[(long)row * a.ldc + jj] = from_f<OutT>(val * uu * sg * (1.0f + g * (1.0f - sg)));
-            C[(long)row * a.ldc + a.cup + jj] = from_f<OutT>(val * g * sg);
-          }
+      if (row < row_end) {
+        if constexpr (DUAL) {
+          static_for<TN / 2>([&](auto tc) {
+            constexpr int t2 = decltype(tc)::value;
+            const int jj = j0 + wn * (TN / 2) * 32 + t2 * 32 + (lane & 31);
+            if (jj < a.N) {
+              const float g = acc[tm][t2][v], uu = acc[tm][t2 + TN / 2][v];
+              if constexpr (EPI == EPI_DUAL) {
+                C[(long)row * a.ldc + jj] = from_f<OutT>(a.scale * g);
+                C[(long)row * a.ldc + a.cup + jj] = from_f<OutT>(a.scale * uu);
+              } else {
+                C[(long)row * a.ldc + jj] = from_f<OutT>(g);
+                C[(long)row * a.ldc + a.cup + jj] = from_f<OutT>(uu);
+                ((OutT*)a.H)[(long)row * a.ldh + jj] = from_f<OutT>(silu_f(g) * uu);
+              }
+            }
+          });
+        } else {
+          static_for<TN>([&](auto tc) {
+            constexpr int tn = decltype(tc)::value;
+            const int jj = j0 + wn * TN * 32 + tn * 32 + (lane & 31);
+            if (jj < a.N) {
+              const float val = a.scale * acc[tm][tn][v];
+              if constexpr (EPI == EPI_STORE) {
+                C[(long)row * a.ldc + jj] = from_f<OutT>(val + (a.bias ? a.bias[jj] : 0.0f));
+              } else {  // EPI_SWIGLU_BWD
+                const OutT* GU = (const OutT*)a.GU;
+                const float g = to_f(GU[(long)row * a.ldgu + jj]);
+                const float uu = to_f(GU[(long)row * a.ldgu + a.guup + jj]);
+                const float sg = 1.0f / (1.0f + __expf(-g));
+                C[(long)row * a.ldc + jj] = from_f<OutT>(val * uu * sg * (1.0f + g * (1.0f - sg)));
+                C[(long)row * a.ldc + a.cup + jj] = from_f<OutT>(val * g * sg);
+              }
+            }
+          });
         }
       }
-    }
-  }
+    });
+  });
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -382,8 +481,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gk_mfma(GemmArgs a) {
       *reinterpret_cast<i32x4_t*>(sB + (c / CPR_B) * LDB + (c % CPR_B) * 8) = rb[u];
     }
   };
-  auto compute = [&](int buf) {
-    const bf16_t* sA = smem + buf * STAGE;
+  auto compute = [&](const bf16_t* sA) {
     const bf16_t* sB = sA + A_ELEMS;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ks++) {
@@ -407,7 +505,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gk_mfma(GemmArgs a) {
     __syncthreads();
     for (int kt = 0; kt < nk; kt++) {
       if (kt + 1 < nk) gload(kb + (kt + 1) * BK);
-      compute(kt & 1);
+      compute(smem + (kt & 1) * STAGE);
       if (kt + 1 < nk) sstore((kt + 1) & 1);
       __syncthreads();
     }
@@ -518,32 +616,58 @@ __global__ void gk_simt(GemmArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------
-template <int WM, int WN, int TM, int TN, int BL, int EPI, typename OutT>
-hipError_t launch_gm_mfma(const GemmArgs& a, int rows_bound, hipStream_t stream) {
+// Tile configuration of the row-grouped MFMA kernel: WM x WN waves, each TM x TN 32x32 MFMA tiles,
+// K tile BKT, S (= 2) LDS stages.
+template <int WM_, int WN_, int TM_, int TN_, int BKT_, int S_>
+struct TileCfg {
+  static constexpr int WM = WM_, WN = WN_, TM = TM_, TN = TN_, BKT = BKT_, S = S_;
+  static constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+  static constexpr size_t lds_bytes = (size_t)S * (BM + BN) * BKT * sizeof(bf16_t);
+};
+
+template <typename Cfg, int BL, int EPI, typename OutT, bool TAIL>
+hipError_t launch_gm_mfma_t(const GemmArgs& a, int rows_bound, hipStream_t stream) {
   constexpr bool DUAL = (EPI == EPI_DUAL || EPI == EPI_SWIGLU);
-  constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
-  constexpr int BNH = DUAL ? BN / 2 : BN;
+  constexpr int BNH = DUAL ? Cfg::BN / 2 : Cfg::BN;
+  auto kern = gm_mfma<Cfg::WM, Cfg::WN, Cfg::TM, Cfg::TN, Cfg::BKT, Cfg::S, BL, EPI, OutT, TAIL>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)Cfg::lds_bytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
   const int tilesN = (a.N + BNH - 1) / BNH;
-  const long mtiles = a.goff ? (long)rows_bound / BM + a.G : ((long)a.M + BM - 1) / BM;
+  const long mtiles = a.goff ? (long)rows_bound / Cfg::BM + a.G : ((long)a.M + Cfg::BM - 1) / Cfg::BM;
   const long units = mtiles * tilesN;
   if (units <= 0) return hipSuccess;
   const long blocks = (units + 7) / 8 * 8;
-  const int tidx = tile_table_index(BM);
+  const int tidx = tile_table_index(Cfg::BM);
   if (a.goff && tidx < 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gm_mfma<WM, WN, TM, TN, BL, EPI, OutT>), dim3((unsigned)blocks),
-                     dim3(WM * WN * 64), 0, stream, a, tidx);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(Cfg::WM * Cfg::WN * 64), Cfg::lds_bytes,
+                     stream, a, tidx);
   return hipGetLastError();
 }
+
+template <typename Cfg, int BL, int EPI, typename OutT>
+hipError_t launch_gm_mfma(const GemmArgs& a, int rows_bound, hipStream_t stream) {
+  if (a.tail != TAIL_NONE) return launch_gm_mfma_t<Cfg, BL, EPI, OutT, true>(a, rows_bound, stream);
+  return launch_gm_mfma_t<Cfg, BL, EPI, OutT, false>(a, rows_bound, stream);
+}
+
+using CfgSkinny = TileCfg<4, 1, 1, 1, 64, 2>;      // 128 x 32
+using CfgSkinnyDual = TileCfg<4, 1, 1, 2, 64, 2>;  // 128 x (32 + 32)
+using CfgMid = TileCfg<2, 2, 2, 2, 64, 2>;         // 128 x 128
 
 template <int BL, int EPI, typename OutT>
 hipError_t dispatch_gm_mfma(const GemmArgs& a, int rows_bound, hipStream_t stream) {
   constexpr bool DUAL = (EPI == EPI_DUAL || EPI == EPI_SWIGLU);
   if constexpr (DUAL) {
-    if (a.N <= 32) return launch_gm_mfma<4, 1, 1, 2, BL, EPI, OutT>(a, rows_bound, stream);
-    return launch_gm_mfma<2, 2, 2, 2, BL, EPI, OutT>(a, rows_bound, stream);
+    if (a.N <= 32) return launch_gm_mfma<CfgSkinnyDual, BL, EPI, OutT>(a, rows_bound, stream);
+    return launch_gm_mfma<CfgMid, BL, EPI, OutT>(a, rows_bound, stream);
   } else {
-    if (a.N <= 32) return launch_gm_mfma<4, 1, 1, 1, BL, EPI, OutT>(a, rows_bound, stream);
-    return launch_gm_mfma<2, 2, 2, 2, BL, EPI, OutT>(a, rows_bound, stream);
+    if (a.N <= 32) return launch_gm_mfma<CfgSkinny, BL, EPI, OutT>(a, rows_bound, stream);
+    return launch_gm_mfma<CfgMid, BL, EPI, OutT>(a, rows_bound, stream);
   }
 }
 

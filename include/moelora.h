@@ -16,7 +16,8 @@
  *
  * Conventions (all calls):
  *  - Tensors are caller-owned DEVICE pointers, dense row-major, 16-byte aligned. The library never
- *    allocates device memory, keeps no state between calls, never prints and never aborts.
+ *    allocates device memory, keeps no state between calls (apart from the opt-in stage timing
+ *    below), never prints and never aborts.
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream). Buffers must
  *    stay valid until the work on `stream` has finished.
  *  - All argument checks run on the host before anything is enqueued; on any error nothing is
@@ -144,6 +145,17 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
                              size_t saved_bytes, void* dX, float* dA_g, float* dB_g, float* dA_u,
                              float* dB_u, float* dA_d, float* dB_d, void* ws, size_t ws_bytes,
                              void* stream);
+
+/*
+ * Stage timing (diagnostics, off by default). While enabled, every call records a hipEvent pair on
+ * its stream around each kernel stage (host-side state in the library; no device memory).
+ * moe_timing_read waits for the recorded events, writes per-stage summed milliseconds and counts
+ * into arrays of nstages >= moe_timing_stage_count() entries, and resets the sums.
+ */
+moe_status moe_timing_enable(int32_t on);
+int32_t moe_timing_stage_count(void);
+const char* moe_timing_stage_name(int32_t stage); /* NULL for an out-of-range index */
+moe_status moe_timing_read(double* total_ms, int64_t* counts, int32_t nstages);
 
 #ifdef __cplusplus
 }
