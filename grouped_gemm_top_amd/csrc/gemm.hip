@@ -63,6 +63,36 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 __device__ inline i32x4_t ld16(const bf16_t* p) { return *reinterpret_cast<const i32x4_t*>(p); }
 
+#ifdef MOE_GEMM_BOUNDS_CHECK
+// Checking builds (test harnesses only): every global address of the streaming kernel must lie in
+// one of the registered allocations and every LDS address inside the kernel's LDS; a stray address
+// is replaced by a valid one and flagged in *err (bit 0 global, bit 1 LDS).
+struct GemmBounds {
+  const char* lo[32];
+  const char* hi[32];
+  int n;
+  unsigned* err;
+};
+__device__ GemmBounds g_gemm_bounds;
+__device__ inline const void* gchk(const void* p, int bytes) {
+  const char* c = (const char*)p;
+  for (int i = 0; i < g_gemm_bounds.n; i++)
+    if (c >= g_gemm_bounds.lo[i] && c + bytes <= g_gemm_bounds.hi[i]) return p;
+  atomicOr(g_gemm_bounds.err, 1u);
+  return g_gemm_bounds.lo[0];
+}
+__device__ inline int lchk(int byte_off, int bytes, int limit) {
+  if (byte_off < 0 || byte_off + bytes > limit) {
+    atomicOr(g_gemm_bounds.err, 2u);
+    return 0;
+  }
+  return byte_off;
+}
+#define GCHK(p, bytes) ((decltype(p))gchk((p), (bytes)))
+#else
+#define GCHK(p, bytes) (p)
+#endif
+
 __device__ inline float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
 // Maps blockIdx to a logical work unit so that each XCD (blockIdx % 8) receives a contiguous range
@@ -412,6 +442,298 @@ __global__ __launch_bounds__(WM * WN * 64) void gm_mfma(GemmArgs a, int tidx) {
 }
 
 // ------------------------------------------------------------------------------------------------
+// Row-grouped GEMM with a deep register prefetch, for the expert projections (the launches that carry
+// a Split-LoRA tail).
+//
+// Every weight byte of an expert meets only the few hundred rows routed to that expert, so these
+// GEMMs stream the expert weights from HBM at about the chip's MFMA/HBM balance point; what limits
+// them is how many bytes each CU keeps in flight. Both operand tiles are fetched with fully coalesced
+// 16-byte-per-lane loads (each wave instruction covers whole 128-byte lines) into a four-slot
+// register ring, three K tiles ahead of the MFMAs, and copied into a two-stage LDS buffer one tile
+// ahead. All loads are plain register loads, so the compiler's waits are exact and leave the later
+// tiles in flight; one barrier per tile (without a vector-memory drain) hands the LDS stages over.
+// Loads past the last tile repeat the last tile, so every step issues the same loads.
+//
+// The Split-LoRA tail (up to 128 reduction rows) follows as one or two more tiles through LDS,
+// filled with zeros beyond its length.
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int N_>
+using IC = std::integral_constant<int, N_>;
+
+template <int WM, int WN, int TM, int TN, int BL, int EPI>
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gm_ring(GemmArgs a, int tidx) {
+  constexpr int BKT = 64, NW = WM * WN, NT = NW * 64;
+  constexpr bool DUAL = (EPI == EPI_DUAL || EPI == EPI_SWIGLU);
+  constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+  constexpr int BNH = DUAL ? BN / 2 : BN;
+  constexpr int A_ELEMS = BM * BKT, STAGE = (BM + BN) * BKT;
+  constexpr int A_CPT = A_ELEMS / 8 / NT;           // 16-byte chunks per thread per tile
+  constexpr int B_CPT = BN * BKT / 8 / NT;
+  constexpr int CPR_A = BKT / 8;
+  constexpr int CPR_B = (BL == LAYOUT_KX) ? BN / 8 : BKT / 8;
+  constexpr int LDS_BYTES = 2 * STAGE * (int)sizeof(bf16_t);
+  static_assert(A_CPT * NT * 8 == A_ELEMS && B_CPT * NT * 8 == BN * BKT, "tile/thread mismatch");
+  static_assert(!DUAL || TN % 2 == 0, "dual epilogue needs an even TN");
+  static_assert(BL == LAYOUT_XK || CPR_B >= 8, "KX tiles need >= 8 chunks per row");
+  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * STAGE];
+#ifdef MOE_GEMM_BOUNDS_CHECK
+  auto lds = [&](bf16_t* p, int bytes) -> bf16_t* {
+    return smem + lchk((int)((char*)p - (char*)smem), bytes, LDS_BYTES) / 2;
+  };
+#else
+  auto lds = [](bf16_t* p, int) { return p; };
+#endif
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+
+  // ---- which (group, row tile, column tile)
+  const int tilesN = (a.N + BNH - 1) / BNH;
+  const int* toff = a.toff_all + tidx * (a.G + 1);
+  const int T = xcd_unit(toff[a.G] * tilesN);
+  if (T < 0) return;
+  int lo = 0, hi = a.G - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (toff[mid] * tilesN <= T) lo = mid; else hi = mid - 1;
+  }
+  const int e = lo;
+  const int nte = toff[e + 1] - toff[e];
+  const int local = T - toff[e] * tilesN;
+  const int nt = local / nte;
+  const int row0 = a.goff[e] + (local - nt * nte) * BM;
+  const int row_end = a.goff[e + 1];
+  const int j0 = nt * BNH;
+
+  // ---- source of every 16-byte chunk this thread moves; LDS chunk position P of a tile holds
+  //      global chunk (P mod CPR) ^ swizzle(row)
+  const bf16_t* asrc[A_CPT];
+#pragma unroll
+  for (int u = 0; u < A_CPT; u++) {
+    const int P = tid + u * NT;
+    const int x = P / CPR_A, q = (P % CPR_A) ^ swz_xk<CPR_A>(x);
+    const int row = min(row0 + x, row_end - 1);
+    const int src = a.arow ? a.arow[row] / a.arow_div : row;
+    asrc[u] = (const bf16_t*)a.A + (long)src * a.lda + q * 8;
+  }
+  const bf16_t* Bg = (const bf16_t*)a.B + (long)e * a.bstride;
+  const bf16_t* Bug = DUAL ? (const bf16_t*)a.Bu + (long)e * a.bstride : Bg;
+  const bf16_t* bsrc[B_CPT];
+#pragma unroll
+  for (int u = 0; u < B_CPT; u++) {
+    const int P = tid + u * NT;
+    if constexpr (BL == LAYOUT_KX) {
+      const int k = P / CPR_B, x = ((P % CPR_B) ^ swz_kx<CPR_B>(k)) * 8;
+      const int half = DUAL ? (x >= BNH) : 0;
+      const int jj = min(j0 + x - half * BNH, a.N - 8);
+      bsrc[u] = (half ? Bug : Bg) + (long)k * a.ldb + jj;
+    } else {
+      const int x = P / CPR_B, q = (P % CPR_B) ^ swz_xk<CPR_B>(x);
+      const int half = DUAL ? (x >= BNH) : 0;
+      const int jj = min(j0 + x - half * BNH, a.N - 1);
+      bsrc[u] = (half ? Bug : Bg) + (long)jj * a.ldb + q * 8;
+    }
+  }
+  const long bstep = (BL == LAYOUT_KX) ? (long)BKT * a.ldb : (long)BKT;  // source advance per tile
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; i++)
+#pragma unroll
+    for (int j = 0; j < TN; j++)
+#pragma unroll
+      for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
+
+  i32x4_t ra[4][A_CPT], rb[4][B_CPT];  // register ring: slot = tile % 4
+  auto load = [&](i32x4_t(&da)[A_CPT], i32x4_t(&db)[B_CPT], int t) {
+#pragma unroll
+    for (int u = 0; u < A_CPT; u++) da[u] = ld16(GCHK(asrc[u] + t * BKT, 16));
+    const long adv = t * bstep;
+#pragma unroll
+    for (int u = 0; u < B_CPT; u++) db[u] = ld16(GCHK(bsrc[u] + adv, 16));
+  };
+  auto store = [&](bf16_t* st, const i32x4_t(&da)[A_CPT], const i32x4_t(&db)[B_CPT]) {
+#pragma unroll
+    for (int u = 0; u < A_CPT; u++) *reinterpret_cast<i32x4_t*>(lds(st + (tid + u * NT) * 8, 16)) = da[u];
+#pragma unroll
+    for (int u = 0; u < B_CPT; u++)
+      *reinterpret_cast<i32x4_t*>(lds(st + A_ELEMS + (tid + u * NT) * 8, 16)) = db[u];
+  };
+  auto wcol = [&](int tn) {
+    if constexpr (DUAL) {
+      constexpr int TH = TN / 2;
+      return (tn >= TH ? BNH : 0) + wn * TH * 32 + (tn % TH) * 32;
+    } else {
+      return wn * TN * 32 + tn * 32;
+    }
+  };
+  auto frags = [&](const bf16_t* sA, int ks, bf16x8_t* fa, bf16x8_t* fb) {
+    const bf16_t* sB = sA + A_ELEMS;
+#pragma unroll
+    for (int tm = 0; tm < TM; tm++) fa[tm] = frag_xk_s<BKT>(sA, wm * TM * 32 + tm * 32, ks * 16, lane);
+#pragma unroll
+    for (int tn = 0; tn < TN; tn++)
+      fb[tn] = (BL == LAYOUT_XK) ? frag_xk_s<BKT>(sB, wcol(tn), ks * 16, lane)
+                                 : frag_kx_s<BN>(sB, wcol(tn), ks * 16, lane);
+  };
+  auto mma = [&](const bf16x8_t* fa, const bf16x8_t* fb) {
+    static_for<TM>([&](auto tmc) {
+      constexpr int tm = decltype(tmc)::value;
+      static_for<TN>([&](auto tnc) {
+        constexpr int tn = decltype(tnc)::value;
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[tm], fb[tn], acc[tm][tn], 0, 0, 0);
+      });
+    });
+  };
+  // fragments of k16 step ks+1 are read while the MFMAs of step ks run
+  auto compute = [&](const bf16_t* sA) {
+    bf16x8_t fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+    frags(sA, 0, fa0, fb0);
+    static_for<BKT / 32>([&](auto kc) {
+      constexpr int ks = 2 * decltype(kc)::value;
+      frags(sA, ks + 1, fa1, fb1);
+      mma(fa0, fb0);
+      if constexpr (ks + 2 < BKT / 16) frags(sA, ks + 2, fa0, fb0);
+      mma(fa1, fb1);
+    });
+  };
+
+  // ---- main loop. Step kt: (barrier) copy tile kt+1 from registers into LDS stage (kt+1)&1,
+  //      multiply tile kt from stage kt&1, load tile kt+4 into the ring slot tile kt left.
+  const int nk = a.K / BKT;
+  const int last = nk - 1;
+  bf16_t* const s0 = smem;
+  bf16_t* const s1 = smem + STAGE;
+  load(ra[0], rb[0], 0);
+  load(ra[1], rb[1], min(1, last));
+  load(ra[2], rb[2], min(2, last));
+  load(ra[3], rb[3], min(3, last));
+  store(s0, ra[0], rb[0]);
+  auto step = [&](auto slot_c, int kt) {
+    constexpr int sl = decltype(slot_c)::value;       // kt % 4
+    constexpr int nx = (sl + 1) & 3;                  // (kt + 1) % 4
+    lds_barrier();
+    store((sl & 1) ? s0 : s1, ra[nx], rb[nx]);
+    if (kt < nk) compute((sl & 1) ? s1 : s0);
+    load(ra[sl], rb[sl], min(kt + 4, last));
+  };
+  for (int kt = 0; kt < nk; kt += 4) {
+    step(IC<0>{}, kt);
+    step(IC<1>{}, kt + 1);
+    step(IC<2>{}, kt + 2);
+    step(IC<3>{}, kt + 3);
+  }
+
+  // ---- Split-LoRA tail: [TA | 0] . [TB ; 0] over K2 <= 128 more reduction rows
+  if (a.tail != TAIL_NONE) {
+    lds_barrier();  // every wave is done with both stages
+    const int r2 = a.r2a;
+    const int K2 = (a.tail == TAIL_SINGLE) ? r2 : 2 * r2;
+    const int tsteps = (K2 + BKT - 1) / BKT;
+    const i32x4_t zero = {0, 0, 0, 0};
+    const bf16_t* T0 = (const bf16_t*)a.TB0 + (long)e * a.tbstride;
+    const bf16_t* T1 = a.TB1 ? (const bf16_t*)a.TB1 + (long)e * a.tbstride : T0;
+    for (int ts = 0; ts < tsteps; ts++) {
+      bf16_t* sA = smem + ts * STAGE;
+      bf16_t* sB = sA + A_ELEMS;
+      for (int P = tid; P < A_ELEMS / 8; P += NT) {
+        const int x = P / CPR_A, q = ((P % CPR_A) ^ swz_xk<CPR_A>(x)) + ts * CPR_A;
+        const int row = min(row0 + x, row_end - 1);
+        *reinterpret_cast<i32x4_t*>(lds(sA + P * 8, 16)) =
+            (q * 8 < K2) ? ld16(GCHK((const bf16_t*)a.TA + (long)row * a.lda2 + q * 8, 16)) : zero;
+      }
+      for (int P = tid; P < BN * BKT / 8; P += NT) {
+        const bf16_t* src = nullptr;
+        if constexpr (BL == LAYOUT_KX) {
+          const int k = P / CPR_B, x = ((P % CPR_B) ^ swz_kx<CPR_B>(k)) * 8;
+          const int kk = k + ts * BKT;
+          const int half = DUAL ? (x >= BNH) : 0;
+          const int jj = min(j0 + x - half * BNH, a.N - 8);
+          if (a.tail == TAIL_SINGLE) {
+            if (kk < r2) src = T0 + (long)kk * a.ldtb + jj;
+          } else if (a.tail == TAIL_BLOCKDIAG) {
+            if (half == 0 && kk < r2) src = T0 + (long)kk * a.ldtb + jj;
+            else if (half == 1 && kk >= r2 && kk < 2 * r2) src = T1 + (long)(kk - r2) * a.ldtb + jj;
+          } else {
+            if (kk < r2) src = T0 + (long)kk * a.ldtb + jj;
+            else if (kk < 2 * r2) src = T1 + (long)(kk - r2) * a.ldtb + jj;
+          }
+        } else {
+          const int x = P / CPR_B;
+          const int k8 = (((P % CPR_B) ^ swz_xk<CPR_B>(x)) + ts * CPR_B) * 8;
+          const int half = DUAL ? (x >= BNH) : 0;
+          const int jj = min(j0 + x - half * BNH, a.N - 1);
+          if (a.tail == TAIL_SINGLE) {
+            if (k8 < r2) src = T0 + (long)jj * a.ldtb + k8;
+          } else if (a.tail == TAIL_BLOCKDIAG) {
+            if (half == 0 && k8 < r2) src = T0 + (long)jj * a.ldtb + k8;
+            else if (half == 1 && k8 >= r2 && k8 < 2 * r2) src = T1 + (long)jj * a.ldtb + (k8 - r2);
+          } else {
+            if (k8 < r2) src = T0 + (long)jj * a.ldtb + k8;
+            else if (k8 < 2 * r2) src = T1 + (long)jj * a.ldtb + (k8 - r2);
+          }
+        }
+        *reinterpret_cast<i32x4_t*>(lds(sB + P * 8, 16)) = src ? ld16(GCHK(src, 16)) : zero;
+      }
+    }
+    __syncthreads();
+    compute(s0);
+    if (tsteps > 1) compute(s1);
+  }
+
+  // ---- epilogue (compile-time accumulator indices; one 32-row MFMA tile row at a time)
+  bf16_t* C = (bf16_t*)a.C;
+  static_for<TM>([&](auto tmc) {
+    constexpr int tm = decltype(tmc)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<16>([&](auto vc) {
+      constexpr int v = decltype(vc)::value;
+      const int row = row0 + wm * TM * 32 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      if (row < row_end) {
+        if constexpr (DUAL) {
+          static_for<TN / 2>([&](auto tc) {
+            constexpr int t2 = decltype(tc)::value;
+            const int jj = j0 + wn * (TN / 2) * 32 + t2 * 32 + (lane & 31);
+            if (jj < a.N) {
+              const float g = acc[tm][t2][v], uu = acc[tm][t2 + TN / 2][v];
+              if constexpr (EPI == EPI_DUAL) {
+                *GCHK(C + (long)row * a.ldc + jj, 2) = f32_to_bf16(a.scale * g);
+                *GCHK(C + (long)row * a.ldc + a.cup + jj, 2) = f32_to_bf16(a.scale * uu);
+              } else {
+                *GCHK(C + (long)row * a.ldc + jj, 2) = f32_to_bf16(g);
+                *GCHK(C + (long)row * a.ldc + a.cup + jj, 2) = f32_to_bf16(uu);
+                *GCHK((bf16_t*)a.H + (long)row * a.ldh + jj, 2) = f32_to_bf16(silu_f(g) * uu);
+              }
+            }
+          });
+        } else {
+          static_for<TN>([&](auto tc) {
+            constexpr int tn = decltype(tc)::value;
+            const int jj = j0 + wn * TN * 32 + tn * 32 + (lane & 31);
+            if (jj < a.N) {
+              const float val = a.scale * acc[tm][tn][v];
+              if constexpr (EPI == EPI_STORE) {
+                *GCHK(C + (long)row * a.ldc + jj, 2) = f32_to_bf16(val + (a.bias ? a.bias[jj] : 0.0f));
+              } else {  // EPI_SWIGLU_BWD
+                const bf16_t* GU = (const bf16_t*)a.GU;
+                const float g = bf16_to_f32(*GCHK(GU + (long)row * a.ldgu + jj, 2));
+                const float uu = bf16_to_f32(*GCHK(GU + (long)row * a.ldgu + a.guup + jj, 2));
+                const float sg = 1.0f / (1.0f + __expf(-g));
+                *GCHK(C + (long)row * a.ldc + jj, 2) = f32_to_bf16(val * uu * sg * (1.0f + g * (1.0f - sg)));
+                *GCHK(C + (long)row * a.ldc + a.cup + jj, 2) = f32_to_bf16(val * g * sg);
+              }
+            }
+          });
+        }
+      }
+    });
+  });
+}
+
+// ------------------------------------------------------------------------------------------------
 // K-grouped MFMA GEMM: C_e = scale * L[rows_e]^T . R[rows_e]; both operands stored with the output
 // axis contiguous, so both fragments come from transposing LDS reads.
 template <int WM, int WN, int TM, int TN>
@@ -671,6 +993,25 @@ hipError_t dispatch_gm_mfma(const GemmArgs& a, int rows_bound, hipStream_t strea
   }
 }
 
+// Deep-prefetch kernel for the launches with a Split-LoRA tail.
+template <int WM, int WN, int TM, int TN, int BL, int EPI>
+hipError_t launch_gm_ring(const GemmArgs& a, int rows_bound, hipStream_t stream) {
+  constexpr bool DUAL = (EPI == EPI_DUAL || EPI == EPI_SWIGLU);
+  constexpr int BM = WM * TM * 32, BN = WN * TN * 32, BNH = DUAL ? BN / 2 : BN;
+  if (!a.goff || !a.toff_all || a.K % 64 || a.tail == TAIL_NONE) return hipErrorInvalidValue;
+  const int K2 = a.tail == TAIL_SINGLE ? a.r2a : 2 * a.r2a;
+  if (K2 <= 0 || K2 > 128 || K2 % 8) return hipErrorInvalidValue;
+  const int tidx = tile_table_index(BM);
+  if (tidx < 0) return hipErrorInvalidValue;
+  const long tilesN = (a.N + BNH - 1) / BNH;
+  const long units = ((long)rows_bound / BM + a.G) * tilesN;
+  if (units <= 0) return hipSuccess;
+  const long blocks = (units + 7) / 8 * 8;
+  hipLaunchKernelGGL((gm_ring<WM, WN, TM, TN, BL, EPI>), dim3((unsigned)blocks), dim3(WM * WN * 64), 0,
+                     stream, a, tidx);
+  return hipGetLastError();
+}
+
 template <typename T, typename OutT, int EPI>
 hipError_t launch_gm_simt(const GemmArgs& a, int b_layout, int rows_bound, hipStream_t stream) {
   const int rows = a.goff ? rows_bound : a.M;
@@ -700,6 +1041,18 @@ hipError_t gemm_gm_launch(const GemmArgs& a, int b_layout, int epi, int out_f32,
   if (reference) {
     return out_f32 ? dispatch_gm_simt<bf16_t, float>(a, b_layout, epi, rows_bound, stream)
                    : dispatch_gm_simt<bf16_t, bf16_t>(a, b_layout, epi, rows_bound, stream);
+  }
+  if (a.tail != TAIL_NONE) {  // the expert projections
+    if (out_f32) return hipErrorInvalidValue;
+    if (b_layout == LAYOUT_KX) {
+      if (epi == EPI_SWIGLU) return launch_gm_ring<2, 2, 2, 2, LAYOUT_KX, EPI_SWIGLU>(a, rows_bound, stream);
+      if (epi == EPI_STORE) return launch_gm_ring<2, 2, 2, 2, LAYOUT_KX, EPI_STORE>(a, rows_bound, stream);
+    } else {
+      if (epi == EPI_STORE) return launch_gm_ring<2, 2, 2, 2, LAYOUT_XK, EPI_STORE>(a, rows_bound, stream);
+      if (epi == EPI_SWIGLU_BWD)
+        return launch_gm_ring<2, 2, 2, 2, LAYOUT_XK, EPI_SWIGLU_BWD>(a, rows_bound, stream);
+    }
+    return hipErrorInvalidValue;
   }
   if (out_f32) {
     if (epi != EPI_STORE) return hipErrorInvalidValue;

@@ -21,6 +21,10 @@ VARIANTS = {
     "qwen3_zipf_small": config("qwen3_30b_a3b_zipf", s=1024, m=256, n=128),
     "gpt_oss_small": config("gpt_oss_20b", s=384, m=320, n=320, E=8, k=4),
     "deepseek_small": config("deepseek_v3", s=512, m=448, n=128, E=32, k=8),
+    # the largest supported rank: two-factor LoRA tails 2r = 128 reduction rows long
+    "gpt_oss_r64": config("gpt_oss_20b", s=384, m=192, n=256, E=8, k=4, r=64, alpha=128.0),
+    # an expert with more than one 256-row tile, and ragged last tiles
+    "big_expert": config("qwen3_30b_a3b_zipf", s=1024, m=128, n=192, E=16, k=2, zipf=2.0),
 }
 
 
