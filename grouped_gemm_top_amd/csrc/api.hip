@@ -35,6 +35,7 @@ struct RouteState {
   int* blk_hist;
   int* blk_base;
   int* tiles;
+  int* tmaps;
 };
 
 struct FwdBufs {
@@ -65,6 +66,7 @@ size_t route_layout(const moe_shape& s, void* base, RouteState* rs) {
   r.blk_hist = c.take<int>((size_t)nb * s.E);
   r.blk_base = c.take<int>((size_t)nb * s.E);
   r.tiles = c.take<int>((size_t)kNumTileSizes * (s.E + 1));
+  r.tmaps = c.take<int>((size_t)tile_map_offset(kNumTileSizes, P, s.E));
   if (rs) *rs = r;
   return align_up(c.off, 256);
 }
@@ -287,7 +289,7 @@ moe_status moe_route(const moe_shape* shape, const void* X, const void* W_r,
   STAGE(ST_ROUTE_LOGITS, gemm_gm_launch(a, LAYOUT_KX, EPI_STORE, 1, s.dtype, s.s, ref, hs));
   STAGE(ST_ROUTE_TOPK, launch_topk(z, s.s, s.E, s.k, s.score, s.renormalize, topk_idx, topk_w, rs.psel, hs));
   STAGE(ST_ROUTE_HIST, launch_hist_rank(topk_idx, s.s, s.k, s.E, rs.blk_hist, rs.rank, hs));
-  STAGE(ST_ROUTE_SCAN, launch_scan(rs.blk_hist, nblocks(s), s.E, (int)P, rs.blk_base, expert_off, rs.tiles, hs));
+  STAGE(ST_ROUTE_SCAN, launch_scan(rs.blk_hist, nblocks(s), s.E, (int)P, rs.blk_base, expert_off, rs.tiles, rs.tmaps, hs));
   STAGE(ST_ROUTE_SCATTER, launch_scatter(topk_idx, rs.rank, rs.blk_base, s.s, s.k, s.E, perm, inv_perm, rs.row_tok, hs));
   return MOE_OK;
 }
@@ -337,6 +339,7 @@ moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t
   base.G = s.E;
   base.goff = expert_off;
   base.toff_all = rs.tiles;
+  base.tmap_all = rs.tmaps;
 
   // Tc_gu = c * Xp [A_g | A_u]
   {
@@ -449,6 +452,7 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
   base.G = s.E;
   base.goff = expert_off;
   base.toff_all = rs.tiles;
+  base.tmap_all = rs.tmaps;
 
   // Uc_d = c * dO B_d^T
   {

@@ -40,6 +40,7 @@ struct GemmArgs {
   int G;             // number of groups
   const int* goff;   // [G+1] group offsets, or nullptr for one group [0, M)
   const int* toff_all;  // GM: kNumTileSizes tables of [G+1] row-tile prefix sums (one per BM)
+  const int* tmap_all;  // GM: kNumTileSizes maps row tile -> group, at tile_map_offset(i, ...)
   // ---- A operand (GM: layout XK with optional row gather; GK: layout KX over group rows)
   const void* A;
   long lda;
@@ -87,5 +88,13 @@ hipError_t gemm_gk_launch(const GemmArgs& a, int dtype, int reference, hipStream
 constexpr int kNumTileSizes = 4;
 constexpr int kTileSizes[kNumTileSizes] = {32, 64, 128, 256};
 int tile_table_index(int bm);
+// Row-tile -> group maps: map i has room for rows_bound / kTileSizes[i] + G entries (a row tile
+// never spans two groups, so there are at most that many tiles); maps are stored back to back.
+__host__ __device__ inline long tile_map_capacity(int i, long rows_bound, int G) { return rows_bound / kTileSizes[i] + G; }
+__host__ __device__ inline long tile_map_offset(int i, long rows_bound, int G) {
+  long o = 0;
+  for (int j = 0; j < i; j++) o += tile_map_capacity(j, rows_bound, G);
+  return o;
+}
 
 }  // namespace moe

@@ -169,7 +169,7 @@ __device__ inline void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) :
 // the loads of tile kt+1 run while tile kt is multiplied. LDS tiles are unpadded and XOR-swizzled at
 // 16-byte chunk granularity against bank conflicts of the fragment reads.
 template <int WM, int WN, int TM, int TN, int BKT, int S, int BL, int EPI, typename OutT, bool TAIL>
-__global__ __launch_bounds__(WM * WN * 64) void gm_mfma(GemmArgs a, int tidx) {
+__global__ __launch_bounds__(WM * WN * 64) void gm_mfma(GemmArgs a, int tidx, const int* tmap) {
   constexpr bool DUAL = (EPI == EPI_DUAL || EPI == EPI_SWIGLU);
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32, NW = WM * WN;
   constexpr int BNH = DUAL ? BN / 2 : BN;
@@ -199,12 +199,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gm_mfma(GemmArgs a, int tidx) {
   if (T < 0) return;
   int e = 0, row0, row_end, nt;
   if (a.goff) {
-    int lo = 0, hi = a.G - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (toff[mid] * tilesN <= T) lo = mid; else hi = mid - 1;
-    }
-    e = lo;
+    e = tmap[T / tilesN];  // row tiles of group e are [toff[e], toff[e+1])
     const int nte = toff[e + 1] - toff[e];
     const int local = T - toff[e] * tilesN;
     nt = local / nte;
@@ -463,7 +458,7 @@ using IC = std::integral_constant<int, N_>;
 
 template <int WM, int WN, int TM, int TN, int BL, int EPI>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void gm_ring(GemmArgs a, int tidx) {
+void gm_ring(GemmArgs a, int tidx, const int* tmap) {
   constexpr int BKT = 64, NW = WM * WN, NT = NW * 64;
   constexpr bool DUAL = (EPI == EPI_DUAL || EPI == EPI_SWIGLU);
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
@@ -495,12 +490,7 @@ void gm_ring(GemmArgs a, int tidx) {
   const int* toff = a.toff_all + tidx * (a.G + 1);
   const int T = xcd_unit(toff[a.G] * tilesN);
   if (T < 0) return;
-  int lo = 0, hi = a.G - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (toff[mid] * tilesN <= T) lo = mid; else hi = mid - 1;
-  }
-  const int e = lo;
+  const int e = tmap[T / tilesN];  // row tiles of group e are [toff[e], toff[e+1])
   const int nte = toff[e + 1] - toff[e];
   const int local = T - toff[e] * tilesN;
   const int nt = local / nte;
@@ -965,9 +955,10 @@ hipError_t launch_gm_mfma_t(const GemmArgs& a, int rows_bound, hipStream_t strea
   if (units <= 0) return hipSuccess;
   const long blocks = (units + 7) / 8 * 8;
   const int tidx = tile_table_index(Cfg::BM);
-  if (a.goff && tidx < 0) return hipErrorInvalidValue;
+  if (a.goff && (tidx < 0 || !a.toff_all || !a.tmap_all)) return hipErrorInvalidValue;
+  const int* tmap = a.goff ? a.tmap_all + tile_map_offset(tidx, rows_bound, a.G) : nullptr;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(Cfg::WM * Cfg::WN * 64), Cfg::lds_bytes,
-                     stream, a, tidx);
+                     stream, a, tidx, tmap);
   return hipGetLastError();
 }
 
@@ -998,7 +989,7 @@ template <int WM, int WN, int TM, int TN, int BL, int EPI>
 hipError_t launch_gm_ring(const GemmArgs& a, int rows_bound, hipStream_t stream) {
   constexpr bool DUAL = (EPI == EPI_DUAL || EPI == EPI_SWIGLU);
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32, BNH = DUAL ? BN / 2 : BN;
-  if (!a.goff || !a.toff_all || a.K % 64 || a.tail == TAIL_NONE) return hipErrorInvalidValue;
+  if (!a.goff || !a.toff_all || !a.tmap_all || a.K % 64 || a.tail == TAIL_NONE) return hipErrorInvalidValue;
   const int K2 = a.tail == TAIL_SINGLE ? a.r2a : 2 * a.r2a;
   if (K2 <= 0 || K2 > 128 || K2 % 8) return hipErrorInvalidValue;
   const int tidx = tile_table_index(BM);
@@ -1007,8 +998,9 @@ hipError_t launch_gm_ring(const GemmArgs& a, int rows_bound, hipStream_t stream)
   const long units = ((long)rows_bound / BM + a.G) * tilesN;
   if (units <= 0) return hipSuccess;
   const long blocks = (units + 7) / 8 * 8;
+  const int* tmap = a.tmap_all + tile_map_offset(tidx, rows_bound, a.G);
   hipLaunchKernelGGL((gm_ring<WM, WN, TM, TN, BL, EPI>), dim3((unsigned)blocks), dim3(WM * WN * 64), 0,
-                     stream, a, tidx);
+                     stream, a, tidx, tmap);
   return hipGetLastError();
 }
 

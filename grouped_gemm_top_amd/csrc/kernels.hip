@@ -157,8 +157,10 @@ __device__ int block_exscan_1024(int v, int* sh, int* total) {
 __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ blk_hist, int nb, int E,
                                                     int P, int* __restrict__ blk_base,
                                                     int* __restrict__ off,
-                                                    int* __restrict__ tile_tables) {
+                                                    int* __restrict__ tile_tables,
+                                                    int* __restrict__ tile_maps) {
   __shared__ int sh[32];
+  __shared__ int tsh[1025];
   const int e = threadIdx.x;
   int cnt = 0;
   if (e < E)
@@ -181,8 +183,20 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ blk_
     const int ts = block_exscan_1024(tiles, sh, &ttot);
     if (e < E) tile_tables[i * (E + 1) + e] = ts;
     if (e == 0) tile_tables[i * (E + 1) + E] = ttot;
+    // row tile -> group map: tile t belongs to the last group whose first tile is <= t
+    if (e <= E) tsh[e] = e < E ? ts : ttot;
+    __syncthreads();
+    int* map = tile_maps + tile_map_offset(i, P, E);
+    for (int t = e; t < ttot; t += 1024) {
+      int lo = 0, hi = E - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (tsh[mid] <= t) lo = mid; else hi = mid - 1;
+      }
+      map[t] = lo;
+    }
+    __syncthreads();
   }
-  (void)P;
 }
 
 __global__ void scatter_kernel(const int* __restrict__ idx, const int* __restrict__ rank,
@@ -397,9 +411,9 @@ hipError_t launch_hist_rank(const int* idx, int s, int k, int E, int* blk_hist, 
 }
 
 hipError_t launch_scan(const int* blk_hist, int nb, int E, int P, int* blk_base, int* off,
-                       int* tile_tables, hipStream_t st) {
+                       int* tile_tables, int* tile_maps, hipStream_t st) {
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, blk_hist, nb, E, P, blk_base, off,
-                     tile_tables);
+                     tile_tables, tile_maps);
   return hipGetLastError();
 }
 
