@@ -36,10 +36,19 @@ struct RouteState {
   int* blk_base;
   int* tiles;
   int* tmaps;
+  float* zpart;  // K-split partial router logits
 };
 
+// K splits of the router-logit GEMM: enough workgroups to fill the chip, chunks of >= 256.
+inline int route_ksplit(const moe_shape& s) {
+  const long tiles = ((long)s.s + 127) / 128 * (((long)s.E + 127) / 128);
+  int n = 1;
+  while (n < 8 && tiles * n < 512 && (s.m % (2 * n * 256)) == 0) n *= 2;
+  return n;
+}
+
 struct FwdBufs {
-  void *Xp, *gu, *h, *Tgu, *Td, *o;
+  void *gu, *h, *Tgu, *Td, *o;
 };
 
 struct BwdBufs {
@@ -67,6 +76,7 @@ size_t route_layout(const moe_shape& s, void* base, RouteState* rs) {
   r.blk_base = c.take<int>((size_t)nb * s.E);
   r.tiles = c.take<int>((size_t)kNumTileSizes * (s.E + 1));
   r.tmaps = c.take<int>((size_t)tile_map_offset(kNumTileSizes, P, s.E));
+  r.zpart = c.take<float>((size_t)route_ksplit(s) * s.s * s.E);
   if (rs) *rs = r;
   return align_up(c.off, 256);
 }
@@ -75,7 +85,6 @@ size_t fwd_layout(const moe_shape& s, void* base, FwdBufs* fb) {
   Carve c(base);
   const size_t P = (size_t)pairs(s), es = esize(s);
   FwdBufs f;
-  f.Xp = c.bytes(P * s.m * es);
   f.gu = c.bytes(P * 2 * s.n * es);
   f.h = c.bytes(P * s.n * es);
   f.Tgu = c.bytes(P * 2 * s.r * es);
@@ -137,13 +146,13 @@ inline bool ptr_ok(const void* p, size_t count) {
 // stage while enabled, resolved and summed by moe_timing_read.
 enum Stage {
   ST_ROUTE_LOGITS, ST_ROUTE_TOPK, ST_ROUTE_HIST, ST_ROUTE_SCAN, ST_ROUTE_SCATTER,
-  ST_FWD_PERMUTE, ST_FWD_T_GU, ST_FWD_GATE_UP, ST_FWD_T_D, ST_FWD_DOWN, ST_FWD_COMBINE,
+  ST_FWD_T_GU, ST_FWD_GATE_UP, ST_FWD_T_D, ST_FWD_DOWN, ST_FWD_COMBINE,
   ST_BWD_COMBINE, ST_BWD_ROUTER, ST_BWD_U_D, ST_BWD_DOWN, ST_BWD_GRAD_D, ST_BWD_U_GU,
   ST_BWD_GATE_UP, ST_BWD_GRAD_GU, ST_BWD_UNPERMUTE, ST_COUNT
 };
 const char* const kStageNames[ST_COUNT] = {
   "route_logits", "route_topk", "route_hist_rank", "route_scan", "route_scatter",
-  "fwd_permute", "fwd_lora_t_gate_up", "fwd_gate_up", "fwd_lora_t_down", "fwd_down", "fwd_combine",
+  "fwd_lora_t_gate_up", "fwd_gate_up", "fwd_lora_t_down", "fwd_down", "fwd_combine",
   "bwd_combine", "bwd_router", "bwd_lora_u_down", "bwd_down", "bwd_lora_grads_down",
   "bwd_lora_u_gate_up", "bwd_gate_up", "bwd_lora_grads_gate_up", "bwd_unpermute"};
 
@@ -273,6 +282,8 @@ moe_status moe_route(const moe_shape* shape, const void* X, const void* W_r,
     return MOE_OK;
   }
   float* z = logits ? logits : rs.logits;
+  const int ref = (s.flags & MOE_FLAG_REFERENCE_GEMM) ? 1 : 0;
+  const int nsplit = (ref || s.dtype != MOE_DTYPE_BF16) ? 1 : route_ksplit(s);
   GemmArgs a = gemm_args();
   a.M = s.s;
   a.N = s.E;
@@ -282,12 +293,16 @@ moe_status moe_route(const moe_shape* shape, const void* X, const void* W_r,
   a.lda = s.m;
   a.B = W_r;
   a.ldb = s.E;
-  a.C = z;
+  a.C = nsplit > 1 ? rs.zpart : z;
   a.ldc = s.E;
   a.bias = router_bias;
-  const int ref = (s.flags & MOE_FLAG_REFERENCE_GEMM) ? 1 : 0;
+  if (nsplit > 1) {
+    a.kchunk = s.m / nsplit;
+    a.csplit = (long)s.s * s.E;
+  }
   STAGE(ST_ROUTE_LOGITS, gemm_gm_launch(a, LAYOUT_KX, EPI_STORE, 1, s.dtype, s.s, ref, hs));
-  STAGE(ST_ROUTE_TOPK, launch_topk(z, s.s, s.E, s.k, s.score, s.renormalize, topk_idx, topk_w, rs.psel, hs));
+  STAGE(ST_ROUTE_TOPK, launch_topk(nsplit > 1 ? rs.zpart : z, nsplit, (long)s.s * s.E, z, s.s, s.E, s.k,
+                                   s.score, s.renormalize, topk_idx, topk_w, rs.psel, hs));
   STAGE(ST_ROUTE_HIST, launch_hist_rank(topk_idx, s.s, s.k, s.E, rs.blk_hist, rs.rank, hs));
   STAGE(ST_ROUTE_SCAN, launch_scan(rs.blk_hist, nblocks(s), s.E, (int)P, rs.blk_base, expert_off, rs.tiles, rs.tmaps, hs));
   STAGE(ST_ROUTE_SCATTER, launch_scatter(topk_idx, rs.rank, rs.blk_base, s.s, s.k, s.E, perm, inv_perm, rs.row_tok, hs));
@@ -332,8 +347,6 @@ moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t
   const float c = s.alpha / (float)s.r;
   const int Pi = (int)P;
 
-  // permute: Xp[row] = X[perm[row] / k]
-  STAGE(ST_FWD_PERMUTE, launch_gather_rows(s.dtype, X, f.Xp, perm, s.k, Pi, s.m, hs));
 
   GemmArgs base = gemm_args();
   base.G = s.E;
@@ -341,11 +354,13 @@ moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t
   base.toff_all = rs.tiles;
   base.tmap_all = rs.tmaps;
 
+  // The grouped row i of every expert GEMM is pair perm[i]; its activation row is X[perm[i] / k],
+  // gathered by the GEMM kernels (no permuted copy of X is written).
   // Tc_gu = c * Xp [A_g | A_u]
   {
     GemmArgs a = base;
     a.N = s.r; a.K = s.m;
-    a.A = f.Xp; a.lda = s.m;
+    a.A = X; a.lda = s.m; a.arow = perm; a.arow_div = s.k;
     a.B = A_g; a.Bu = A_u; a.ldb = s.r; a.bstride = (long)m * r;
     a.C = f.Tgu; a.ldc = 2 * s.r; a.cup = s.r; a.scale = c;
     STAGE(ST_FWD_T_GU, gemm_gm_launch(a, LAYOUT_KX, EPI_DUAL, 0, s.dtype, Pi, ref, hs));
@@ -354,7 +369,7 @@ moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t
   {
     GemmArgs a = base;
     a.N = s.n; a.K = s.m;
-    a.A = f.Xp; a.lda = s.m;
+    a.A = X; a.lda = s.m; a.arow = perm; a.arow_div = s.k;
     a.B = W_gu; a.Bu = (const char*)W_gu + n * esize(s); a.ldb = 2 * s.n; a.bstride = (long)m * 2 * n;
     a.tail = TAIL_BLOCKDIAG; a.r2a = s.r;
     a.TA = f.Tgu; a.lda2 = 2 * s.r;
@@ -521,7 +536,7 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
     GemmArgs a = base;
     a.toff_all = nullptr;
     a.M = s.m; a.N = 2 * s.r;
-    a.A = f.Xp; a.lda = s.m;
+    a.A = X; a.lda = s.m; a.arow = perm; a.arow_div = s.k;
     a.B = b.Ugu; a.ldb = 2 * s.r;
     a.C = dA_g; a.C1 = dA_u; a.nsplit = s.r; a.ldc = s.r; a.cstride = (long)m * r;
     STAGE(ST_BWD_GRAD_GU, gemm_gk_launch(a, s.dtype, ref, hs));

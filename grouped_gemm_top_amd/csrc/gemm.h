@@ -69,7 +69,9 @@ struct GemmArgs {
   long cup;          // dual epilogues: column offset of the up half in C
   long cstride;      // GK: elements between groups' outputs
   float scale;
-  const float* bias; // EPI_STORE: per-column bias (fp32) or nullptr
+  const float* bias; // EPI_STORE: per-column bias (fp32) or nullptr; added by K split 0 only
+  int kchunk;        // GM without groups or tail: gridDim.y K splits of kchunk each (0: one split)
+  long csplit;       //   elements between the outputs of consecutive K splits
   void* H;           // EPI_SWIGLU: silu(gate)*up output
   long ldh;
   const void* GU;    // EPI_SWIGLU_BWD: saved [g | u]

@@ -255,8 +255,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gm_mfma(GemmArgs a, int tidx, co
 #pragma unroll
       for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
 
+  // K split of this workgroup (ungrouped launches only): reduction rows [kbase, kbase + Keff)
+  const int kbase = a.kchunk ? (int)blockIdx.y * a.kchunk : 0;
+  const int Keff = a.kchunk ? a.kchunk : a.K;
   // DMA of one K tile into the stage at sA (A tile) / sA + A_ELEMS (B tile)
   auto issue = [&](bf16_t* sA, int k0) {
+    k0 += kbase;
     bf16_t* sB = sA + A_ELEMS;
 #pragma unroll
     for (int i = 0; i < A_IPW; i++) dma16(Ab + aoff[i] + k0, sA + (wave * A_IPW + i) * 512);
@@ -312,7 +316,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gm_mfma(GemmArgs a, int tidx, co
   };
 
   // ---- main K loop: loads of tile kt+1 in flight while tile kt is multiplied
-  const int nk = a.K / BKT;
+  const int nk = Keff / BKT;
   bf16_t* const stage0 = smem;
   bf16_t* const stage1 = smem + STAGE;
   issue(stage0, 0);
@@ -388,7 +392,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gm_mfma(GemmArgs a, int tidx, co
   }
 
   // ---- epilogue (compile-time accumulator indices; one 32-row MFMA tile row at a time)
-  OutT* C = (OutT*)a.C;
+  OutT* C = (OutT*)a.C + (a.kchunk ? (long)blockIdx.y * a.csplit : 0L);
+  const float* bias = blockIdx.y == 0 ? a.bias : nullptr;
   static_for<TM>([&](auto tmc) {
     constexpr int tm = decltype(tmc)::value;
     __builtin_amdgcn_sched_barrier(0);
@@ -419,7 +424,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gm_mfma(GemmArgs a, int tidx, co
             if (jj < a.N) {
               const float val = a.scale * acc[tm][tn][v];
               if constexpr (EPI == EPI_STORE) {
-                C[(long)row * a.ldc + jj] = from_f<OutT>(val + (a.bias ? a.bias[jj] : 0.0f));
+                C[(long)row * a.ldc + jj] = from_f<OutT>(val + (bias ? bias[jj] : 0.0f));
               } else {  // EPI_SWIGLU_BWD
                 const OutT* GU = (const OutT*)a.GU;
                 const float g = to_f(GU[(long)row * a.ldgu + jj]);
@@ -957,8 +962,13 @@ hipError_t launch_gm_mfma_t(const GemmArgs& a, int rows_bound, hipStream_t strea
   const int tidx = tile_table_index(Cfg::BM);
   if (a.goff && (tidx < 0 || !a.toff_all || !a.tmap_all)) return hipErrorInvalidValue;
   const int* tmap = a.goff ? a.tmap_all + tile_map_offset(tidx, rows_bound, a.G) : nullptr;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(Cfg::WM * Cfg::WN * 64), Cfg::lds_bytes,
-                     stream, a, tidx, tmap);
+  int splits = 1;
+  if (a.kchunk) {
+    if (a.goff || TAIL || a.kchunk % 64 || a.K % a.kchunk) return hipErrorInvalidValue;
+    splits = a.K / a.kchunk;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks, (unsigned)splits), dim3(Cfg::WM * Cfg::WN * 64),
+                     Cfg::lds_bytes, stream, a, tidx, tmap);
   return hipGetLastError();
 }
 

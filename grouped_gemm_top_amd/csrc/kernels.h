@@ -7,8 +7,10 @@ namespace moe {
 constexpr int kRouteBlockTokens = 256;  // tokens per block in the histogram/rank pass
 
 // Per token: top-k logits (ties -> lower expert id), routing weights, raw scores.
-hipError_t launch_topk(const float* z, int s, int E, int k, int score, int renorm, int* idx,
-                       float* w, float* psel, hipStream_t st);
+// Top-k over logits given as nsplit partial arrays (split_stride floats apart, summed in order);
+// with nsplit > 1 the summed logits are written to zout (when not null).
+hipError_t launch_topk(const float* z, int nsplit, long split_stride, float* zout, int s, int E,
+                       int k, int score, int renorm, int* idx, float* w, float* psel, hipStream_t st);
 // Per block of 256 tokens: expert histogram and each pair's rank among the block's pairs of the
 // same expert (token order).
 hipError_t launch_hist_rank(const int* idx, int s, int k, int E, int* blk_hist, int* rank,
@@ -20,9 +22,6 @@ hipError_t launch_scan(const int* blk_hist, int nb, int E, int P, int* blk_base,
 hipError_t launch_scatter(const int* idx, const int* rank, const int* blk_base, int s, int k, int E,
                           int* perm, int* inv, int* row_tok, hipStream_t st);
 
-// dst[i, :] = src[map[i] / div, :] for i < rows (row of `row_elems` elements).
-hipError_t launch_gather_rows(int dtype, const void* src, void* dst, const int* map, int div,
-                              int rows, int row_elems, hipStream_t st);
 // Y[t] = sum_j w[t,j] o[inv[t k + j]] (fp32 accumulate, slot order).
 hipError_t launch_combine(int dtype, const void* o, const int* inv, const float* w, void* Y, int s,
                           int k, int m, hipStream_t st);

@@ -17,9 +17,13 @@ namespace {
 // ---------------------------------------------------------------------------------------- top-k
 constexpr int kMaxPerLane = 16;  // E <= 1024
 
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ z, int s, int E, int k,
-                                                   int score, int renorm, int* __restrict__ idx,
-                                                   float* __restrict__ w, float* __restrict__ psel) {
+// z holds nsplit partial logit arrays (split_stride floats apart), summed here in split order;
+// with nsplit > 1 the sums are also written to zout.
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ z, int nsplit,
+                                                   long split_stride, float* __restrict__ zout, int s,
+                                                   int E, int k, int score, int renorm,
+                                                   int* __restrict__ idx, float* __restrict__ w,
+                                                   float* __restrict__ psel) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= s) return;
@@ -30,8 +34,15 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ z, 
 #pragma unroll
   for (int q = 0; q < kMaxPerLane; q++) {
     const int e = lane + 64 * q;
-    v[q] = (q < npl && e < E) ? zt[e] : -INFINITY;
-    if (!(q < npl && e < E)) taken |= 1u << q;
+    const bool in = q < npl && e < E;
+    float acc = -INFINITY;
+    if (in) {
+      acc = zt[e];
+      for (int p = 1; p < nsplit; p++) acc += zt[(long)p * split_stride + e];
+      if (nsplit > 1 && zout) zout[(long)t * E + e] = acc;
+    }
+    v[q] = acc;
+    if (!in) taken |= 1u << q;
   }
   float selv[kMaxPerLane];  // lane L keeps the values of slots j with j % 64 == L
   for (int j = 0; j < k; j++) {
@@ -215,22 +226,6 @@ __global__ void scatter_kernel(const int* __restrict__ idx, const int* __restric
 
 // --------------------------------------------------------------------------- data movement
 // Rows are moved as 16-byte chunks; row_elems * sizeof(T) is a multiple of 16.
-template <typename T>
-__global__ __launch_bounds__(256) void gather_rows_kernel(const T* __restrict__ src, T* __restrict__ dst,
-                                                          const int* __restrict__ map, int div, int rows,
-                                                          int row_elems) {
-  constexpr int V = 16 / sizeof(T);
-  const int cpr = row_elems / V;
-  const long total = (long)rows * cpr;
-  for (long c = (long)blockIdx.x * blockDim.x + threadIdx.x; c < total; c += (long)gridDim.x * blockDim.x) {
-    const long i = c / cpr;
-    const int q = (int)(c - i * cpr);
-    const long srow = map[i] / div;
-    *reinterpret_cast<i32x4_t*>(dst + i * row_elems + q * V) =
-        *reinterpret_cast<const i32x4_t*>(src + srow * row_elems + q * V);
-  }
-}
-
 template <typename T> struct Vec8;
 template <> struct Vec8<bf16_t> {
   static constexpr int N = 8;
@@ -393,11 +388,11 @@ __global__ void zero_kernel(int* p, size_t n) {
 
 }  // namespace
 
-hipError_t launch_topk(const float* z, int s, int E, int k, int score, int renorm, int* idx,
-                       float* w, float* psel, hipStream_t st) {
+hipError_t launch_topk(const float* z, int nsplit, long split_stride, float* zout, int s, int E,
+                       int k, int score, int renorm, int* idx, float* w, float* psel, hipStream_t st) {
   if (s <= 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3((s + 3) / 4), dim3(256), 0, st, z, s, E, k, score, renorm,
-                     idx, w, psel);
+  hipLaunchKernelGGL(topk_kernel, dim3((s + 3) / 4), dim3(256), 0, st, z, nsplit, split_stride, zout,
+                     s, E, k, score, renorm, idx, w, psel);
   return hipGetLastError();
 }
 
@@ -426,19 +421,6 @@ hipError_t launch_scatter(const int* idx, const int* rank, const int* blk_base, 
   return hipGetLastError();
 }
 
-hipError_t launch_gather_rows(int dtype, const void* src, void* dst, const int* map, int div,
-                              int rows, int row_elems, hipStream_t st) {
-  if (rows <= 0) return hipSuccess;
-  const long chunks = (long)rows * row_elems * (dtype ? 2 : 4) / 16;
-  const long blocks = std::min<long>((chunks + 255) / 256, 256L * 64);
-  if (dtype)
-    hipLaunchKernelGGL(gather_rows_kernel<bf16_t>, dim3((unsigned)blocks), dim3(256), 0, st,
-                       (const bf16_t*)src, (bf16_t*)dst, map, div, rows, row_elems);
-  else
-    hipLaunchKernelGGL(gather_rows_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st,
-                       (const float*)src, (float*)dst, map, div, rows, row_elems);
-  return hipGetLastError();
-}
 
 hipError_t launch_combine(int dtype, const void* o, const int* inv, const float* w, void* Y, int s,
                           int k, int m, hipStream_t st) {
