@@ -88,7 +88,7 @@ __device__ inline int lchk(int byte_off, int bytes, int limit) {
   }
   return byte_off;
 }
-#define GCHK(p, bytes) ((decltype(p))gchk((p), (bytes)))
+#define GCHK(p, bytes) ((std::remove_reference_t<decltype(p)>)gchk((p), (bytes)))
 #else
 #define GCHK(p, bytes) (p)
 #endif
@@ -476,7 +476,7 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
   constexpr int LDS_BYTES = 2 * STAGE * (int)sizeof(bf16_t);
   static_assert(A_CPT * NT * 8 == A_ELEMS && B_CPT * NT * 8 == BN * BKT, "tile/thread mismatch");
   static_assert(!DUAL || TN % 2 == 0, "dual epilogue needs an even TN");
-  static_assert(BL == LAYOUT_XK || CPR_B >= 8, "KX tiles need >= 8 chunks per row");
+  static_assert(BL == LAYOUT_XK || CPR_B >= 4, "KX tiles need >= 4 chunks per row");
   __shared__ __attribute__((aligned(16))) bf16_t smem[2 * STAGE];
 #ifdef MOE_GEMM_BOUNDS_CHECK
   auto lds = [&](bf16_t* p, int bytes) -> bf16_t* {
@@ -982,9 +982,20 @@ using CfgSkinny = TileCfg<4, 1, 1, 1, 64, 2>;      // 128 x 32
 using CfgSkinnyDual = TileCfg<4, 1, 1, 2, 64, 2>;  // 128 x (32 + 32)
 using CfgMid = TileCfg<2, 2, 2, 2, 64, 2>;         // 128 x 128
 
+template <int WM, int WN, int TM, int TN, int BL, int EPI>
+hipError_t launch_gm_ring(const GemmArgs& a, int rows_bound, hipStream_t stream);
+
 template <int BL, int EPI, typename OutT>
 hipError_t dispatch_gm_mfma(const GemmArgs& a, int rows_bound, hipStream_t stream) {
   constexpr bool DUAL = (EPI == EPI_DUAL || EPI == EPI_SWIGLU);
+  // grouped low-rank products (N <= 32, bf16 out): 32- and 64-row tiles give ~P/32 and ~P/64
+  // workgroups (the 128-row skinny tiles leave most of the chip idle on these short launches)
+  if constexpr (std::is_same<OutT, bf16_t>::value && EPI != EPI_SWIGLU && EPI != EPI_SWIGLU_BWD) {
+    if (a.goff && a.N <= 32 && a.tail == TAIL_NONE) {
+      if constexpr (DUAL) return launch_gm_ring<2, 1, 1, 2, BL, EPI>(a, rows_bound, stream);
+      else return launch_gm_ring<1, 1, 1, 1, BL, EPI>(a, rows_bound, stream);
+    }
+  }
   if constexpr (DUAL) {
     if (a.N <= 32) return launch_gm_mfma<CfgSkinnyDual, BL, EPI, OutT>(a, rows_bound, stream);
     return launch_gm_mfma<CfgMid, BL, EPI, OutT>(a, rows_bound, stream);
@@ -994,14 +1005,16 @@ hipError_t dispatch_gm_mfma(const GemmArgs& a, int rows_bound, hipStream_t strea
   }
 }
 
-// Deep-prefetch kernel for the launches with a Split-LoRA tail.
+// Deep-prefetch kernel (grouped launches).
 template <int WM, int WN, int TM, int TN, int BL, int EPI>
 hipError_t launch_gm_ring(const GemmArgs& a, int rows_bound, hipStream_t stream) {
   constexpr bool DUAL = (EPI == EPI_DUAL || EPI == EPI_SWIGLU);
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32, BNH = DUAL ? BN / 2 : BN;
-  if (!a.goff || !a.toff_all || !a.tmap_all || a.K % 64 || a.tail == TAIL_NONE) return hipErrorInvalidValue;
-  const int K2 = a.tail == TAIL_SINGLE ? a.r2a : 2 * a.r2a;
-  if (K2 <= 0 || K2 > 128 || K2 % 8) return hipErrorInvalidValue;
+  if (!a.goff || !a.toff_all || !a.tmap_all || a.K % 64 || a.kchunk) return hipErrorInvalidValue;
+  if (a.tail != TAIL_NONE) {
+    const int K2 = a.tail == TAIL_SINGLE ? a.r2a : 2 * a.r2a;
+    if (K2 <= 0 || K2 > 128 || K2 % 8) return hipErrorInvalidValue;
+  }
   const int tidx = tile_table_index(BM);
   if (tidx < 0) return hipErrorInvalidValue;
   const long tilesN = (a.N + BNH - 1) / BNH;
