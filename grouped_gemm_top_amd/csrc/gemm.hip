@@ -622,6 +622,45 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
     step(IC<3>{}, kt + 3);
   }
 
+  // ---- epilogue (after the tail): each wave stages its fp32 accumulators in its own LDS region, then writes whole
+  //      16-byte row chunks (8 columns). Staged row r keeps its 4-float groups XOR-permuted by one
+  //      bit of r, which makes both the MFMA-layout writes and the row-chunk reads conflict-free.
+  constexpr int WR = TM * 32, WC = TN * 32;   // rows and columns of a wave's tile
+  constexpr int CH = WC / 8;                  // 8-column chunks per staged row
+  constexpr int PER = WR * CH / 64;           // chunks per lane
+  static_assert(NW * WR * WC * (int)sizeof(float) <= LDS_BYTES, "staging fits the LDS stages");
+  static_assert((WR * CH) % 64 == 0, "whole chunks per lane");
+  auto sidx = [](int r, int c) { return r * WC + (c ^ (((r >> (WC >= 64 ? 0 : 1)) & 1) << 2)); };
+  const int wrow0 = row0 + wm * WR;
+  bf16_t* C = (bf16_t*)a.C;
+  auto pack8 = [](const float* f) {
+    i32x4_t o;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      o[i] = (int)((unsigned)f32_to_bf16(f[2 * i]) | ((unsigned)f32_to_bf16(f[2 * i + 1]) << 16));
+    return o;
+  };
+  auto unpack8 = [](const i32x4_t& v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      f[2 * i] = bf16_to_f32((bf16_t)(v[i] & 0xffff));
+      f[2 * i + 1] = bf16_to_f32((bf16_t)((unsigned)v[i] >> 16));
+    }
+  };
+  // SwiGLU backward reads the saved [g | u] chunks of the lane's outputs; issue those loads first
+  i32x4_t gch[EPI == EPI_SWIGLU_BWD ? PER : 1], uch[EPI == EPI_SWIGLU_BWD ? PER : 1];
+  if constexpr (EPI == EPI_SWIGLU_BWD) {
+    const bf16_t* GU = (const bf16_t*)a.GU;
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+      const int q = lane + 64 * i, r = q / CH, c8 = q % CH;
+      const int grow = min(wrow0 + r, row_end - 1);
+      const int gcol = min(j0 + wn * WC + 8 * c8, a.N - 8);
+      gch[i] = ld16(GCHK(GU + (long)grow * a.ldgu + gcol, 16));
+      uch[i] = ld16(GCHK(GU + (long)grow * a.ldgu + a.guup + gcol, 16));
+    }
+  }
+
   // ---- Split-LoRA tail: [TA | 0] . [TB ; 0] over K2 <= 128 more reduction rows
   if (a.tail != TAIL_NONE) {
     lds_barrier();  // every wave is done with both stages
@@ -679,56 +718,88 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
     if (tsteps > 1) compute(s1);
   }
 
-  // ---- epilogue (compile-time accumulator indices; one 32-row MFMA tile row at a time)
-  bf16_t* C = (bf16_t*)a.C;
+  lds_barrier();  // every wave is done reading the K-tile stages
+  float* stg = reinterpret_cast<float*>(smem) + wave * WR * WC;
   static_for<TM>([&](auto tmc) {
     constexpr int tm = decltype(tmc)::value;
-    __builtin_amdgcn_sched_barrier(0);
-    static_for<16>([&](auto vc) {
-      constexpr int v = decltype(vc)::value;
-      const int row = row0 + wm * TM * 32 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (row < row_end) {
-        if constexpr (DUAL) {
-          static_for<TN / 2>([&](auto tc) {
-            constexpr int t2 = decltype(tc)::value;
-            const int jj = j0 + wn * (TN / 2) * 32 + t2 * 32 + (lane & 31);
-            if (jj < a.N) {
-              const float g = acc[tm][t2][v], uu = acc[tm][t2 + TN / 2][v];
-              if constexpr (EPI == EPI_DUAL) {
-                *GCHK(C + (long)row * a.ldc + jj, 2) = f32_to_bf16(a.scale * g);
-                *GCHK(C + (long)row * a.ldc + a.cup + jj, 2) = f32_to_bf16(a.scale * uu);
-              } else {
-                *GCHK(C + (long)row * a.ldc + jj, 2) = f32_to_bf16(g);
-                *GCHK(C + (long)row * a.ldc + a.cup + jj, 2) = f32_to_bf16(uu);
-                *GCHK((bf16_t*)a.H + (long)row * a.ldh + jj, 2) = f32_to_bf16(silu_f(g) * uu);
-              }
-            }
-          });
-        } else {
-          static_for<TN>([&](auto tc) {
-            constexpr int tn = decltype(tc)::value;
-            const int jj = j0 + wn * TN * 32 + tn * 32 + (lane & 31);
-            if (jj < a.N) {
-              const float val = a.scale * acc[tm][tn][v];
-              if constexpr (EPI == EPI_STORE) {
-                *GCHK(C + (long)row * a.ldc + jj, 2) = f32_to_bf16(val + (a.bias ? a.bias[jj] : 0.0f));
-              } else {  // EPI_SWIGLU_BWD
-                const bf16_t* GU = (const bf16_t*)a.GU;
-                const float g = bf16_to_f32(*GCHK(GU + (long)row * a.ldgu + jj, 2));
-                const float uu = bf16_to_f32(*GCHK(GU + (long)row * a.ldgu + a.guup + jj, 2));
-                const float sg = 1.0f / (1.0f + __expf(-g));
-                *GCHK(C + (long)row * a.ldc + jj, 2) = f32_to_bf16(val * uu * sg * (1.0f + g * (1.0f - sg)));
-                *GCHK(C + (long)row * a.ldc + a.cup + jj, 2) = f32_to_bf16(val * g * sg);
-              }
-            }
-          });
-        }
-      }
+    static_for<TN>([&](auto tnc) {
+      constexpr int tn = decltype(tnc)::value;
+      static_for<16>([&](auto vc) {
+        constexpr int v = decltype(vc)::value;
+        const int r = tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        stg[sidx(r, tn * 32 + (lane & 31))] = acc[tm][tn][v];
+      });
     });
   });
+  // (a wave reads back only its own region: its LDS operations complete in issue order)
+  auto rd8 = [&](int r, int c8, float* f) {
+    const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(stg + sidx(r, 8 * c8));
+    const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(stg + sidx(r, 8 * c8 + 4));
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      f[i] = lo[i];
+      f[4 + i] = hi[i];
+    }
+  };
+  if constexpr (DUAL) {
+    constexpr int HC = CH / 2;  // gate chunks per row; the up chunk of the same columns is HC later
+#pragma unroll
+    for (int i = 0; i < WR * HC / 64; i++) {
+      const int q = lane + 64 * i, r = q / HC, c8 = q % HC;
+      const int grow = wrow0 + r;
+      const int gcol = j0 + wn * (WC / 2) + 8 * c8;
+      if (grow < row_end && gcol < a.N) {
+        float g[8], uu[8];
+        rd8(r, c8, g);
+        rd8(r, c8 + HC, uu);
+        if constexpr (EPI == EPI_DUAL) {
+#pragma unroll
+          for (int j = 0; j < 8; j++) {
+            g[j] *= a.scale;
+            uu[j] *= a.scale;
+          }
+        } else {
+          float hh[8];
+#pragma unroll
+          for (int j = 0; j < 8; j++) hh[j] = silu_f(g[j]) * uu[j];
+          *reinterpret_cast<i32x4_t*>(GCHK((bf16_t*)a.H + (long)grow * a.ldh + gcol, 16)) = pack8(hh);
+        }
+        *reinterpret_cast<i32x4_t*>(GCHK(C + (long)grow * a.ldc + gcol, 16)) = pack8(g);
+        *reinterpret_cast<i32x4_t*>(GCHK(C + (long)grow * a.ldc + a.cup + gcol, 16)) = pack8(uu);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+      const int q = lane + 64 * i, r = q / CH, c8 = q % CH;
+      const int grow = wrow0 + r;
+      const int gcol = j0 + wn * WC + 8 * c8;
+      if (grow < row_end && gcol < a.N) {
+        float f[8];
+        rd8(r, c8, f);
+        if constexpr (EPI == EPI_STORE) {
+#pragma unroll
+          for (int j = 0; j < 8; j++) f[j] = a.scale * f[j] + (a.bias ? a.bias[gcol + j] : 0.0f);
+          *reinterpret_cast<i32x4_t*>(GCHK(C + (long)grow * a.ldc + gcol, 16)) = pack8(f);
+        } else {  // EPI_SWIGLU_BWD: f = dh; dg = dh u s (1 + g (1 - s)), du = dh silu(g)
+          float g[8], uu[8], dg[8], du[8];
+          unpack8(gch[i], g);
+          unpack8(uch[i], uu);
+#pragma unroll
+          for (int j = 0; j < 8; j++) {
+            const float dh = a.scale * f[j];
+            const float sg = 1.0f / (1.0f + __expf(-g[j]));
+            dg[j] = dh * uu[j] * sg * (1.0f + g[j] * (1.0f - sg));
+            du[j] = dh * g[j] * sg;
+          }
+          *reinterpret_cast<i32x4_t*>(GCHK(C + (long)grow * a.ldc + gcol, 16)) = pack8(dg);
+          *reinterpret_cast<i32x4_t*>(GCHK(C + (long)grow * a.ldc + a.cup + gcol, 16)) = pack8(du);
+        }
+      }
+    }
+  }
 }
 
-// ------------------------------------------------------------------------------------------------
 // K-grouped MFMA GEMM: C_e = scale * L[rows_e]^T . R[rows_e]; both operands stored with the output
 // axis contiguous, so both fragments come from transposing LDS reads.
 template <int WM, int WN, int TM, int TN>
