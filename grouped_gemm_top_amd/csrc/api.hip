@@ -1,5 +1,6 @@
 // C ABI of libmoelora: argument checks, buffer layout and the launch sequence of the MoE-LoRA
 // layer (routing, forward, backward). See include/moelora.h for the contract of each call.
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -57,6 +58,8 @@ struct BwdBufs {
   float* dz;
   void* WrT;
   void *Ud, *dgu, *Ugu, *dXp;
+  float* gkpart;  // partial LoRA-factor gradients of experts longer than one row chunk, one region
+                  // per gradient launch (outputs n x r, m x r, m x 2r, n x r, n x r)
 };
 
 inline size_t esize(const moe_shape& s) { return s.dtype == MOE_DTYPE_BF16 ? 2 : 4; }
@@ -106,6 +109,7 @@ size_t bwd_layout(const moe_shape& s, void* base, BwdBufs* bb) {
   b.dgu = c.bytes(P * 2 * s.n * es);
   b.Ugu = c.bytes(P * 2 * s.r * es);
   b.dXp = c.bytes(P * s.m * es);
+  b.gkpart = c.take<float>((size_t)gk_part_floats((long)P, s.E, 1, 3L * (s.n + s.m) * s.r));
   if (bb) *bb = b;
   return align_up(c.off, 256);
 }
@@ -463,6 +467,20 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
     STAGE(ST_BWD_ROUTER, launch_transpose(s.dtype, W_r, b.WrT, s.m, s.E, hs));
   }
 
+  // LoRA-factor gradients (K-grouped launches): an expert longer than one row chunk leaves fp32
+  // partials in its launch's region of b.gkpart, and one reduce after the last of them completes all
+  const bool chunked = s.dtype == MOE_DTYPE_BF16 && !ref;
+  GemmArgs gk_jobs[kGkMaxJobs];
+  int n_gk = 0;
+  float* gk_next = b.gkpart;
+  auto gk_prep = [&](GemmArgs& a) {
+    a.gkpart = nullptr;
+    if (!chunked) return;
+    a.gkpart = gk_next;
+    gk_next += gk_part_floats((long)P, s.E, a.M, a.N);
+    gk_jobs[n_gk++] = a;
+  };
+
   GemmArgs base = gemm_args();
   base.G = s.E;
   base.goff = expert_off;
@@ -494,17 +512,18 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
   // dA_d = h^T Uc_d ;  dB_d = Tc_d^T dO  (computed as (dO^T Tc_d)^T)
   {
     GemmArgs a = base;
-    a.toff_all = nullptr;
     a.M = s.n; a.N = s.r;
     a.A = f.h; a.lda = s.n;
     a.B = b.Ud; a.ldb = s.r;
     a.C = dA_d; a.ldc = s.r; a.cstride = (long)n * r;
-    STAGE(ST_BWD_GRAD_D, gemm_gk_launch(a, s.dtype, ref, hs));
+    gk_prep(a);
+    STAGE(ST_BWD_GRAD_D, gemm_gk_launch(a, s.dtype, ref, Pi, hs));
     a.M = s.m; a.N = s.r;
     a.A = b.dO; a.lda = s.m;
     a.B = f.Td; a.ldb = s.r;
     a.C = dB_d; a.ldc = s.m; a.cstride = (long)r * m; a.ctrans = 1;
-    STAGE(ST_BWD_GRAD_D, gemm_gk_launch(a, s.dtype, ref, hs));
+    gk_prep(a);
+    STAGE(ST_BWD_GRAD_D, gemm_gk_launch(a, s.dtype, ref, Pi, hs));
   }
   // Uc_gu = c * [dg B_g^T | du B_u^T]
   {
@@ -534,23 +553,25 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
   // dA_g | dA_u = Xp^T [Uc_g | Uc_u] ;  dB_g = Tc_g^T dg, dB_u = Tc_u^T du
   {
     GemmArgs a = base;
-    a.toff_all = nullptr;
     a.M = s.m; a.N = 2 * s.r;
     a.A = X; a.lda = s.m; a.arow = perm; a.arow_div = s.k;
     a.B = b.Ugu; a.ldb = 2 * s.r;
     a.C = dA_g; a.C1 = dA_u; a.nsplit = s.r; a.ldc = s.r; a.cstride = (long)m * r;
-    STAGE(ST_BWD_GRAD_GU, gemm_gk_launch(a, s.dtype, ref, hs));
+    gk_prep(a);
+    STAGE(ST_BWD_GRAD_GU, gemm_gk_launch(a, s.dtype, ref, Pi, hs));
     GemmArgs bg = base;
-    bg.toff_all = nullptr;
     bg.M = s.n; bg.N = s.r;
     bg.A = b.dgu; bg.lda = 2 * s.n;
     bg.B = f.Tgu; bg.ldb = 2 * s.r;
     bg.C = dB_g; bg.ldc = s.n; bg.cstride = (long)r * n; bg.ctrans = 1;
-    STAGE(ST_BWD_GRAD_GU, gemm_gk_launch(bg, s.dtype, ref, hs));
+    gk_prep(bg);
+    STAGE(ST_BWD_GRAD_GU, gemm_gk_launch(bg, s.dtype, ref, Pi, hs));
     bg.A = (const char*)b.dgu + n * es;
     bg.B = (const char*)f.Tgu + r * es;
     bg.C = dB_u;
-    STAGE(ST_BWD_GRAD_GU, gemm_gk_launch(bg, s.dtype, ref, hs));
+    gk_prep(bg);
+    STAGE(ST_BWD_GRAD_GU, gemm_gk_launch(bg, s.dtype, ref, Pi, hs));
+    if (n_gk) STAGE(ST_BWD_GRAD_GU, gemm_gk_reduce(gk_jobs, n_gk, Pi, hs));
   }
   // unpermute: dX[t] = sum_j dXp[inv[t k + j]] (+ sum_j dz[t,j] W_r[:, idx[t,j]])
   STAGE(ST_BWD_UNPERMUTE, launch_unpermute(s.dtype, b.dXp, inv_perm, s.router_grad ? b.dz : nullptr, topk_idx,

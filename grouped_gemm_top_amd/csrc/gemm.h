@@ -77,6 +77,8 @@ struct GemmArgs {
   const void* GU;    // EPI_SWIGLU_BWD: saved [g | u]
   long ldgu;
   long guup;         // column offset of u in GU
+  float* gkpart;     // GK: fp32 partial products of groups longer than one chunk, [chunk][M][N]
+                     // (gk_part_floats); nullptr: one workgroup reduces a whole group
 };
 
 // Launchers (hipStream_t passed as void* to keep this header light). Each returns a HIP error.
@@ -84,11 +86,17 @@ struct GemmArgs {
 // GM: rows_bound = upper bound on the total number of rows over all groups (sizes the grid).
 hipError_t gemm_gm_launch(const GemmArgs& a, int b_layout, int epi, int out_f32, int dtype,
                           int rows_bound, int reference, hipStream_t stream);
-hipError_t gemm_gk_launch(const GemmArgs& a, int dtype, int reference, hipStream_t stream);
+// GK: rows_bound bounds the total group rows (sizes the chunk grid when a.gkpart is set).
+hipError_t gemm_gk_launch(const GemmArgs& a, int dtype, int reference, int rows_bound, hipStream_t stream);
 
 // Row-tile tables for the MFMA row tile sizes used by gemm_gm_launch.
-constexpr int kNumTileSizes = 4;
-constexpr int kTileSizes[kNumTileSizes] = {32, 64, 128, 256};
+constexpr int kNumTileSizes = 5;
+constexpr int kTileSizes[kNumTileSizes] = {32, 64, 128, 256, 1024};
+// K-grouped launches split a group's rows into chunks of kGkChunk rows (table kGkChunkTable), so
+// that one long group does not serialise its whole reduction in a few workgroups.
+constexpr int kGkChunkTable = 4;
+constexpr int kGkChunk = 1024;
+static_assert(kTileSizes[kGkChunkTable] == kGkChunk, "chunk table");
 int tile_table_index(int bm);
 // Row-tile -> group maps: map i has room for rows_bound / kTileSizes[i] + G entries (a row tile
 // never spans two groups, so there are at most that many tiles); maps are stored back to back.
@@ -99,4 +107,14 @@ __host__ __device__ inline long tile_map_offset(int i, long rows_bound, int G) {
   return o;
 }
 
+// Floats of GemmArgs::gkpart needed by a K-grouped launch with output M x N.
+inline long gk_part_floats(long rows_bound, int G, long M, long N) {
+  return tile_map_capacity(kGkChunkTable, rows_bound, G) * M * N;
+}
+// Completes chunked K-grouped launches (made with gkpart): for every job and every group with
+// several chunks, C_e = scale * (sum of the group's chunk partials, in chunk order). Up to
+// kGkMaxJobs launches of one routing are completed together.
+constexpr int kGkMaxJobs = 8;
+constexpr int kGkMaxGroups = 1024;
+hipError_t gemm_gk_reduce(const GemmArgs* jobs, int njobs, int rows_bound, hipStream_t stream);
 }  // namespace moe

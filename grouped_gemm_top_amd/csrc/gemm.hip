@@ -800,10 +800,26 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
   }
 }
 
+// Stores element (row, col) of group e's K-grouped output.
+__device__ inline void gk_store(const GemmArgs& a, int e, int row, int col, float v) {
+  float* C = (float*)a.C;
+  if (a.C1 && col >= a.nsplit) {
+    C = (float*)a.C1;
+    col -= a.nsplit;
+  }
+  C += (long)e * a.cstride;
+  C[a.ctrans ? (long)col * a.ldc + row : (long)row * a.ldc + col] = v;
+}
+
 // K-grouped MFMA GEMM: C_e = scale * L[rows_e]^T . R[rows_e]; both operands stored with the output
 // axis contiguous, so both fragments come from transposing LDS reads.
+// Without a.gkpart, one workgroup per output tile reduces all rows of its group. With it, work
+// units are (chunk of kGkChunk group rows, output tile), listed by the chunk table (toffc: chunk
+// prefix sums per group, tmapc: chunk -> group; an empty group has one empty chunk). A group of
+// one chunk stores its result directly; the chunks of a longer group store fp32 partials, which
+// gk_reduce adds up in chunk order after the launch.
 template <int WM, int WN, int TM, int TN>
-__global__ __launch_bounds__(WM * WN * 64) void gk_mfma(GemmArgs a) {
+__global__ __launch_bounds__(WM * WN * 64) void gk_mfma(GemmArgs a, const int* toffc, const int* tmapc) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32, NT = WM * WN * 64;
   constexpr int LDA = BM + PADE, LDB = BN + PADE;
   constexpr int A_ELEMS = BK * LDA, B_ELEMS = BK * LDB, STAGE = A_ELEMS + B_ELEMS;
@@ -815,12 +831,25 @@ __global__ __launch_bounds__(WM * WN * 64) void gk_mfma(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int tilesM = (a.M + BM - 1) / BM, tilesN = (a.N + BN - 1) / BN;
-  const int T = xcd_unit(a.G * tilesM * tilesN);
+  const int units = a.gkpart ? toffc[a.G] : a.G;
+  const int T = xcd_unit(units * tilesM * tilesN);
   if (T < 0) return;
-  const int e = T / (tilesM * tilesN);
-  const int rem = T - e * tilesM * tilesN;
+  const int u0 = T / (tilesM * tilesN);  // group (whole-group mode) or chunk
+  const int rem = T - u0 * tilesM * tilesN;
   const int nt = rem / tilesM, mt = rem - nt * tilesM;
-  const int kb = a.goff[e], ke = a.goff[e + 1];
+  int e, kb, ke, nch = 1;
+  int c0 = 0;
+  if (a.gkpart) {
+    e = tmapc[u0];
+    c0 = toffc[e];
+    nch = toffc[e + 1] - c0;
+    kb = a.goff[e] + (u0 - c0) * kGkChunk;
+    ke = min(kb + kGkChunk, a.goff[e + 1]);
+  } else {
+    e = u0;
+    kb = a.goff[e];
+    ke = a.goff[e + 1];
+  }
 
   int acol[A_PT], bcol[B_PT];
 #pragma unroll
@@ -906,13 +935,36 @@ __global__ __launch_bounds__(WM * WN * 64) void gk_mfma(GemmArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; v++) {
         const int row = mt * BM + wm * TM * 32 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        int col = nt * BN + wn * TN * 32 + tn * 32 + (lane & 31);
+        const int col = nt * BN + wn * TN * 32 + tn * 32 + (lane & 31);
         if (row >= a.M || col >= a.N) continue;
-        float* C = (float*)a.C;
-        if (a.C1 && col >= a.nsplit) { C = (float*)a.C1; col -= a.nsplit; }
-        C += (long)e * a.cstride;
-        C[a.ctrans ? (long)col * a.ldc + row : (long)row * a.ldc + col] = a.scale * acc[tm][tn][v];
+        if (nch == 1) gk_store(a, e, row, col, a.scale * acc[tm][tn][v]);
+        else a.gkpart[((long)u0 * a.M + row) * a.N + col] = acc[tm][tn][v];
       }
+}
+
+
+// Completion of chunked K-grouped launches: block (x, j) walks the groups of job j and, for each
+// group of several chunks, strides over its output with the gridDim.x blocks of the job (groups of
+// one chunk are already stored).
+struct GkJobs {
+  GemmArgs job[kGkMaxJobs];
+};
+__global__ __launch_bounds__(256) void gk_reduce(GkJobs jobs, const int* toffc) {
+  __shared__ int off[kGkMaxGroups + 1];
+  const GemmArgs& a = jobs.job[blockIdx.y];
+  if (toffc[a.G] == a.G) return;  // every group has one chunk (none has fewer): nothing to add up
+  for (int e = threadIdx.x; e <= a.G; e += 256) off[e] = toffc[e];
+  __syncthreads();
+  const long MN = (long)a.M * a.N;
+  for (int e = 0; e < a.G; e++) {
+    const int c0 = off[e], nch = off[e + 1] - c0;
+    if (nch <= 1) continue;
+    for (long idx = (long)blockIdx.x * 256 + threadIdx.x; idx < MN; idx += (long)gridDim.x * 256) {
+      float v = 0.0f;
+      for (int c = 0; c < nch; c++) v += a.gkpart[(long)(c0 + c) * MN + idx];
+      gk_store(a, e, (int)(idx / a.N), (int)(idx % a.N), a.scale * v);
+    }
+  }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -1160,7 +1212,8 @@ hipError_t gemm_gm_launch(const GemmArgs& a, int b_layout, int epi, int out_f32,
   }
 }
 
-hipError_t gemm_gk_launch(const GemmArgs& a, int dtype, int reference, hipStream_t stream) {
+hipError_t gemm_gk_launch(const GemmArgs& a, int dtype, int reference, int rows_bound,
+                          hipStream_t stream) {
   if (a.G <= 0 || a.M <= 0 || a.N <= 0) return hipSuccess;
   if (dtype == 0 || reference) {
     dim3 grid((a.N + 63) / 64, a.M, a.G);
@@ -1171,10 +1224,39 @@ hipError_t gemm_gk_launch(const GemmArgs& a, int dtype, int reference, hipStream
   // output rows = the wide dimension (m or n), output columns = the LoRA rank side
   constexpr int WM = 4, WN = 1, TM = 1, TN = 1;
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
-  const long units = (long)a.G * ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  const long tiles = (long)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  const int* toffc = nullptr;
+  const int* tmapc = nullptr;
+  long units = (long)a.G * tiles;
+  if (a.gkpart) {
+    if (!a.toff_all || !a.tmap_all || rows_bound < 0) return hipErrorInvalidValue;
+    toffc = a.toff_all + kGkChunkTable * (a.G + 1);
+    tmapc = a.tmap_all + tile_map_offset(kGkChunkTable, rows_bound, a.G);
+    units = tile_map_capacity(kGkChunkTable, rows_bound, a.G) * tiles;
+  }
   const long blocks = (units + 7) / 8 * 8;
-  hipLaunchKernelGGL((gk_mfma<WM, WN, TM, TN>), dim3((unsigned)blocks), dim3(WM * WN * 64), 0,
-                     stream, a);
+  if (blocks > 0)
+    hipLaunchKernelGGL((gk_mfma<WM, WN, TM, TN>), dim3((unsigned)blocks), dim3(WM * WN * 64), 0,
+                       stream, a, toffc, tmapc);
+  return hipGetLastError();
+}
+
+hipError_t gemm_gk_reduce(const GemmArgs* jobs, int njobs, int rows_bound, hipStream_t stream) {
+  if (njobs <= 0) return hipSuccess;
+  if (njobs > kGkMaxJobs) return hipErrorInvalidValue;
+  GkJobs j;
+  long mn = 0;
+  for (int i = 0; i < kGkMaxJobs; i++) j.job[i] = jobs[i < njobs ? i : 0];
+  for (int i = 0; i < njobs; i++) {
+    if (!jobs[i].gkpart || !jobs[i].toff_all || jobs[i].G != jobs[0].G) return hipErrorInvalidValue;
+    mn = std::max(mn, (long)jobs[i].M * jobs[i].N);
+  }
+  if (jobs[0].G <= 0 || mn <= 0) return hipSuccess;
+  if (jobs[0].G > kGkMaxGroups) return hipErrorInvalidValue;
+  const unsigned bx = (unsigned)std::min<long>((mn + 255) / 256, 256);
+  hipLaunchKernelGGL(gk_reduce, dim3(bx, (unsigned)njobs), dim3(256), 0, stream, j,
+                     (const int*)(jobs[0].toff_all + kGkChunkTable * (jobs[0].G + 1)));
+  (void)rows_bound;
   return hipGetLastError();
 }
 

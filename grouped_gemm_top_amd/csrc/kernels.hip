@@ -189,7 +189,8 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ blk_
   if (e == 0) off[E] = total;
   for (int i = 0; i < kNumTileSizes; i++) {
     const int bm = kTileSizes[i];
-    const int tiles = e < E ? (cnt + bm - 1) / bm : 0;
+    // (the K-grouped chunk table gives an empty group one empty chunk, which writes its zeros)
+    const int tiles = e < E ? (i == kGkChunkTable ? max(1, (cnt + bm - 1) / bm) : (cnt + bm - 1) / bm) : 0;
     int ttot;
     const int ts = block_exscan_1024(tiles, sh, &ttot);
     if (e < E) tile_tables[i * (E + 1) + e] = ts;
