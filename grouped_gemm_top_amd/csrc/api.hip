@@ -460,7 +460,7 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
   const size_t es = esize(s);
 
   // combine backward: dO = s_{t,j} dY_t, ds_{t,j} = dY_t . o_{t,j}
-  STAGE(ST_BWD_COMBINE, launch_combine_bwd(s.dtype, dY, f.o, perm, topk_w, b.dO, b.ds, Pi, s.k, s.m, hs));
+  STAGE(ST_BWD_COMBINE, launch_combine_bwd(s.dtype, dY, f.o, inv_perm, topk_w, b.dO, b.ds, s.s, s.k, s.m, hs));
   // router backward: dz on the selected logits; W_r^T rows for the unpermute
   if (s.router_grad) {
     STAGE(ST_BWD_ROUTER, launch_router_bwd(b.ds, topk_w, rs.psel, s.s, s.k, s.score, s.renormalize, b.dz, hs));

@@ -25,9 +25,10 @@ hipError_t launch_scatter(const int* idx, const int* rank, const int* blk_base, 
 // Y[t] = sum_j w[t,j] o[inv[t k + j]] (fp32 accumulate, slot order).
 hipError_t launch_combine(int dtype, const void* o, const int* inv, const float* w, void* Y, int s,
                           int k, int m, hipStream_t st);
-// dO[i] = w[p] dY[t], ds[p] = dY[t] . o[i] for row i holding pair p = perm[i], t = p / k.
-hipError_t launch_combine_bwd(int dtype, const void* dY, const void* o, const int* perm,
-                              const float* w, void* dO, float* ds, int P, int k, int m,
+// For each pair p = t k + j (row i = inv[p] of the grouped order): dO[i] = w[p] dY[t],
+// ds[p] = dY[t] . o[i].
+hipError_t launch_combine_bwd(int dtype, const void* dY, const void* o, const int* inv,
+                              const float* w, void* dO, float* ds, int s, int k, int m,
                               hipStream_t st);
 // dz[t, j] from ds, w, p_sel (softmax or sigmoid, renormalised or not).
 hipError_t launch_router_bwd(const float* ds, const float* w, const float* psel, int s, int k,

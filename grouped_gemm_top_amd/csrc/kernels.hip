@@ -261,6 +261,10 @@ template <> struct Vec8<float> {
   }
 };
 
+// The expert rows of one token are gathered in groups of up to kRowGroup, all loads of a group in
+// flight together (the token's k rows lie anywhere in the grouped order).
+constexpr int kRowGroup = 8;
+
 // One block per token; threads walk the row in 16-byte chunks.
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ o, const int* __restrict__ inv,
@@ -270,51 +274,81 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ o, c
   const long t = blockIdx.x;
   for (int c = threadIdx.x; c * V < m; c += blockDim.x) {
     float acc[V] = {};
-    for (int j = 0; j < k; j++) {
-      const float wj = w[t * k + j];
-      float f[V];
-      Vec8<T>::load(o + (long)inv[t * k + j] * m + c * V, f);
+    for (int j0 = 0; j0 < k; j0 += kRowGroup) {
+      float f[kRowGroup][V], wj[kRowGroup];
 #pragma unroll
-      for (int i = 0; i < V; i++) acc[i] += wj * f[i];
+      for (int jj = 0; jj < kRowGroup; jj++) {
+        if (j0 + jj < k) {
+          wj[jj] = w[t * k + j0 + jj];
+          Vec8<T>::load(o + (long)inv[t * k + j0 + jj] * m + c * V, f[jj]);
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < kRowGroup; jj++) {
+        if (j0 + jj < k) {
+#pragma unroll
+          for (int i = 0; i < V; i++) acc[i] += wj[jj] * f[jj][i];
+        }
+      }
     }
     Vec8<T>::store(Y + t * m + c * V, acc);
   }
 }
-
-// One block per group row.
+// One block per token: dO[inv[t k + j]] = w[t k + j] dY_t and ds[t k + j] = dY_t . o[inv[t k + j]]
+// for its k pairs, so that dY_t is read once.
 template <typename T>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ dY, const T* __restrict__ o,
-                                                          const int* __restrict__ perm,
+                                                          const int* __restrict__ inv,
                                                           const float* __restrict__ w, T* __restrict__ dO,
                                                           float* __restrict__ ds, int k, int m) {
   constexpr int V = Vec8<T>::N;
-  __shared__ float red[4];
-  const long i = blockIdx.x;
-  const int p = perm[i];
-  const long t = p / k;
-  const float wp = w[p];
-  float dot = 0.0f;
-  for (int c = threadIdx.x; c * V < m; c += blockDim.x) {
-    float fy[V], fo[V], out[V];
-    Vec8<T>::load(dY + t * m + c * V, fy);
-    Vec8<T>::load(o + i * m + c * V, fo);
+  __shared__ float red[4][kRowGroup];
+  const long t = blockIdx.x;
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  for (int j0 = 0; j0 < k; j0 += kRowGroup) {
+    long row[kRowGroup];
+    float wj[kRowGroup], dot[kRowGroup];
 #pragma unroll
-    for (int q = 0; q < V; q++) {
-      dot += fy[q] * fo[q];
-      out[q] = wp * fy[q];
+    for (int jj = 0; jj < kRowGroup; jj++) {
+      dot[jj] = 0.0f;
+      if (j0 + jj < k) {
+        row[jj] = inv[t * k + j0 + jj];
+        wj[jj] = w[t * k + j0 + jj];
+      }
     }
-    Vec8<T>::store(dO + i * m + c * V, out);
-  }
-  dot = wave_sum(dot);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = dot;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float sum = 0.0f;
-    for (int q = 0; q < (int)(blockDim.x >> 6); q++) sum += red[q];
-    ds[p] = sum;
+    for (int c = threadIdx.x; c * V < m; c += blockDim.x) {
+      float fy[V], fo[kRowGroup][V];
+      Vec8<T>::load(dY + t * m + c * V, fy);
+#pragma unroll
+      for (int jj = 0; jj < kRowGroup; jj++)
+        if (j0 + jj < k) Vec8<T>::load(o + row[jj] * m + c * V, fo[jj]);
+#pragma unroll
+      for (int jj = 0; jj < kRowGroup; jj++) {
+        if (j0 + jj < k) {
+          float out[V];
+#pragma unroll
+          for (int q = 0; q < V; q++) {
+            dot[jj] += fy[q] * fo[jj][q];
+            out[q] = wj[jj] * fy[q];
+          }
+          Vec8<T>::store(dO + row[jj] * m + c * V, out);
+        }
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < kRowGroup; jj++) {
+      const float d = wave_sum(dot[jj]);
+      if ((threadIdx.x & 63) == 0) red[wave][jj] = d;
+    }
+    __syncthreads();
+    if (threadIdx.x < kRowGroup && j0 + (int)threadIdx.x < k) {
+      float sum = 0.0f;
+      for (int q = 0; q < nw; q++) sum += red[q][threadIdx.x];
+      ds[t * k + j0 + threadIdx.x] = sum;
+    }
+    __syncthreads();
   }
 }
-
 __global__ void router_bwd_kernel(const float* __restrict__ ds, const float* __restrict__ w,
                                   const float* __restrict__ psel, int s, int k, int score, int renorm,
                                   float* __restrict__ dz) {
@@ -363,25 +397,39 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const T* __restrict__ dX
   const long t = blockIdx.x;
   for (int c = threadIdx.x; c * V < m; c += blockDim.x) {
     float acc[V] = {};
-    for (int j = 0; j < k; j++) {
-      float f[V];
-      Vec8<T>::load(dXp + (long)inv[t * k + j] * m + c * V, f);
+    for (int j0 = 0; j0 < k; j0 += kRowGroup) {
+      float f[kRowGroup][V];
 #pragma unroll
-      for (int i = 0; i < V; i++) acc[i] += f[i];
-    }
-    if (dz) {
-      for (int j = 0; j < k; j++) {
-        const float g = dz[t * k + j];
-        float f[V];
-        Vec8<T>::load(WrT + (long)idx[t * k + j] * m + c * V, f);
+      for (int jj = 0; jj < kRowGroup; jj++)
+        if (j0 + jj < k) Vec8<T>::load(dXp + (long)inv[t * k + j0 + jj] * m + c * V, f[jj]);
 #pragma unroll
-        for (int i = 0; i < V; i++) acc[i] += g * f[i];
+      for (int jj = 0; jj < kRowGroup; jj++) {
+        if (j0 + jj < k) {
+#pragma unroll
+          for (int i = 0; i < V; i++) acc[i] += f[jj][i];
+        }
+      }
+      if (dz) {
+        float g[kRowGroup];
+#pragma unroll
+        for (int jj = 0; jj < kRowGroup; jj++) {
+          if (j0 + jj < k) {
+            g[jj] = dz[t * k + j0 + jj];
+            Vec8<T>::load(WrT + (long)idx[t * k + j0 + jj] * m + c * V, f[jj]);
+          }
+        }
+#pragma unroll
+        for (int jj = 0; jj < kRowGroup; jj++) {
+          if (j0 + jj < k) {
+#pragma unroll
+            for (int i = 0; i < V; i++) acc[i] += g[jj] * f[jj][i];
+          }
+        }
       }
     }
     Vec8<T>::store(dX + t * m + c * V, acc);
   }
 }
-
 __global__ void zero_kernel(int* p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
     p[i] = 0;
@@ -435,16 +483,16 @@ hipError_t launch_combine(int dtype, const void* o, const int* inv, const float*
   return hipGetLastError();
 }
 
-hipError_t launch_combine_bwd(int dtype, const void* dY, const void* o, const int* perm,
-                              const float* w, void* dO, float* ds, int P, int k, int m,
+hipError_t launch_combine_bwd(int dtype, const void* dY, const void* o, const int* inv,
+                              const float* w, void* dO, float* ds, int s, int k, int m,
                               hipStream_t st) {
-  if (P <= 0) return hipSuccess;
+  if (s <= 0) return hipSuccess;
   if (dtype)
-    hipLaunchKernelGGL(combine_bwd_kernel<bf16_t>, dim3(P), dim3(256), 0, st, (const bf16_t*)dY,
-                       (const bf16_t*)o, perm, w, (bf16_t*)dO, ds, k, m);
+    hipLaunchKernelGGL(combine_bwd_kernel<bf16_t>, dim3(s), dim3(256), 0, st, (const bf16_t*)dY,
+                       (const bf16_t*)o, inv, w, (bf16_t*)dO, ds, k, m);
   else
-    hipLaunchKernelGGL(combine_bwd_kernel<float>, dim3(P), dim3(256), 0, st, (const float*)dY,
-                       (const float*)o, perm, w, (float*)dO, ds, k, m);
+    hipLaunchKernelGGL(combine_bwd_kernel<float>, dim3(s), dim3(256), 0, st, (const float*)dY,
+                       (const float*)o, inv, w, (float*)dO, ds, k, m);
   return hipGetLastError();
 }
 
