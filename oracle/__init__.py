@@ -207,7 +207,14 @@ def expert_rows_backward(Xr, dO, ew: dict, c: float, fwd: dict | None = None) ->
 
 # ----------------------------------------------------------------------------- layer
 
-def forward(X, W: dict, rt: dict, alpha: float, r: int, keep: bool = True):
+def lora_scale(alpha: float, r: int, rslora: bool = False) -> float:
+    """The LoRA scale c: alpha/r (Split LoRA [ALK] section "2. Split LoRA Associative
+    Transformation"), or alpha/sqrt(r) for rank-stabilised LoRA (bluecore.net/archives/629,
+    LoRA section, rsLoRA item)."""
+    return alpha / np.sqrt(r) if rslora else alpha / r
+
+
+def forward(X, W: dict, rt: dict, alpha: float, r: int, keep: bool = True, rslora: bool = False):
     """Layer output y_t = sum_j s_{t,j} Expert_{e_{t,j}}(x_t), evaluated over expert groups.
 
     [ALK] routing equation; experts run per contiguous group (perm), the combine sums the
@@ -215,7 +222,7 @@ def forward(X, W: dict, rt: dict, alpha: float, r: int, keep: bool = True):
     intermediates (rows in group order) when keep is set.
     """
     X = _f64(X)
-    c = alpha / r
+    c = lora_scale(alpha, r, rslora)
     k, E = rt["k"], rt["E"]
     s, m = X.shape
     P = s * k
@@ -271,7 +278,8 @@ def router_backward(ds, rt: dict, W_r, score: str = "softmax", renormalize: bool
 
 
 def backward(dY, X, W_r, W: dict, rt: dict, alpha: float, r: int, score: str = "softmax",
-             renormalize: bool = True, router_grad: bool = True, saved: dict | None = None):
+             renormalize: bool = True, router_grad: bool = True, saved: dict | None = None,
+             rslora: bool = False):
     """dX and the LoRA-factor gradients of the whole layer for upstream gradient dY.
 
     Returns dict with dX [s,m], dA_g/dA_u [E,m,r], dB_g/dB_u [E,r,n], dA_d [E,n,r],
@@ -279,14 +287,14 @@ def backward(dY, X, W_r, W: dict, rt: dict, alpha: float, r: int, score: str = "
     """
     dY = _f64(dY)
     X = _f64(X)
-    c = alpha / r
+    c = lora_scale(alpha, r, rslora)
     k, E = rt["k"], rt["E"]
     s, m = X.shape
     P = s * k
     n = W["W_d"].shape[1]
     perm, inv, off, w = rt["perm"], rt["inv"], rt["off"], rt["w"]
     if saved is None:
-        _, saved = forward(X, W, rt, alpha, r, keep=True)
+        _, saved = forward(X, W, rt, alpha, r, keep=True, rslora=rslora)
     o = saved["o"]
     tok_of_row = perm // k
     slot_of_row = perm % k

@@ -158,6 +158,31 @@ def test_split_lora_equals_dense_merge_and_per_token_loop(score):
     np.testing.assert_allclose(Y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
 
 
+def test_rslora_scale_is_alpha_over_sqrt_r():
+    """Rank-stabilised LoRA (bluecore.net/archives/629, LoRA section, rsLoRA item) scales the
+    low-rank update by alpha/sqrt(r): the forward equals the dense merge with that scale, and the
+    backward equals the plain-scale one at the alpha that gives the same c."""
+    rng = np.random.default_rng(6)
+    s, m, n, E, k, r, alpha = 29, 16, 8, 4, 2, 4, 6.0
+    X, W_r, W, dY = _rand_layer(rng, s, m, n, E, k, r)
+    c = alpha / math.sqrt(r)
+    rt = oracle.route(oracle.router_logits(X, W_r), k, E)
+    Y, sv = oracle.forward(X, W, rt, alpha, r, rslora=True)
+    ref = np.zeros((s, m))
+    for t in range(s):
+        for j in range(k):
+            Wg, Wu, Wd = _merged(W, int(rt["idx"][t, j]), c)
+            x = X[t]
+            ref[t] += rt["w"][t, j] * ((_silu(x @ Wg) * (x @ Wu)) @ Wd)
+    np.testing.assert_allclose(Y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    assert oracle.lora_scale(alpha, r, True) == c and oracle.lora_scale(alpha, r) == alpha / r
+    # backward: the same as the plain-scale oracle at alpha' = alpha sqrt(r) (same c)
+    g = oracle.backward(dY, X, W_r, W, rt, alpha, r, saved=sv, rslora=True)
+    g2 = oracle.backward(dY, X, W_r, W, rt, alpha * math.sqrt(r), r)
+    for key in ("dX", "dA_g", "dB_g", "dA_u", "dB_u", "dA_d", "dB_d"):
+        np.testing.assert_allclose(g[key], g2[key], rtol=1e-12, atol=1e-12 * np.abs(g2[key]).max())
+
+
 def test_single_expert_is_a_dense_swiglu_mlp():
     rng = np.random.default_rng(9)
     s, m, n, r, alpha = 11, 12, 6, 2, 4.0
