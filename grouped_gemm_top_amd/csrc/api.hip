@@ -60,9 +60,15 @@ struct BwdBufs {
   void *Ud, *dgu, *Ugu, *dXp;
   float* gkpart;  // partial LoRA-factor gradients of experts longer than one row chunk, one region
                   // per gradient launch (outputs n x r, m x r, m x 2r, n x r, n x r)
+  void *At_d, *At_g, *At_u;  // output-major base weights only: A_d, A_g, A_u per expert transposed
 };
 
 inline size_t esize(const moe_shape& s) { return s.dtype == MOE_DTYPE_BF16 ? 2 : 4; }
+// LoRA scale c: alpha / r, or alpha / sqrt(r) for rank-stabilised LoRA.
+inline float lora_scale(const moe_shape& s) {
+  return (s.flags & MOE_FLAG_RSLORA) ? s.alpha / std::sqrt((float)s.r) : s.alpha / (float)s.r;
+}
+inline bool out_in(const moe_shape& s) { return (s.flags & MOE_FLAG_WEIGHTS_OUT_IN) != 0; }
 inline long pairs(const moe_shape& s) { return (long)s.s * s.k; }
 inline int nblocks(const moe_shape& s) { return (s.s + kRouteBlockTokens - 1) / kRouteBlockTokens; }
 
@@ -97,6 +103,22 @@ size_t fwd_layout(const moe_shape& s, void* base, FwdBufs* fb) {
   return align_up(c.off, 256);
 }
 
+// Forward scratch for output-major base weights: B_g, B_u, B_d per expert transposed, so that the
+// Split-LoRA tails read them in the layout of the weights they extend.
+struct FwdFactors {
+  void *Bt_g, *Bt_u, *Bt_d;
+};
+size_t fwd_factor_layout(const moe_shape& s, void* base, FwdFactors* ff) {
+  Carve c(base);
+  const size_t es = esize(s), fac = out_in(s) ? 1 : 0;
+  FwdFactors f;
+  f.Bt_g = c.bytes(fac * s.E * s.r * s.n * es);
+  f.Bt_u = c.bytes(fac * s.E * s.r * s.n * es);
+  f.Bt_d = c.bytes(fac * s.E * s.r * s.m * es);
+  if (ff) *ff = f;
+  return align_up(c.off, 256);
+}
+
 size_t bwd_layout(const moe_shape& s, void* base, BwdBufs* bb) {
   Carve c(base);
   const size_t P = (size_t)pairs(s), es = esize(s);
@@ -110,6 +132,10 @@ size_t bwd_layout(const moe_shape& s, void* base, BwdBufs* bb) {
   b.Ugu = c.bytes(P * 2 * s.r * es);
   b.dXp = c.bytes(P * s.m * es);
   b.gkpart = c.take<float>((size_t)gk_part_floats((long)P, s.E, 1, 3L * (s.n + s.m) * s.r));
+  const size_t fac = out_in(s) ? 1 : 0;  // the tails then read the factors in the weights' layout
+  b.At_d = c.bytes(fac * s.E * s.r * s.n * es);
+  b.At_g = c.bytes(fac * s.E * s.r * s.m * es);
+  b.At_u = c.bytes(fac * s.E * s.r * s.m * es);
   if (bb) *bb = b;
   return align_up(c.off, 256);
 }
@@ -123,7 +149,8 @@ moe_status check_shape(const moe_shape* sp) {
   if (s.score != MOE_SCORE_SOFTMAX && s.score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
   if ((s.renormalize != 0 && s.renormalize != 1) || (s.router_grad != 0 && s.router_grad != 1))
     return MOE_ERR_INVALID_ARG;
-  if (s.flags & ~MOE_FLAG_REFERENCE_GEMM) return MOE_ERR_INVALID_ARG;
+  if (s.flags & ~(MOE_FLAG_REFERENCE_GEMM | MOE_FLAG_RSLORA | MOE_FLAG_WEIGHTS_OUT_IN))
+    return MOE_ERR_INVALID_ARG;
   if (!std::isfinite(s.alpha)) return MOE_ERR_INVALID_ARG;
   if (s.m % 64 || s.n % 64) return MOE_ERR_UNSUPPORTED;
   if (s.E > 1024 || s.r > 64) return MOE_ERR_UNSUPPORTED;
@@ -252,7 +279,7 @@ size_t moe_fwd_saved_bytes(const moe_shape* shape) {
 
 size_t moe_fwd_ws_bytes(const moe_shape* shape, int32_t with_saved) {
   if (check_shape(shape) != MOE_OK) return 0;
-  return with_saved ? 0 : fwd_layout(*shape, nullptr, nullptr);
+  return (with_saved ? 0 : fwd_layout(*shape, nullptr, nullptr)) + fwd_factor_layout(*shape, nullptr, nullptr);
 }
 
 size_t moe_bwd_ws_bytes(const moe_shape* shape) {
@@ -332,24 +359,33 @@ moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t
     return MOE_ERR_INVALID_ARG;
   if (!route_state || ((uintptr_t)route_state & 255u)) return MOE_ERR_INVALID_ARG;
   const size_t need_saved = fwd_layout(s, nullptr, nullptr);
+  const size_t need_fac = fwd_factor_layout(s, nullptr, nullptr);
+  const size_t need_ws = (saved ? 0 : need_saved) + need_fac;
   void* inter = saved;
   if (saved) {
     if ((uintptr_t)saved & 255u) return MOE_ERR_INVALID_ARG;
     if (saved_bytes < need_saved) return MOE_ERR_WORKSPACE;
   } else {
-    if (ws_bytes < need_saved) return MOE_ERR_WORKSPACE;
-    if (need_saved && (!ws || ((uintptr_t)ws & 255u))) return MOE_ERR_INVALID_ARG;
     inter = ws;
   }
+  if (ws_bytes < need_ws) return MOE_ERR_WORKSPACE;
+  if (need_ws && (!ws || ((uintptr_t)ws & 255u))) return MOE_ERR_INVALID_ARG;
   if (s.s == 0) return MOE_OK;
   hipStream_t hs = (hipStream_t)stream;
   RouteState rs;
   route_layout(s, const_cast<void*>(route_state), &rs);
   FwdBufs f;
   fwd_layout(s, inter, &f);
+  FwdFactors ff;
+  fwd_factor_layout(s, (char*)ws + (saved ? 0 : need_saved), &ff);
   const int ref = (s.flags & MOE_FLAG_REFERENCE_GEMM) ? 1 : 0;
-  const float c = s.alpha / (float)s.r;
+  const float c = lora_scale(s);
   const int Pi = (int)P;
+  if (out_in(s)) {  // [E, r, n] -> [E, n, r] and [E, r, m] -> [E, m, r]
+    STAGE(ST_FWD_GATE_UP, launch_transpose(s.dtype, B_g, ff.Bt_g, s.r, s.n, s.E, hs));
+    STAGE(ST_FWD_GATE_UP, launch_transpose(s.dtype, B_u, ff.Bt_u, s.r, s.n, s.E, hs));
+    STAGE(ST_FWD_DOWN, launch_transpose(s.dtype, B_d, ff.Bt_d, s.r, s.m, s.E, hs));
+  }
 
 
   GemmArgs base = gemm_args();
@@ -374,13 +410,24 @@ moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t
     GemmArgs a = base;
     a.N = s.n; a.K = s.m;
     a.A = X; a.lda = s.m; a.arow = perm; a.arow_div = s.k;
-    a.B = W_gu; a.Bu = (const char*)W_gu + n * esize(s); a.ldb = 2 * s.n; a.bstride = (long)m * 2 * n;
+    a.B = W_gu; a.bstride = (long)m * 2 * n;
+    if (out_in(s)) {  // W_gu [E, 2n, m]: the up half starts n rows in
+      a.Bu = (const char*)W_gu + n * m * esize(s); a.ldb = s.m;
+    } else {          // W_gu [E, m, 2n]: the up half starts n columns in
+      a.Bu = (const char*)W_gu + n * esize(s); a.ldb = 2 * s.n;
+    }
     a.tail = TAIL_BLOCKDIAG; a.r2a = s.r;
     a.TA = f.Tgu; a.lda2 = 2 * s.r;
-    a.TB0 = B_g; a.TB1 = B_u; a.ldtb = s.n; a.tbstride = (long)r * n;
+    if (out_in(s)) {
+      a.TB0 = ff.Bt_g; a.TB1 = ff.Bt_u; a.ldtb = s.r;
+    } else {
+      a.TB0 = B_g; a.TB1 = B_u; a.ldtb = s.n;
+    }
+    a.tbstride = (long)r * n;
     a.C = f.gu; a.ldc = 2 * s.n; a.cup = s.n;
     a.H = f.h; a.ldh = s.n;
-    STAGE(ST_FWD_GATE_UP, gemm_gm_launch(a, LAYOUT_KX, EPI_SWIGLU, 0, s.dtype, Pi, ref, hs));
+    STAGE(ST_FWD_GATE_UP, gemm_gm_launch(a, out_in(s) ? LAYOUT_XK : LAYOUT_KX, EPI_SWIGLU, 0, s.dtype, Pi,
+                                         ref, hs));
   }
   // Tc_d = c * h A_d
   {
@@ -396,12 +443,13 @@ moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t
     GemmArgs a = base;
     a.N = s.m; a.K = s.n;
     a.A = f.h; a.lda = s.n;
-    a.B = W_d; a.ldb = s.m; a.bstride = (long)n * m;
+    a.B = W_d; a.ldb = out_in(s) ? s.n : s.m; a.bstride = (long)n * m;
     a.tail = TAIL_SINGLE; a.r2a = s.r;
     a.TA = f.Td; a.lda2 = s.r;
-    a.TB0 = B_d; a.ldtb = s.m; a.tbstride = (long)r * m;
+    a.TB0 = out_in(s) ? ff.Bt_d : B_d; a.ldtb = out_in(s) ? s.r : s.m; a.tbstride = (long)r * m;
     a.C = f.o; a.ldc = s.m;
-    STAGE(ST_FWD_DOWN, gemm_gm_launch(a, LAYOUT_KX, EPI_STORE, 0, s.dtype, Pi, ref, hs));
+    STAGE(ST_FWD_DOWN, gemm_gm_launch(a, out_in(s) ? LAYOUT_XK : LAYOUT_KX, EPI_STORE, 0, s.dtype, Pi, ref,
+                                      hs));
   }
   // combine
   STAGE(ST_FWD_COMBINE, launch_combine(s.dtype, f.o, inv_perm, topk_w, Y, s.s, s.k, s.m, hs));
@@ -455,7 +503,7 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
   BwdBufs b;
   bwd_layout(s, ws, &b);
   const int ref = (s.flags & MOE_FLAG_REFERENCE_GEMM) ? 1 : 0;
-  const float c = s.alpha / (float)s.r;
+  const float c = lora_scale(s);
   const int Pi = (int)P;
   const size_t es = esize(s);
 
@@ -464,7 +512,7 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
   // router backward: dz on the selected logits; W_r^T rows for the unpermute
   if (s.router_grad) {
     STAGE(ST_BWD_ROUTER, launch_router_bwd(b.ds, topk_w, rs.psel, s.s, s.k, s.score, s.renormalize, b.dz, hs));
-    STAGE(ST_BWD_ROUTER, launch_transpose(s.dtype, W_r, b.WrT, s.m, s.E, hs));
+    STAGE(ST_BWD_ROUTER, launch_transpose(s.dtype, W_r, b.WrT, s.m, s.E, 1, hs));
   }
 
   // LoRA-factor gradients (K-grouped launches): an expert longer than one row chunk leaves fp32
@@ -501,13 +549,20 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
     GemmArgs a = base;
     a.N = s.n; a.K = s.m;
     a.A = b.dO; a.lda = s.m;
-    a.B = W_d; a.ldb = s.m; a.bstride = (long)n * m;
+    a.B = W_d; a.ldb = out_in(s) ? s.n : s.m; a.bstride = (long)n * m;
     a.tail = TAIL_SINGLE; a.r2a = s.r;
     a.TA = b.Ud; a.lda2 = s.r;
-    a.TB0 = A_d; a.ldtb = s.r; a.tbstride = (long)n * r;
+    if (out_in(s)) {  // A_d [E, n, r] -> [E, r, n]
+      STAGE(ST_BWD_DOWN, launch_transpose(s.dtype, A_d, b.At_d, s.n, s.r, s.E, hs));
+      a.TB0 = b.At_d; a.ldtb = s.n;
+    } else {
+      a.TB0 = A_d; a.ldtb = s.r;
+    }
+    a.tbstride = (long)n * r;
     a.GU = f.gu; a.ldgu = 2 * s.n; a.guup = s.n;
     a.C = b.dgu; a.ldc = 2 * s.n; a.cup = s.n;
-    STAGE(ST_BWD_DOWN, gemm_gm_launch(a, LAYOUT_XK, EPI_SWIGLU_BWD, 0, s.dtype, Pi, ref, hs));
+    STAGE(ST_BWD_DOWN, gemm_gm_launch(a, out_in(s) ? LAYOUT_KX : LAYOUT_XK, EPI_SWIGLU_BWD, 0, s.dtype, Pi,
+                                      ref, hs));
   }
   // dA_d = h^T Uc_d ;  dB_d = Tc_d^T dO  (computed as (dO^T Tc_d)^T)
   {
@@ -543,12 +598,20 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
     GemmArgs a = base;
     a.N = s.m; a.K = 2 * s.n;
     a.A = b.dgu; a.lda = 2 * s.n;
-    a.B = W_gu; a.ldb = 2 * s.n; a.bstride = (long)m * 2 * n;
+    a.B = W_gu; a.ldb = out_in(s) ? s.m : 2 * s.n; a.bstride = (long)m * 2 * n;
     a.tail = TAIL_STACKED; a.r2a = s.r;
     a.TA = b.Ugu; a.lda2 = 2 * s.r;
-    a.TB0 = A_g; a.TB1 = A_u; a.ldtb = s.r; a.tbstride = (long)m * r;
+    if (out_in(s)) {  // A_g, A_u [E, m, r] -> [E, r, m]
+      STAGE(ST_BWD_GATE_UP, launch_transpose(s.dtype, A_g, b.At_g, s.m, s.r, s.E, hs));
+      STAGE(ST_BWD_GATE_UP, launch_transpose(s.dtype, A_u, b.At_u, s.m, s.r, s.E, hs));
+      a.TB0 = b.At_g; a.TB1 = b.At_u; a.ldtb = s.m;
+    } else {
+      a.TB0 = A_g; a.TB1 = A_u; a.ldtb = s.r;
+    }
+    a.tbstride = (long)m * r;
     a.C = b.dXp; a.ldc = s.m;
-    STAGE(ST_BWD_GATE_UP, gemm_gm_launch(a, LAYOUT_XK, EPI_STORE, 0, s.dtype, Pi, ref, hs));
+    STAGE(ST_BWD_GATE_UP, gemm_gm_launch(a, out_in(s) ? LAYOUT_KX : LAYOUT_XK, EPI_STORE, 0, s.dtype, Pi, ref,
+                                         hs));
   }
   // dA_g | dA_u = Xp^T [Uc_g | Uc_u] ;  dB_g = Tc_g^T dg, dB_u = Tc_u^T du
   {

@@ -1185,10 +1185,14 @@ hipError_t gemm_gm_launch(const GemmArgs& a, int b_layout, int epi, int out_f32,
     if (b_layout == LAYOUT_KX) {
       if (epi == EPI_SWIGLU) return launch_gm_ring<2, 2, 2, 2, LAYOUT_KX, EPI_SWIGLU>(a, rows_bound, stream);
       if (epi == EPI_STORE) return launch_gm_ring<2, 2, 2, 2, LAYOUT_KX, EPI_STORE>(a, rows_bound, stream);
+      if (epi == EPI_SWIGLU_BWD)  // output-major weights
+        return launch_gm_ring<2, 2, 2, 2, LAYOUT_KX, EPI_SWIGLU_BWD>(a, rows_bound, stream);
     } else {
       if (epi == EPI_STORE) return launch_gm_ring<2, 2, 2, 2, LAYOUT_XK, EPI_STORE>(a, rows_bound, stream);
       if (epi == EPI_SWIGLU_BWD)
         return launch_gm_ring<2, 2, 2, 2, LAYOUT_XK, EPI_SWIGLU_BWD>(a, rows_bound, stream);
+      if (epi == EPI_SWIGLU)  // output-major weights
+        return launch_gm_ring<2, 2, 2, 2, LAYOUT_XK, EPI_SWIGLU>(a, rows_bound, stream);
     }
     return hipErrorInvalidValue;
   }

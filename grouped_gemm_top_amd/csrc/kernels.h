@@ -33,8 +33,9 @@ hipError_t launch_combine_bwd(int dtype, const void* dY, const void* o, const in
 // dz[t, j] from ds, w, p_sel (softmax or sigmoid, renormalised or not).
 hipError_t launch_router_bwd(const float* ds, const float* w, const float* psel, int s, int k,
                              int score, int renorm, float* dz, hipStream_t st);
-// WT[e, a] = W[a, e]
-hipError_t launch_transpose(int dtype, const void* W, void* WT, int rows, int cols, hipStream_t st);
+// WT[b][c, a] = W[b][a, c] for `batch` consecutive rows x cols matrices
+hipError_t launch_transpose(int dtype, const void* W, void* WT, int rows, int cols, int batch,
+                            hipStream_t st);
 // dX[t] = sum_j dXp[inv[t k + j]] (+ sum_j dz[t,j] WrT[idx[t,j]] when dz != nullptr)
 hipError_t launch_unpermute(int dtype, const void* dXp, const int* inv, const float* dz,
                             const int* idx, const void* WrT, void* dX, int s, int k, int m,

@@ -374,6 +374,8 @@ __global__ void router_bwd_kernel(const float* __restrict__ ds, const float* __r
 template <typename T>
 __global__ void transpose_kernel(const T* __restrict__ W, T* __restrict__ WT, int rows, int cols) {
   __shared__ T tile[32][33];
+  W += (long)blockIdx.z * rows * cols;  // one matrix of a batch per blockIdx.z
+  WT += (long)blockIdx.z * rows * cols;
   const int bx = blockIdx.x * 32, by = blockIdx.y * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
   for (int yy = ty; yy < 32; yy += 8) {
@@ -504,8 +506,10 @@ hipError_t launch_router_bwd(const float* ds, const float* w, const float* psel,
   return hipGetLastError();
 }
 
-hipError_t launch_transpose(int dtype, const void* W, void* WT, int rows, int cols, hipStream_t st) {
-  dim3 grid((cols + 31) / 32, (rows + 31) / 32);
+hipError_t launch_transpose(int dtype, const void* W, void* WT, int rows, int cols, int batch,
+                            hipStream_t st) {
+  if (rows <= 0 || cols <= 0 || batch <= 0) return hipSuccess;
+  dim3 grid((cols + 31) / 32, (rows + 31) / 32, batch);
   if (dtype)
     hipLaunchKernelGGL(transpose_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)W, (bf16_t*)WT,
                        rows, cols);

@@ -27,6 +27,8 @@
  *    Routing weights, logits and LoRA-factor gradients are fp32; indices are int32.
  *  - Weights use the x.W orientation: W_r [m, E]; W_gu [E, m, 2n] (columns [0,n) gate, [n,2n) up);
  *    W_d [E, n, m]; A_g, A_u [E, m, r]; B_g, B_u [E, r, n]; A_d [E, n, r]; B_d [E, r, m].
+ *    With MOE_FLAG_WEIGHTS_OUT_IN the two base expert tensors are stored output-major instead:
+ *    W_gu [E, 2n, m] (rows [0,n) gate, [n,2n) up) and W_d [E, m, n].
  *  - Pair id p = t*k + j (token t, slot j of its selection order); P = s*k pairs.
  *
  * Supported shapes: s >= 0; m and n multiples of 64; 1 <= k <= E <= 1024; 1 <= r <= 64, and for
@@ -58,6 +60,13 @@ typedef int32_t moe_status;
 
 /* flags */
 #define MOE_FLAG_REFERENCE_GEMM 1 /* run every GEMM with the plain one-thread-per-output kernels */
+/* rank-stabilised LoRA scale c = alpha / sqrt(r) instead of alpha / r (bluecore.net/archives/629,
+ * LoRA section, rsLoRA item) */
+#define MOE_FLAG_RSLORA 2
+/* base expert weights output-major, W_gu [E, 2n, m] and W_d [E, m, n]: the one-tensor-per-projection
+ * layout that the unsloth.ai "Faster MoE" page shows for Transformers v5 (section "What is
+ * torch._grouped_mm?"); the LoRA factors keep their shapes */
+#define MOE_FLAG_WEIGHTS_OUT_IN 4
 
 typedef struct moe_shape {
   int32_t s;           /* tokens */
@@ -66,7 +75,7 @@ typedef struct moe_shape {
   int32_t E;           /* experts */
   int32_t k;           /* experts per token */
   int32_t r;           /* LoRA rank */
-  float alpha;         /* LoRA alpha; the LoRA scale is c = alpha / r */
+  float alpha;         /* LoRA alpha; the LoRA scale is c = alpha / r (alpha / sqrt(r) with RSLORA) */
   int32_t dtype;       /* MOE_DTYPE_* */
   int32_t score;       /* MOE_SCORE_* */
   int32_t renormalize; /* 1: s_{t,j} = p_j / sum of the token's k selected p; 0: s_{t,j} = p_j */

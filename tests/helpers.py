@@ -25,6 +25,8 @@ VARIANTS = {
     "gpt_oss_r64": config("gpt_oss_20b", s=384, m=192, n=256, E=8, k=4, r=64, alpha=128.0),
     # an expert with more than one 256-row tile, and ragged last tiles
     "big_expert": config("qwen3_30b_a3b_zipf", s=1024, m=128, n=192, E=16, k=2, zipf=2.0),
+    # an expert longer than several 1024-row chunks (chunked LoRA-gradient reductions)
+    "chunked_expert": config("qwen3_30b_a3b_zipf", s=4096, m=128, n=64, E=8, k=2, zipf=2.0),
 }
 
 

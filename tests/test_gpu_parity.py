@@ -25,10 +25,17 @@ def _say(msg):
     print(msg, flush=True)
 
 
+FLAG_RSLORA = 2
+FLAG_WEIGHTS_OUT_IN = 4
+
+
 def run_gpu(cfg, device, flags=0, router_grad=True):
     from grouped_gemm_top_amd import layer
     inp = make_inputs(cfg, seed=0, device="cpu", with_grad_output=cfg.backward)
     d = {k: (v.to(device) if v is not None else None) for k, v in inp.items()}
+    if flags & FLAG_WEIGHTS_OUT_IN:  # the library gets W_gu [E, 2n, m] and W_d [E, m, n]
+        d["W_gu"] = d["W_gu"].transpose(1, 2).contiguous()
+        d["W_d"] = d["W_d"].transpose(1, 2).contiguous()
     shape = layer.shape_of(cfg, router_grad=router_grad, flags=flags)
     rt = layer.route(shape, d["X"], d["W_r"], d["router_bias"])
     Y, saved = layer.forward(shape, d["X"], rt, d, training=cfg.backward)
@@ -63,19 +70,36 @@ def check_routing(cfg, inp, rt):
 @pytest.mark.parametrize("flags", [0, 1], ids=["mfma", "reference"])
 @pytest.mark.parametrize("name", list(VARIANTS))
 def test_layer_parity(name, flags, cuda):
-    cfg = VARIANTS[name]
+    _parity(VARIANTS[name], name, flags, cuda)
+
+
+# rsLoRA scale; output-major base weights (forward GEMMs on the reduction-contiguous path,
+# backward on the transposing one, LoRA factors transposed for the tails); both; and output-major
+# weights on the reference kernels
+FLAG_CASES = {"rslora": FLAG_RSLORA, "out_in": FLAG_WEIGHTS_OUT_IN,
+              "out_in_rslora": FLAG_WEIGHTS_OUT_IN | FLAG_RSLORA, "out_in_reference": FLAG_WEIGHTS_OUT_IN | 1}
+
+
+@pytest.mark.parametrize("mode", list(FLAG_CASES))
+@pytest.mark.parametrize("name", ["qwen3_small", "gpt_oss_r64", "tiny_fp32_bwd"])
+def test_layer_parity_flags(name, mode, cuda):
+    _parity(VARIANTS[name], name, FLAG_CASES[mode], cuda)
+
+
+def _parity(cfg, name, flags, cuda):
     _say(f"[parity] {name} flags={flags} s={cfg.s} m={cfg.m} n={cfg.n} E={cfg.E} k={cfg.k} "
          f"r={cfg.r} {cfg.dtype} {cfg.score} backward={cfg.backward}")
     inp, out = run_gpu(cfg, cuda, flags=flags)
     ort = check_routing(cfg, inp, out["rt"])
     W = host_weights(inp)
     X = np64(inp["X"])
-    Y_ref, saved = oracle.forward(X, W, ort, cfg.alpha, cfg.r)
+    rs = bool(flags & FLAG_RSLORA)
+    Y_ref, saved = oracle.forward(X, W, ort, cfg.alpha, cfg.r, rslora=rs)
     tol = TOL[cfg.dtype]
     errs = {"Y": rel_err(np64(out["Y"]), Y_ref)}
     if cfg.backward:
         g = oracle.backward(np64(inp["dY"]), X, np64(inp["W_r"]), W, ort, cfg.alpha, cfg.r,
-                            cfg.score, cfg.renormalize, True, saved)
+                            cfg.score, cfg.renormalize, True, saved, rslora=rs)
         errs["dX"] = rel_err(np64(out["dX"]), g["dX"])
         for key in GRAD_KEYS:
             errs[key] = rel_err(np64(out[key]), g[key])
