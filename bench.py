@@ -102,6 +102,62 @@ def cpu_baseline(cfg, inp, tokens, min_seconds=10.0, max_passes=8):
                       f"(fp64 numpy), {passes} pass(es) in {dt:.1f} s"}
 
 
+def crossover(args, g, layer, config, make_inputs, torch, dev):
+    """Forward of one layer evaluated two ways at growing token counts s (inputs resident, HIP
+    events around each variant, median of 5 after 2 warm-up runs):
+      split:  the library's Split-LoRA forward (X W + c (X A) B, no m x n product formed);
+      merged: moe_peft_merge (W' = W + c A B for every expert, the materialised form) followed by the
+              forward on W' with no LoRA work; reported with and without the merge.
+    The merge is per training step, since A and B change every step."""
+    import statistics
+    s_list = [512, 1024, 2048, 4096, 8192, 16384, 32768]
+    base = config(args.workload)
+    big = config(args.workload, s=max(s_list))
+    inp = make_inputs(big, seed=0, device=dev, with_grad_output=False)
+    shape0 = layer.shape_of(big)
+    Wm_gu, Wm_d = torch.empty_like(inp["W_gu"]), torch.empty_like(inp["W_d"])
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps=5, warm=2):
+        for _ in range(warm):
+            fn()
+        out = []
+        for _ in range(reps):
+            ev0.record()
+            fn()
+            ev1.record()
+            torch.cuda.synchronize()
+            out.append(ev0.elapsed_time(ev1))
+        return statistics.median(out)
+
+    def merge():
+        g.moe_peft_merge(shape0, inp["W_gu"], inp["W_d"], inp["A_g"], inp["B_g"], inp["A_u"],
+                         inp["B_u"], inp["A_d"], inp["B_d"], Wm_gu, Wm_d)
+
+    t_merge = timed(merge)
+    dm = dict(inp, W_gu=Wm_gu, W_d=Wm_d, A_g=None, B_g=None, A_u=None, B_u=None, A_d=None, B_d=None)
+    b = 2 if base.dtype == "bf16" else 4
+    E, m, n, k, r = base.E, base.m, base.n, base.k, base.r
+    for s in s_list:
+        cfg = config(args.workload, s=s)
+        X = inp["X"][:s].contiguous()
+        shape = layer.shape_of(cfg)
+        shape_m = layer.shape_of(cfg, flags=g.MOE_FLAG_MERGED)
+        rt = layer.route(shape, X, inp["W_r"], inp["router_bias"])
+        Y = torch.empty_like(X)
+        ws = torch.empty(max(1, g.moe_fwd_ws_bytes(shape, 0)), dtype=torch.uint8, device=dev)
+        wsm = torch.empty(max(1, g.moe_fwd_ws_bytes(shape_m, 0)), dtype=torch.uint8, device=dev)
+        t_split = timed(lambda: layer.forward(shape, X, rt, inp, training=False, Y=Y, ws=ws))
+        t_mfwd = timed(lambda: layer.forward(shape_m, X, rt, dm, training=False, Y=Y, ws=wsm))
+        print(json.dumps({
+            "workload": base.name, "s": s, "split_fwd_ms": round(t_split, 4),
+            "merged_fwd_ms": round(t_mfwd, 4), "merge_ms": round(t_merge, 4),
+            "merged_total_ms": round(t_merge + t_mfwd, 4),
+            "split_lowrank_bytes": 3 * k * s * r * b, "merged_delta_bytes": 3 * E * m * n * b,
+        }), flush=True)
+        del ws, wsm, Y, rt
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,6 +168,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--reference-gemm", action="store_true",
                     help="run every GEMM with the plain SIMT kernels (diagnostics)")
+    ap.add_argument("--crossover", action="store_true",
+                    help="only time the forward with Split LoRA against the materialised PEFT form "
+                         "(merge W + cAB, then plain expert GEMMs) over a sweep of token counts, "
+                         "print one JSON line per token count and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (scales "
                          "the HBM byte counters of a profiler against a known size) and exit")
@@ -141,6 +201,9 @@ def main():
 
     g.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
+    if args.crossover:
+        crossover(args, g, layer, config, make_inputs, torch, dev)
+        return
     cfg = config(args.workload)
     log(f"[bench] workload {cfg.name}: s={cfg.s} m={cfg.m} n={cfg.n} E={cfg.E} k={cfg.k} r={cfg.r} "
         f"{cfg.dtype} {cfg.score}")

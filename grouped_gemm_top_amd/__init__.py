@@ -17,7 +17,8 @@ __all__ = [
     "moe_check_shape", "moe_route_state_bytes", "moe_fwd_saved_bytes", "moe_fwd_ws_bytes",
     "moe_bwd_ws_bytes", "moe_route", "moe_lora_forward", "moe_lora_backward",
     "MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP",
-    "MOE_FLAG_REFERENCE_GEMM", "moe_timing_enable", "moe_timing_read",
+    "MOE_FLAG_REFERENCE_GEMM", "MOE_FLAG_RSLORA", "MOE_FLAG_WEIGHTS_OUT_IN", "MOE_FLAG_MERGED",
+    "moe_peft_merge", "moe_timing_enable", "moe_timing_read",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoelora.so")
@@ -26,6 +27,9 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_DTYPE = {"f32": 0, "bf16": 1}
 MOE_SCORE = {"softmax": 0, "sigmoid": 1}
 MOE_FLAG_REFERENCE_GEMM = 1
+MOE_FLAG_RSLORA = 2
+MOE_FLAG_WEIGHTS_OUT_IN = 4
+MOE_FLAG_MERGED = 8
 
 
 class MoeShape(ctypes.Structure):
@@ -59,6 +63,7 @@ _SIGNATURES = {
     "moe_route": (_I32, [_SHAPE] + [_P] * 10 + [_SZ, _P]),
     "moe_lora_forward": (_I32, [_SHAPE] + [_P] * 17 + [_SZ, _P, _SZ, _P]),
     "moe_lora_backward": (_I32, [_SHAPE] + [_P] * 18 + [_SZ] + [_P] * 8 + [_SZ, _P]),
+    "moe_peft_merge": (_I32, [_SHAPE] + [_P] * 11),
     "moe_timing_enable": (_I32, [_I32]),
     "moe_timing_stage_count": (_I32, []),
     "moe_timing_stage_name": (ctypes.c_char_p, [_I32]),
@@ -160,6 +165,14 @@ def moe_lora_forward(shape, X, topk_idx, topk_w, expert_off, perm, inv_perm, rou
         _ptr(B_u), _ptr(A_d), _ptr(B_d), _ptr(Y), _ptr(saved), _nbytes(saved), _ptr(ws),
         _nbytes(ws), _stream(stream))
     _check(st, "moe_lora_forward")
+
+
+def moe_peft_merge(shape, W_gu, W_d, A_g, B_g, A_u, B_u, A_d, B_d, W_gu_merged, W_d_merged,
+                   stream=None):
+    st = lib().moe_peft_merge(
+        ctypes.byref(shape), _ptr(W_gu), _ptr(W_d), _ptr(A_g), _ptr(B_g), _ptr(A_u), _ptr(B_u),
+        _ptr(A_d), _ptr(B_d), _ptr(W_gu_merged), _ptr(W_d_merged), _stream(stream))
+    _check(st, "moe_peft_merge")
 
 
 def moe_lora_backward(shape, dY, X, W_r, topk_idx, topk_w, expert_off, perm, inv_perm, route_state,

@@ -69,6 +69,7 @@ inline float lora_scale(const moe_shape& s) {
   return (s.flags & MOE_FLAG_RSLORA) ? s.alpha / std::sqrt((float)s.r) : s.alpha / (float)s.r;
 }
 inline bool out_in(const moe_shape& s) { return (s.flags & MOE_FLAG_WEIGHTS_OUT_IN) != 0; }
+inline bool merged(const moe_shape& s) { return (s.flags & MOE_FLAG_MERGED) != 0; }
 inline long pairs(const moe_shape& s) { return (long)s.s * s.k; }
 inline int nblocks(const moe_shape& s) { return (s.s + kRouteBlockTokens - 1) / kRouteBlockTokens; }
 
@@ -110,7 +111,7 @@ struct FwdFactors {
 };
 size_t fwd_factor_layout(const moe_shape& s, void* base, FwdFactors* ff) {
   Carve c(base);
-  const size_t es = esize(s), fac = out_in(s) ? 1 : 0;
+  const size_t es = esize(s), fac = (out_in(s) && !merged(s)) ? 1 : 0;
   FwdFactors f;
   f.Bt_g = c.bytes(fac * s.E * s.r * s.n * es);
   f.Bt_u = c.bytes(fac * s.E * s.r * s.n * es);
@@ -149,7 +150,7 @@ moe_status check_shape(const moe_shape* sp) {
   if (s.score != MOE_SCORE_SOFTMAX && s.score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
   if ((s.renormalize != 0 && s.renormalize != 1) || (s.router_grad != 0 && s.router_grad != 1))
     return MOE_ERR_INVALID_ARG;
-  if (s.flags & ~(MOE_FLAG_REFERENCE_GEMM | MOE_FLAG_RSLORA | MOE_FLAG_WEIGHTS_OUT_IN))
+  if (s.flags & ~(MOE_FLAG_REFERENCE_GEMM | MOE_FLAG_RSLORA | MOE_FLAG_WEIGHTS_OUT_IN | MOE_FLAG_MERGED))
     return MOE_ERR_INVALID_ARG;
   if (!std::isfinite(s.alpha)) return MOE_ERR_INVALID_ARG;
   if (s.m % 64 || s.n % 64) return MOE_ERR_UNSUPPORTED;
@@ -353,9 +354,10 @@ moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t
   const size_t E = s.E, m = s.m, n = s.n, r = s.r;
   if (!ptr_ok(X, (size_t)s.s * m) || !ptr_ok(topk_idx, P) || !ptr_ok(topk_w, P) ||
       !ptr_ok(expert_off, E + 1) || !ptr_ok(perm, P) || !ptr_ok(inv_perm, P) ||
-      !ptr_ok(W_gu, E * m * 2 * n) || !ptr_ok(W_d, E * n * m) || !ptr_ok(A_g, E * m * r) ||
-      !ptr_ok(B_g, E * r * n) || !ptr_ok(A_u, E * m * r) || !ptr_ok(B_u, E * r * n) ||
-      !ptr_ok(A_d, E * n * r) || !ptr_ok(B_d, E * r * m) || !ptr_ok(Y, (size_t)s.s * m))
+      !ptr_ok(W_gu, E * m * 2 * n) || !ptr_ok(W_d, E * n * m) || !ptr_ok(Y, (size_t)s.s * m))
+    return MOE_ERR_INVALID_ARG;
+  if (!merged(s) && (!ptr_ok(A_g, E * m * r) || !ptr_ok(B_g, E * r * n) || !ptr_ok(A_u, E * m * r) ||
+                     !ptr_ok(B_u, E * r * n) || !ptr_ok(A_d, E * n * r) || !ptr_ok(B_d, E * r * m)))
     return MOE_ERR_INVALID_ARG;
   if (!route_state || ((uintptr_t)route_state & 255u)) return MOE_ERR_INVALID_ARG;
   const size_t need_saved = fwd_layout(s, nullptr, nullptr);
@@ -381,7 +383,7 @@ moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t
   const int ref = (s.flags & MOE_FLAG_REFERENCE_GEMM) ? 1 : 0;
   const float c = lora_scale(s);
   const int Pi = (int)P;
-  if (out_in(s)) {  // [E, r, n] -> [E, n, r] and [E, r, m] -> [E, m, r]
+  if (out_in(s) && !merged(s)) {  // [E, r, n] -> [E, n, r] and [E, r, m] -> [E, m, r]
     STAGE(ST_FWD_GATE_UP, launch_transpose(s.dtype, B_g, ff.Bt_g, s.r, s.n, s.E, hs));
     STAGE(ST_FWD_GATE_UP, launch_transpose(s.dtype, B_u, ff.Bt_u, s.r, s.n, s.E, hs));
     STAGE(ST_FWD_DOWN, launch_transpose(s.dtype, B_d, ff.Bt_d, s.r, s.m, s.E, hs));
@@ -397,7 +399,7 @@ moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t
   // The grouped row i of every expert GEMM is pair perm[i]; its activation row is X[perm[i] / k],
   // gathered by the GEMM kernels (no permuted copy of X is written).
   // Tc_gu = c * Xp [A_g | A_u]
-  {
+  if (!merged(s)) {
     GemmArgs a = base;
     a.N = s.r; a.K = s.m;
     a.A = X; a.lda = s.m; a.arow = perm; a.arow_div = s.k;
@@ -416,7 +418,7 @@ moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t
     } else {          // W_gu [E, m, 2n]: the up half starts n columns in
       a.Bu = (const char*)W_gu + n * esize(s); a.ldb = 2 * s.n;
     }
-    a.tail = TAIL_BLOCKDIAG; a.r2a = s.r;
+    a.tail = merged(s) ? TAIL_NONE : TAIL_BLOCKDIAG; a.r2a = s.r;
     a.TA = f.Tgu; a.lda2 = 2 * s.r;
     if (out_in(s)) {
       a.TB0 = ff.Bt_g; a.TB1 = ff.Bt_u; a.ldtb = s.r;
@@ -430,7 +432,7 @@ moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t
                                          ref, hs));
   }
   // Tc_d = c * h A_d
-  {
+  if (!merged(s)) {
     GemmArgs a = base;
     a.N = s.r; a.K = s.n;
     a.A = f.h; a.lda = s.n;
@@ -444,7 +446,7 @@ moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t
     a.N = s.m; a.K = s.n;
     a.A = f.h; a.lda = s.n;
     a.B = W_d; a.ldb = out_in(s) ? s.n : s.m; a.bstride = (long)n * m;
-    a.tail = TAIL_SINGLE; a.r2a = s.r;
+    a.tail = merged(s) ? TAIL_NONE : TAIL_SINGLE; a.r2a = s.r;
     a.TA = f.Td; a.lda2 = s.r;
     a.TB0 = out_in(s) ? ff.Bt_d : B_d; a.ldtb = out_in(s) ? s.r : s.m; a.tbstride = (long)r * m;
     a.C = f.o; a.ldc = s.m;
@@ -453,6 +455,32 @@ moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t
   }
   // combine
   STAGE(ST_FWD_COMBINE, launch_combine(s.dtype, f.o, inv_perm, topk_w, Y, s.s, s.k, s.m, hs));
+  return MOE_OK;
+}
+
+moe_status moe_peft_merge(const moe_shape* shape, const void* W_gu, const void* W_d, const void* A_g,
+                          const void* B_g, const void* A_u, const void* B_u, const void* A_d,
+                          const void* B_d, void* W_gu_merged, void* W_d_merged, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape& s = *shape;
+  const size_t E = s.E, m = s.m, n = s.n, r = s.r;
+  if (!ptr_ok(W_gu, E * m * 2 * n) || !ptr_ok(W_d, E * n * m) || !ptr_ok(A_g, E * m * r) ||
+      !ptr_ok(B_g, E * r * n) || !ptr_ok(A_u, E * m * r) || !ptr_ok(B_u, E * r * n) ||
+      !ptr_ok(A_d, E * n * r) || !ptr_ok(B_d, E * r * m) || !ptr_ok(W_gu_merged, E * m * 2 * n) ||
+      !ptr_ok(W_d_merged, E * n * m) || W_gu_merged == W_gu || W_d_merged == W_d)
+    return MOE_ERR_INVALID_ARG;
+  hipStream_t hs = (hipStream_t)stream;
+  const float c = lora_scale(s);
+  const bool kx = !out_in(s);
+  const long ld_gu = kx ? 2L * n : (long)m, ld_d = kx ? (long)m : (long)n;
+  // gate columns [0, n) and up columns [n, 2n) of W_gu (K = m), then W_d (K = n, N = m)
+  HIP_TRY(launch_merge(s.dtype, kx, W_gu, A_g, B_g, W_gu_merged, s.E, s.m, s.n, s.r, ld_gu, 0,
+                       (long)m * 2 * n, c, hs));
+  HIP_TRY(launch_merge(s.dtype, kx, W_gu, A_u, B_u, W_gu_merged, s.E, s.m, s.n, s.r, ld_gu, (long)n,
+                       (long)m * 2 * n, c, hs));
+  HIP_TRY(launch_merge(s.dtype, kx, W_d, A_d, B_d, W_d_merged, s.E, s.n, s.m, s.r, ld_d, 0,
+                       (long)n * m, c, hs));
   return MOE_OK;
 }
 
@@ -469,6 +497,7 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
   if (st != MOE_OK) return st;
   const moe_shape& s = *shape;
   if (s.router_grad && s.score == MOE_SCORE_SOFTMAX && !s.renormalize) return MOE_ERR_UNSUPPORTED;
+  if (merged(s)) return MOE_ERR_UNSUPPORTED;
   const long P = pairs(s);
   const size_t E = s.E, m = s.m, n = s.n, r = s.r;
   if (!ptr_ok(dY, (size_t)s.s * m) || !ptr_ok(X, (size_t)s.s * m) || !ptr_ok(W_r, m * E) ||

@@ -1119,6 +1119,11 @@ hipError_t dispatch_gm_mfma(const GemmArgs& a, int rows_bound, hipStream_t strea
       else return launch_gm_ring<1, 1, 1, 1, BL, EPI>(a, rows_bound, stream);
     }
   }
+  // grouped products without a LoRA tail and with wide outputs (merged-weight expert projections)
+  if constexpr (std::is_same<OutT, bf16_t>::value && EPI != EPI_DUAL) {
+    if (a.goff && a.N > 32 && a.K % 64 == 0 && a.tail == TAIL_NONE && !a.kchunk)
+      return launch_gm_ring<2, 2, 2, 2, BL, EPI>(a, rows_bound, stream);
+  }
   if constexpr (DUAL) {
     if (a.N <= 32) return launch_gm_mfma<CfgSkinnyDual, BL, EPI, OutT>(a, rows_bound, stream);
     return launch_gm_mfma<CfgMid, BL, EPI, OutT>(a, rows_bound, stream);
@@ -1212,6 +1217,7 @@ hipError_t gemm_gm_launch(const GemmArgs& a, int b_layout, int epi, int out_f32,
   switch (epi) {
     case EPI_STORE: return dispatch_gm_mfma<LAYOUT_XK, EPI_STORE, bf16_t>(a, rows_bound, stream);
     case EPI_SWIGLU_BWD: return dispatch_gm_mfma<LAYOUT_XK, EPI_SWIGLU_BWD, bf16_t>(a, rows_bound, stream);
+    case EPI_SWIGLU: return dispatch_gm_mfma<LAYOUT_XK, EPI_SWIGLU, bf16_t>(a, rows_bound, stream);
     default: return hipErrorInvalidValue;
   }
 }

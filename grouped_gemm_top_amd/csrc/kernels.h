@@ -43,4 +43,9 @@ hipError_t launch_unpermute(int dtype, const void* dXp, const int* inv, const fl
 // zero-fill n 32-bit words
 hipError_t launch_zero(void* p, size_t words, hipStream_t st);
 
+// Wo = W + c A B over one projection block of every expert (see merge_kernel): kx selects the
+// x.W orientation (off = i * ld + j + col0) over the output-major one ((j + col0) * ld + i).
+hipError_t launch_merge(int dtype, bool kx, const void* W, const void* A, const void* B, void* Wo,
+                        int E, int K, int N, int r, long ld, long col0, long wstride, float c,
+                        hipStream_t st);
 }  // namespace moe

@@ -432,6 +432,59 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const T* __restrict__ dX
     Vec8<T>::store(dX + t * m + c * V, acc);
   }
 }
+// W' = W + c A B over one projection block of every expert: element (i, j) of the block
+// (i < K over the reduction axis, j < N over the outputs) is Wo[e * wstride + off(i, j)] with
+// off = i * ld + j + col0 (x.W orientation, kx) or (j + col0) * ld + i (output-major); A is
+// [E, K, r], B is [E, r, N]. Threads run along the contiguous axis of W; in the x.W orientation
+// each thread owns V consecutive outputs (one 16-byte chunk; N is a multiple of 8).
+template <typename T>
+__global__ __launch_bounds__(256) void merge_kx_kernel(const T* __restrict__ W, const T* __restrict__ A,
+                                                       const T* __restrict__ B, T* __restrict__ Wo,
+                                                       int K, int N, int r, long ld, long col0,
+                                                       long wstride, float c) {
+  constexpr int V = Vec8<T>::N;
+  const long e = blockIdx.y;
+  const int cpr = N / V;  // chunks per row
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long)K * cpr) return;
+  const int i = (int)(idx / cpr), j = (int)(idx % cpr) * V;
+  const T* Ai = A + (e * K + i) * r;
+  const T* Bj = B + e * r * N + j;
+  float acc[V] = {};
+  for (int q0 = 0; q0 < r; q0 += V) {  // r is a multiple of V (8 for bf16, 4 for fp32)
+    float a[V];
+    Vec8<T>::load(Ai + q0, a);
+#pragma unroll
+    for (int q = 0; q < V; q++) {
+      float b[V];
+      Vec8<T>::load(Bj + (long)(q0 + q) * N, b);
+#pragma unroll
+      for (int u = 0; u < V; u++) acc[u] += a[q] * b[u];
+    }
+  }
+  const long off = e * wstride + (long)i * ld + j + col0;
+  float w[V];
+  Vec8<T>::load(W + off, w);
+#pragma unroll
+  for (int u = 0; u < V; u++) w[u] += c * acc[u];
+  Vec8<T>::store(Wo + off, w);
+}
+template <typename T>
+__global__ __launch_bounds__(256) void merge_xk_kernel(const T* __restrict__ W, const T* __restrict__ A,
+                                                       const T* __restrict__ B, T* __restrict__ Wo,
+                                                       int K, int N, int r, long ld, long col0,
+                                                       long wstride, float c) {
+  const long e = blockIdx.z;
+  const int i = blockIdx.x * 256 + threadIdx.x, j = blockIdx.y;
+  if (i >= K) return;
+  const T* Ai = A + (e * K + i) * r;
+  const T* Bj = B + e * r * N + j;
+  float acc = 0.0f;
+  for (int q = 0; q < r; q++) acc += to_f(Ai[q]) * to_f(Bj[(long)q * N]);
+  const long off = e * wstride + (long)(j + col0) * ld + i;
+  Wo[off] = from_f<T>(to_f(W[off]) + c * acc);
+}
+
 __global__ void zero_kernel(int* p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
     p[i] = 0;
@@ -536,6 +589,32 @@ hipError_t launch_zero(void* p, size_t words, hipStream_t st) {
   if (words == 0) return hipSuccess;
   const size_t blocks = std::min<size_t>((words + 255) / 256, 4096);
   hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (int*)p, words);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(int dtype, bool kx, const void* W, const void* A, const void* B, void* Wo,
+                        int E, int K, int N, int r, long ld, long col0, long wstride, float c,
+                        hipStream_t st) {
+  if (E <= 0 || K <= 0 || N <= 0) return hipSuccess;
+  if (kx) {
+    const int V = dtype ? 8 : 4;
+    if (N % 8 || r % V) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(((long)K * (N / V) + 255) / 256), (unsigned)E);
+    if (dtype)
+      hipLaunchKernelGGL(merge_kx_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)W,
+                         (const bf16_t*)A, (const bf16_t*)B, (bf16_t*)Wo, K, N, r, ld, col0, wstride, c);
+    else
+      hipLaunchKernelGGL(merge_kx_kernel<float>, grid, dim3(256), 0, st, (const float*)W,
+                         (const float*)A, (const float*)B, (float*)Wo, K, N, r, ld, col0, wstride, c);
+  } else {
+    const dim3 grid((unsigned)((K + 255) / 256), (unsigned)N, (unsigned)E);
+    if (dtype)
+      hipLaunchKernelGGL(merge_xk_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)W,
+                         (const bf16_t*)A, (const bf16_t*)B, (bf16_t*)Wo, K, N, r, ld, col0, wstride, c);
+    else
+      hipLaunchKernelGGL(merge_xk_kernel<float>, grid, dim3(256), 0, st, (const float*)W,
+                         (const float*)A, (const float*)B, (float*)Wo, K, N, r, ld, col0, wstride, c);
+  }
   return hipGetLastError();
 }
 

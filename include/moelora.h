@@ -67,6 +67,10 @@ typedef int32_t moe_status;
  * layout that the unsloth.ai "Faster MoE" page shows for Transformers v5 (section "What is
  * torch._grouped_mm?"); the LoRA factors keep their shapes */
 #define MOE_FLAG_WEIGHTS_OUT_IN 4
+/* moe_lora_forward only: W_gu and W_d hold merged weights from moe_peft_merge; the LoRA factors
+ * are not read (may be NULL) and no Split-LoRA work runs. moe_lora_backward rejects it
+ * (MOE_ERR_UNSUPPORTED). */
+#define MOE_FLAG_MERGED 8
 
 typedef struct moe_shape {
   int32_t s;           /* tokens */
@@ -154,6 +158,19 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
                              size_t saved_bytes, void* dX, float* dA_g, float* dB_g, float* dA_u,
                              float* dB_u, float* dA_d, float* dB_d, void* ws, size_t ws_bytes,
                              void* stream);
+
+/*
+ * moe_peft_merge -- the materialised form of the LoRA update that Split LoRA avoids
+ * (ailinkdeeptech.com cookbook page, section "1. Standard PEFT Materialization Overhead"):
+ *     W_gu' = W_gu + c [A_g B_g | A_u B_u],   W_d' = W_d + c A_d B_d      (per expert)
+ * fp32 products rounded to dtype, in the base weights' orientation (x.W, or output-major with
+ * MOE_FLAG_WEIGHTS_OUT_IN). Out: W_gu_merged and W_d_merged, shaped like W_gu and W_d (distinct
+ * buffers). Feeds moe_lora_forward with MOE_FLAG_MERGED, to set the two evaluation orders side by
+ * side; no training call needs it.
+ */
+moe_status moe_peft_merge(const moe_shape* shape, const void* W_gu, const void* W_d, const void* A_g,
+                          const void* B_g, const void* A_u, const void* B_u, const void* A_d,
+                          const void* B_d, void* W_gu_merged, void* W_d_merged, void* stream);
 
 /*
  * Stage timing (diagnostics, off by default). While enabled, every call records a hipEvent pair on

@@ -139,3 +139,44 @@ def test_determinism(cuda):
     _, b = run_gpu(cfg, cuda)
     for key in ("Y", "dX") + GRAD_KEYS:
         assert torch.equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("out_in", [False, True], ids=["x_w", "out_in"])
+@pytest.mark.parametrize("name", ["qwen3_small", "tiny_fp32", "gpt_oss_r64"])
+def test_merged_weights_forward(name, out_in, cuda):
+    """The materialised PEFT form: moe_peft_merge against W + c A B on the host, and the forward on
+    merged weights (no Split-LoRA work) against the oracle's Split-LoRA forward."""
+    from grouped_gemm_top_amd import layer, moe_peft_merge
+    cfg = VARIANTS[name]
+    _say(f"[merged] {name} out_in={out_in}")
+    flags = FLAG_WEIGHTS_OUT_IN if out_in else 0
+    inp = make_inputs(cfg, seed=0, device="cpu", with_grad_output=False)
+    d = {k: (v.to(cuda) if v is not None else None) for k, v in inp.items()}
+    if out_in:
+        d["W_gu"] = d["W_gu"].transpose(1, 2).contiguous()
+        d["W_d"] = d["W_d"].transpose(1, 2).contiguous()
+    shape = layer.shape_of(cfg, flags=flags)
+    Wm_gu, Wm_d = torch.empty_like(d["W_gu"]), torch.empty_like(d["W_d"])
+    moe_peft_merge(shape, d["W_gu"], d["W_d"], d["A_g"], d["B_g"], d["A_u"], d["B_u"], d["A_d"],
+                   d["B_d"], Wm_gu, Wm_d)
+    torch.cuda.synchronize()
+    W = host_weights(inp)
+    c = cfg.alpha / cfg.r
+    n = cfg.n
+    ref_gu = W["W_gu"] + c * np.concatenate([W["A_g"] @ W["B_g"], W["A_u"] @ W["B_u"]], axis=2)
+    ref_d = W["W_d"] + c * W["A_d"] @ W["B_d"]
+    got_gu, got_d = np64(Wm_gu), np64(Wm_d)
+    if out_in:
+        got_gu, got_d = got_gu.transpose(0, 2, 1), got_d.transpose(0, 2, 1)
+    tol = TOL[cfg.dtype]
+    assert rel_err(got_gu, ref_gu) <= tol and rel_err(got_d, ref_d) <= tol
+    assert ref_gu.shape[2] == 2 * n
+    rt = layer.route(shape, d["X"], d["W_r"], d["router_bias"])
+    dm = dict(d, W_gu=Wm_gu, W_d=Wm_d, A_g=None, B_g=None, A_u=None, B_u=None, A_d=None, B_d=None)
+    Y, _ = layer.forward(layer.shape_of(cfg, flags=flags | 8), d["X"], rt, dm, training=False)
+    torch.cuda.synchronize()
+    ort = check_routing(cfg, inp, rt)
+    Y_ref, _ = oracle.forward(np64(inp["X"]), W, ort, cfg.alpha, cfg.r, keep=False)
+    err = rel_err(np64(Y), Y_ref)
+    _say(f"  merge err gu {rel_err(got_gu, ref_gu):.2e} d {rel_err(got_d, ref_d):.2e}; Y {err:.2e}")
+    assert err <= tol
