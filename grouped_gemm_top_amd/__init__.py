@@ -17,7 +17,7 @@ __all__ = [
     "moe_check_shape", "moe_route_state_bytes", "moe_fwd_saved_bytes", "moe_fwd_ws_bytes",
     "moe_bwd_ws_bytes", "moe_route", "moe_lora_forward", "moe_lora_backward",
     "MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP",
-    "MOE_FLAG_REFERENCE_GEMM", "MOE_FLAG_RSLORA", "MOE_FLAG_WEIGHTS_OUT_IN", "MOE_FLAG_MERGED",
+    "MOE_FLAG_REFERENCE_GEMM", "MOE_FLAG_RSLORA", "MOE_FLAG_WEIGHTS_OUT_IN", "MOE_FLAG_MERGED", "MOE_FLAG_RECOMPUTE",
     "moe_peft_merge", "moe_timing_enable", "moe_timing_read",
 ]
 
@@ -30,6 +30,7 @@ MOE_FLAG_REFERENCE_GEMM = 1
 MOE_FLAG_RSLORA = 2
 MOE_FLAG_WEIGHTS_OUT_IN = 4
 MOE_FLAG_MERGED = 8
+MOE_FLAG_RECOMPUTE = 16
 
 
 class MoeShape(ctypes.Structure):

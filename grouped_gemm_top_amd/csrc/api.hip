@@ -70,6 +70,7 @@ inline float lora_scale(const moe_shape& s) {
 }
 inline bool out_in(const moe_shape& s) { return (s.flags & MOE_FLAG_WEIGHTS_OUT_IN) != 0; }
 inline bool merged(const moe_shape& s) { return (s.flags & MOE_FLAG_MERGED) != 0; }
+inline bool recompute(const moe_shape& s) { return (s.flags & MOE_FLAG_RECOMPUTE) != 0; }
 inline long pairs(const moe_shape& s) { return (long)s.s * s.k; }
 inline int nblocks(const moe_shape& s) { return (s.s + kRouteBlockTokens - 1) / kRouteBlockTokens; }
 
@@ -120,6 +121,11 @@ size_t fwd_factor_layout(const moe_shape& s, void* base, FwdFactors* ff) {
   return align_up(c.off, 256);
 }
 
+// Backward workspace tail for recomputing the forward's intermediates (MOE_FLAG_RECOMPUTE).
+size_t recompute_bytes(const moe_shape& s) {
+  return recompute(s) ? fwd_layout(s, nullptr, nullptr) + fwd_factor_layout(s, nullptr, nullptr) : 0;
+}
+
 size_t bwd_layout(const moe_shape& s, void* base, BwdBufs* bb) {
   Carve c(base);
   const size_t P = (size_t)pairs(s), es = esize(s);
@@ -150,7 +156,8 @@ moe_status check_shape(const moe_shape* sp) {
   if (s.score != MOE_SCORE_SOFTMAX && s.score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
   if ((s.renormalize != 0 && s.renormalize != 1) || (s.router_grad != 0 && s.router_grad != 1))
     return MOE_ERR_INVALID_ARG;
-  if (s.flags & ~(MOE_FLAG_REFERENCE_GEMM | MOE_FLAG_RSLORA | MOE_FLAG_WEIGHTS_OUT_IN | MOE_FLAG_MERGED))
+  if (s.flags & ~(MOE_FLAG_REFERENCE_GEMM | MOE_FLAG_RSLORA | MOE_FLAG_WEIGHTS_OUT_IN | MOE_FLAG_MERGED |
+                  MOE_FLAG_RECOMPUTE))
     return MOE_ERR_INVALID_ARG;
   if (!std::isfinite(s.alpha)) return MOE_ERR_INVALID_ARG;
   if (s.m % 64 || s.n % 64) return MOE_ERR_UNSUPPORTED;
@@ -166,6 +173,12 @@ inline bool ptr_ok(const void* p, size_t count) {
   if (count == 0) return true;
   return p != nullptr && ((uintptr_t)p & 15u) == 0;
 }
+
+#define HIP_TRY_STATUS(x)           \
+  do {                              \
+    const moe_status st_ = (x);     \
+    if (st_ != MOE_OK) return st_;  \
+  } while (0)
 
 #define HIP_TRY(x)                           \
   do {                                       \
@@ -285,7 +298,7 @@ size_t moe_fwd_ws_bytes(const moe_shape* shape, int32_t with_saved) {
 
 size_t moe_bwd_ws_bytes(const moe_shape* shape) {
   if (check_shape(shape) != MOE_OK) return 0;
-  return bwd_layout(*shape, nullptr, nullptr);
+  return bwd_layout(*shape, nullptr, nullptr) + recompute_bytes(*shape);
 }
 
 moe_status moe_route(const moe_shape* shape, const void* X, const void* W_r,
@@ -341,45 +354,17 @@ moe_status moe_route(const moe_shape* shape, const void* X, const void* W_r,
   return MOE_OK;
 }
 
-moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t* topk_idx,
-                            const float* topk_w, const int32_t* expert_off, const int32_t* perm,
-                            const int32_t* inv_perm, const void* route_state, const void* W_gu,
-                            const void* W_d, const void* A_g, const void* B_g, const void* A_u,
-                            const void* B_u, const void* A_d, const void* B_d, void* Y, void* saved,
-                            size_t saved_bytes, void* ws, size_t ws_bytes, void* stream) {
-  moe_status st = check_shape(shape);
-  if (st != MOE_OK) return st;
-  const moe_shape& s = *shape;
+// The forward's expert stages, everything but the combine: the low-rank products Tc, the gate/up
+// GEMM with its SwiGLU epilogue and the down GEMM, writing gu, h, Tc_gu, Tc_d and o into f (ff:
+// transposed tail factors for output-major weights). Shared by the forward and by a backward that
+// recomputes them.
+moe_status forward_experts(const moe_shape& s, const void* X, const int32_t* expert_off,
+                           const int32_t* perm, const RouteState& rs, const void* W_gu, const void* W_d,
+                           const void* A_g, const void* B_g, const void* A_u, const void* B_u,
+                           const void* A_d, const void* B_d, const FwdBufs& f, const FwdFactors& ff,
+                           hipStream_t hs) {
   const long P = pairs(s);
-  const size_t E = s.E, m = s.m, n = s.n, r = s.r;
-  if (!ptr_ok(X, (size_t)s.s * m) || !ptr_ok(topk_idx, P) || !ptr_ok(topk_w, P) ||
-      !ptr_ok(expert_off, E + 1) || !ptr_ok(perm, P) || !ptr_ok(inv_perm, P) ||
-      !ptr_ok(W_gu, E * m * 2 * n) || !ptr_ok(W_d, E * n * m) || !ptr_ok(Y, (size_t)s.s * m))
-    return MOE_ERR_INVALID_ARG;
-  if (!merged(s) && (!ptr_ok(A_g, E * m * r) || !ptr_ok(B_g, E * r * n) || !ptr_ok(A_u, E * m * r) ||
-                     !ptr_ok(B_u, E * r * n) || !ptr_ok(A_d, E * n * r) || !ptr_ok(B_d, E * r * m)))
-    return MOE_ERR_INVALID_ARG;
-  if (!route_state || ((uintptr_t)route_state & 255u)) return MOE_ERR_INVALID_ARG;
-  const size_t need_saved = fwd_layout(s, nullptr, nullptr);
-  const size_t need_fac = fwd_factor_layout(s, nullptr, nullptr);
-  const size_t need_ws = (saved ? 0 : need_saved) + need_fac;
-  void* inter = saved;
-  if (saved) {
-    if ((uintptr_t)saved & 255u) return MOE_ERR_INVALID_ARG;
-    if (saved_bytes < need_saved) return MOE_ERR_WORKSPACE;
-  } else {
-    inter = ws;
-  }
-  if (ws_bytes < need_ws) return MOE_ERR_WORKSPACE;
-  if (need_ws && (!ws || ((uintptr_t)ws & 255u))) return MOE_ERR_INVALID_ARG;
-  if (s.s == 0) return MOE_OK;
-  hipStream_t hs = (hipStream_t)stream;
-  RouteState rs;
-  route_layout(s, const_cast<void*>(route_state), &rs);
-  FwdBufs f;
-  fwd_layout(s, inter, &f);
-  FwdFactors ff;
-  fwd_factor_layout(s, (char*)ws + (saved ? 0 : need_saved), &ff);
+  const size_t m = s.m, n = s.n, r = s.r;
   const int ref = (s.flags & MOE_FLAG_REFERENCE_GEMM) ? 1 : 0;
   const float c = lora_scale(s);
   const int Pi = (int)P;
@@ -453,6 +438,50 @@ moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t
     STAGE(ST_FWD_DOWN, gemm_gm_launch(a, out_in(s) ? LAYOUT_XK : LAYOUT_KX, EPI_STORE, 0, s.dtype, Pi, ref,
                                       hs));
   }
+  return MOE_OK;
+}
+
+moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t* topk_idx,
+                            const float* topk_w, const int32_t* expert_off, const int32_t* perm,
+                            const int32_t* inv_perm, const void* route_state, const void* W_gu,
+                            const void* W_d, const void* A_g, const void* B_g, const void* A_u,
+                            const void* B_u, const void* A_d, const void* B_d, void* Y, void* saved,
+                            size_t saved_bytes, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape& s = *shape;
+  const long P = pairs(s);
+  const size_t E = s.E, m = s.m, n = s.n, r = s.r;
+  if (!ptr_ok(X, (size_t)s.s * m) || !ptr_ok(topk_idx, P) || !ptr_ok(topk_w, P) ||
+      !ptr_ok(expert_off, E + 1) || !ptr_ok(perm, P) || !ptr_ok(inv_perm, P) ||
+      !ptr_ok(W_gu, E * m * 2 * n) || !ptr_ok(W_d, E * n * m) || !ptr_ok(Y, (size_t)s.s * m))
+    return MOE_ERR_INVALID_ARG;
+  if (!merged(s) && (!ptr_ok(A_g, E * m * r) || !ptr_ok(B_g, E * r * n) || !ptr_ok(A_u, E * m * r) ||
+                     !ptr_ok(B_u, E * r * n) || !ptr_ok(A_d, E * n * r) || !ptr_ok(B_d, E * r * m)))
+    return MOE_ERR_INVALID_ARG;
+  if (!route_state || ((uintptr_t)route_state & 255u)) return MOE_ERR_INVALID_ARG;
+  const size_t need_saved = fwd_layout(s, nullptr, nullptr);
+  const size_t need_fac = fwd_factor_layout(s, nullptr, nullptr);
+  const size_t need_ws = (saved ? 0 : need_saved) + need_fac;
+  void* inter = saved;
+  if (saved) {
+    if ((uintptr_t)saved & 255u) return MOE_ERR_INVALID_ARG;
+    if (saved_bytes < need_saved) return MOE_ERR_WORKSPACE;
+  } else {
+    inter = ws;
+  }
+  if (ws_bytes < need_ws) return MOE_ERR_WORKSPACE;
+  if (need_ws && (!ws || ((uintptr_t)ws & 255u))) return MOE_ERR_INVALID_ARG;
+  if (s.s == 0) return MOE_OK;
+  hipStream_t hs = (hipStream_t)stream;
+  RouteState rs;
+  route_layout(s, const_cast<void*>(route_state), &rs);
+  FwdBufs f;
+  fwd_layout(s, inter, &f);
+  FwdFactors ff;
+  fwd_factor_layout(s, (char*)ws + (saved ? 0 : need_saved), &ff);
+  HIP_TRY_STATUS(forward_experts(s, X, expert_off, perm, rs, W_gu, W_d, A_g, B_g, A_u, B_u, A_d, B_d, f,
+                                 ff, hs));
   // combine
   STAGE(ST_FWD_COMBINE, launch_combine(s.dtype, f.o, inv_perm, topk_w, Y, s.s, s.k, s.m, hs));
   return MOE_OK;
@@ -510,9 +539,12 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
       !ptr_ok(dA_d, E * n * r) || !ptr_ok(dB_d, E * r * m))
     return MOE_ERR_INVALID_ARG;
   if (!route_state || ((uintptr_t)route_state & 255u)) return MOE_ERR_INVALID_ARG;
-  if (!saved || ((uintptr_t)saved & 255u)) return MOE_ERR_INVALID_ARG;
-  if (saved_bytes < fwd_layout(s, nullptr, nullptr)) return MOE_ERR_WORKSPACE;
-  const size_t need_ws = bwd_layout(s, nullptr, nullptr);
+  const bool redo = !saved;  // recompute the forward's intermediates
+  if (redo && !recompute(s)) return MOE_ERR_INVALID_ARG;
+  if (saved && ((uintptr_t)saved & 255u)) return MOE_ERR_INVALID_ARG;
+  if (saved && saved_bytes < fwd_layout(s, nullptr, nullptr)) return MOE_ERR_WORKSPACE;
+  const size_t bwd_bytes = bwd_layout(s, nullptr, nullptr);
+  const size_t need_ws = bwd_bytes + (redo ? recompute_bytes(s) : 0);
   if (ws_bytes < need_ws) return MOE_ERR_WORKSPACE;
   if (!ws || ((uintptr_t)ws & 255u)) return MOE_ERR_INVALID_ARG;
   hipStream_t hs = (hipStream_t)stream;
@@ -528,9 +560,18 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
   RouteState rs;
   route_layout(s, const_cast<void*>(route_state), &rs);
   FwdBufs f;
-  fwd_layout(s, const_cast<void*>(saved), &f);
   BwdBufs b;
   bwd_layout(s, ws, &b);
+  if (redo) {
+    char* rbase = (char*)ws + bwd_bytes;
+    FwdFactors ff;
+    fwd_layout(s, rbase, &f);
+    fwd_factor_layout(s, rbase + fwd_layout(s, nullptr, nullptr), &ff);
+    HIP_TRY_STATUS(forward_experts(s, X, expert_off, perm, rs, W_gu, W_d, A_g, B_g, A_u, B_u, A_d, B_d,
+                                   f, ff, hs));
+  } else {
+    fwd_layout(s, const_cast<void*>(saved), &f);
+  }
   const int ref = (s.flags & MOE_FLAG_REFERENCE_GEMM) ? 1 : 0;
   const float c = lora_scale(s);
   const int Pi = (int)P;

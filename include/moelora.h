@@ -71,6 +71,12 @@ typedef int32_t moe_status;
  * are not read (may be NULL) and no Split-LoRA work runs. moe_lora_backward rejects it
  * (MOE_ERR_UNSUPPORTED). */
 #define MOE_FLAG_MERGED 8
+/* moe_lora_backward may be called with saved == NULL: it then recomputes the forward's expert
+ * intermediates (gu, h, the low-rank products, o) into its workspace first, trading one more
+ * forward's GEMMs for the saved buffer (bluecore.net/archives/629, section 4 on Unsloth's gradient
+ * checkpointing: activations are not kept and the forward is recomputed in the backward). With
+ * this flag moe_bwd_ws_bytes includes that room; the forward may then run with saved == NULL. */
+#define MOE_FLAG_RECOMPUTE 16
 
 typedef struct moe_shape {
   int32_t s;           /* tokens */
@@ -147,7 +153,8 @@ moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t
  *      dA_g, dA_u [E, m, r], dB_g, dB_u [E, r, n], dA_d [E, n, r], dB_d [E, r, m], all fp32.
  *      Experts that received no pair get exact zeros.
  * In: the routing outputs and route_state of moe_route, the same weights as the forward, and the
- *     `saved` buffer that moe_lora_forward filled. ws >= moe_bwd_ws_bytes bytes of scratch.
+ *     `saved` buffer that moe_lora_forward filled (or NULL with MOE_FLAG_RECOMPUTE).
+ *     ws >= moe_bwd_ws_bytes bytes of scratch.
  */
 moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void* X,
                              const void* W_r, const int32_t* topk_idx, const float* topk_w,

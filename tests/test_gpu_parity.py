@@ -27,6 +27,7 @@ def _say(msg):
 
 FLAG_RSLORA = 2
 FLAG_WEIGHTS_OUT_IN = 4
+FLAG_RECOMPUTE = 16
 
 
 def run_gpu(cfg, device, flags=0, router_grad=True):
@@ -38,7 +39,9 @@ def run_gpu(cfg, device, flags=0, router_grad=True):
         d["W_d"] = d["W_d"].transpose(1, 2).contiguous()
     shape = layer.shape_of(cfg, router_grad=router_grad, flags=flags)
     rt = layer.route(shape, d["X"], d["W_r"], d["router_bias"])
-    Y, saved = layer.forward(shape, d["X"], rt, d, training=cfg.backward)
+    # with FLAG_RECOMPUTE nothing is saved: the backward recomputes the forward's intermediates
+    keep = cfg.backward and not (flags & FLAG_RECOMPUTE)
+    Y, saved = layer.forward(shape, d["X"], rt, d, training=keep)
     out = {"rt": rt, "Y": Y}
     if cfg.backward:
         dX, grads = layer.backward(shape, d["dY"], d["X"], d["W_r"], rt, d, saved)
@@ -77,7 +80,8 @@ def test_layer_parity(name, flags, cuda):
 # backward on the transposing one, LoRA factors transposed for the tails); both; and output-major
 # weights on the reference kernels
 FLAG_CASES = {"rslora": FLAG_RSLORA, "out_in": FLAG_WEIGHTS_OUT_IN,
-              "out_in_rslora": FLAG_WEIGHTS_OUT_IN | FLAG_RSLORA, "out_in_reference": FLAG_WEIGHTS_OUT_IN | 1}
+              "out_in_rslora": FLAG_WEIGHTS_OUT_IN | FLAG_RSLORA, "out_in_reference": FLAG_WEIGHTS_OUT_IN | 1,
+              "recompute": FLAG_RECOMPUTE, "recompute_out_in": FLAG_RECOMPUTE | FLAG_WEIGHTS_OUT_IN}
 
 
 @pytest.mark.parametrize("mode", list(FLAG_CASES))
