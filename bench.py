@@ -168,6 +168,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--reference-gemm", action="store_true",
                     help="run every GEMM with the plain SIMT kernels (diagnostics)")
+    ap.add_argument("--recompute", action="store_true",
+                    help="keep no forward intermediates: the backward recomputes them")
     ap.add_argument("--crossover", action="store_true",
                     help="only time the forward with Split LoRA against the materialised PEFT form "
                          "(merge W + cAB, then plain expert GEMMs) over a sweep of token counts, "
@@ -209,10 +211,15 @@ def main():
         f"{cfg.dtype} {cfg.score}")
     inp = make_inputs(cfg, seed=0, device=dev, with_grad_output=True)
     flags = g.MOE_FLAG_REFERENCE_GEMM if args.reference_gemm else 0
+    if args.recompute:
+        flags |= g.MOE_FLAG_RECOMPUTE
     shape = layer.shape_of(cfg, flags=flags)
     X, Wr, bias, dY = inp["X"], inp["W_r"], inp["router_bias"], inp["dY"]
     rt = layer.alloc_route(shape, dev)
-    saved = torch.empty(g.moe_fwd_saved_bytes(shape), dtype=torch.uint8, device=dev)
+    saved = None if args.recompute else torch.empty(g.moe_fwd_saved_bytes(shape), dtype=torch.uint8,
+                                                    device=dev)
+    fws = (torch.empty(max(1, g.moe_fwd_ws_bytes(shape, 0)), dtype=torch.uint8, device=dev)
+           if args.recompute else None)
     bws = torch.empty(g.moe_bwd_ws_bytes(shape), dtype=torch.uint8, device=dev)
     Y = torch.empty_like(X)
     dX = torch.empty_like(X)
@@ -220,7 +227,7 @@ def main():
 
     def step():
         layer.route(shape, X, Wr, bias, bufs=rt)
-        layer.forward(shape, X, rt, inp, Y=Y, saved=saved)
+        layer.forward(shape, X, rt, inp, training=not args.recompute, Y=Y, saved=saved, ws=fws)
         layer.backward(shape, dY, X, Wr, rt, inp, saved, dX=dX, grads=grads, ws=bws)
 
     for _ in range(args.warmup):
@@ -292,7 +299,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "s": cfg.s, "m": cfg.m, "n": cfg.n, "E": cfg.E,
                    "k": cfg.k, "r": cfg.r, "alpha": cfg.alpha, "router": cfg.score,
-                   "step": "route+forward+backward",
+                   "step": "route+forward+backward" + (" (backward recomputes the forward)"
+                                                        if args.recompute else ""),
                    "gemm": "reference-simt" if args.reference_gemm else "mfma"},
         "tflops": round(tflops, 2),
         "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
