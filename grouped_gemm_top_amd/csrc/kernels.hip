@@ -37,8 +37,17 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ z, 
     const bool in = q < npl && e < E;
     float acc = -INFINITY;
     if (in) {
+      // partials added in split order; loaded 8 at a time so that their loads overlap
       acc = zt[e];
-      for (int p = 1; p < nsplit; p++) acc += zt[(long)p * split_stride + e];
+      for (int p0 = 1; p0 < nsplit; p0 += 8) {
+        float part[8];
+#pragma unroll
+        for (int pp = 0; pp < 8; pp++)
+          part[pp] = (p0 + pp < nsplit) ? zt[(long)(p0 + pp) * split_stride + e] : 0.0f;
+#pragma unroll
+        for (int pp = 0; pp < 8; pp++)
+          if (p0 + pp < nsplit) acc += part[pp];
+      }
       if (nsplit > 1 && zout) zout[(long)t * E + e] = acc;
     }
     v[q] = acc;
@@ -174,16 +183,31 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ blk_
   __shared__ int tsh[1025];
   const int e = threadIdx.x;
   int cnt = 0;
-  if (e < E)
-    for (int b = 0; b < nb; b++) cnt += blk_hist[(long)b * E + e];
+  if (e < E) {
+    for (int b0 = 0; b0 < nb; b0 += 8) {
+      int h[8];
+#pragma unroll
+      for (int bb = 0; bb < 8; bb++) h[bb] = (b0 + bb < nb) ? blk_hist[(long)(b0 + bb) * E + e] : 0;
+#pragma unroll
+      for (int bb = 0; bb < 8; bb++) cnt += h[bb];
+    }
+  }
   int total;
   const int start = block_exscan_1024(e < E ? cnt : 0, sh, &total);
   if (e < E) {
     off[e] = start;
     int run = start;
-    for (int b = 0; b < nb; b++) {
-      blk_base[(long)b * E + e] = run;
-      run += blk_hist[(long)b * E + e];
+    for (int b0 = 0; b0 < nb; b0 += 8) {  // per-block counts loaded 8 at a time
+      int h[8];
+#pragma unroll
+      for (int bb = 0; bb < 8; bb++) h[bb] = (b0 + bb < nb) ? blk_hist[(long)(b0 + bb) * E + e] : 0;
+#pragma unroll
+      for (int bb = 0; bb < 8; bb++) {
+        if (b0 + bb < nb) {
+          blk_base[(long)(b0 + bb) * E + e] = run;
+          run += h[bb];
+        }
+      }
     }
   }
   if (e == 0) off[E] = total;
