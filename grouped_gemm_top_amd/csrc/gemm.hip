@@ -583,21 +583,43 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
       });
     });
   };
-  // fragments of k16 step ks+1 are read while the MFMAs of step ks run
-  auto compute = [&](const bf16_t* sA) {
+  // fragments of k16 step ks+1 are read while the MFMAs of step ks run; side(IC<ks>) runs after
+  // the MFMAs of k16 step ks (the main loop hands it the next tile's LDS copy and ring refill, so
+  // that each wave's memory work is spread over its MFMAs)
+  auto compute = [&](const bf16_t* sA, auto&& side) {
     bf16x8_t fa0[TM], fb0[TN], fa1[TM], fb1[TN];
     frags(sA, 0, fa0, fb0);
     static_for<BKT / 32>([&](auto kc) {
       constexpr int ks = 2 * decltype(kc)::value;
       frags(sA, ks + 1, fa1, fb1);
       mma(fa0, fb0);
+      side(IC<ks>{});
+      __builtin_amdgcn_sched_barrier(0);
       if constexpr (ks + 2 < BKT / 16) frags(sA, ks + 2, fa0, fb0);
       mma(fa1, fb1);
+      side(IC<ks + 1>{});
+      __builtin_amdgcn_sched_barrier(0);
     });
   };
+  auto no_side = [](auto) {};
+  // one 16-byte chunk c of a ring slot (c < A_CPT: A chunk c, else B chunk c - A_CPT)
+  auto load1 = [&](auto cc, i32x4_t(&da)[A_CPT], i32x4_t(&db)[B_CPT], int t) {
+    constexpr int c = decltype(cc)::value;
+    if constexpr (c < A_CPT) da[c] = ld16(GCHK(asrc[c] + t * BKT, 16));
+    else db[c - A_CPT] = ld16(GCHK(bsrc[c - A_CPT] + t * bstep, 16));
+  };
+  auto store1 = [&](auto cc, bf16_t* st, const i32x4_t(&da)[A_CPT], const i32x4_t(&db)[B_CPT]) {
+    constexpr int c = decltype(cc)::value;
+    if constexpr (c < A_CPT)
+      *reinterpret_cast<i32x4_t*>(lds(st + (tid + c * NT) * 8, 16)) = da[c];
+    else
+      *reinterpret_cast<i32x4_t*>(lds(st + A_ELEMS + (tid + (c - A_CPT) * NT) * 8, 16)) = db[c - A_CPT];
+  };
+  constexpr int CPT = A_CPT + B_CPT, NSIDE = BKT / 16, CPJ = (CPT + NSIDE - 1) / NSIDE;
 
-  // ---- main loop. Step kt: (barrier) copy tile kt+1 from registers into LDS stage (kt+1)&1,
-  //      multiply tile kt from stage kt&1, load tile kt+4 into the ring slot tile kt left.
+  // ---- main loop. Step kt: (barrier) multiply tile kt from stage kt&1; spread over its MFMAs, copy
+  //      tile kt+1 from registers into LDS stage (kt+1)&1 and load tile kt+4 into the ring slot tile
+  //      kt left.
   const int nk = a.K / BKT;
   const int last = nk - 1;
   bf16_t* const s0 = smem;
@@ -611,16 +633,31 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
     constexpr int sl = decltype(slot_c)::value;       // kt % 4
     constexpr int nx = (sl + 1) & 3;                  // (kt + 1) % 4
     lds_barrier();
-    store((sl & 1) ? s0 : s1, ra[nx], rb[nx]);
-    if (kt < nk) compute((sl & 1) ? s1 : s0);
-    load(ra[sl], rb[sl], min(kt + 4, last));
+    bf16_t* const st = (sl & 1) ? s0 : s1;
+    const int tl = min(kt + 4, last);
+    compute((sl & 1) ? s1 : s0, [&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      static_for<CPJ>([&](auto qc) {
+        constexpr int c = j * CPJ + decltype(qc)::value;
+        if constexpr (c < CPT) {
+          store1(IC<c>{}, st, ra[nx], rb[nx]);
+          load1(IC<c>{}, ra[sl], rb[sl], tl);
+        }
+      });
+    });
   };
-  for (int kt = 0; kt < nk; kt += 4) {
+  // whole groups of four steps run unguarded (the same loads in flight on every path into the loop
+  // head), the last nk % 4 steps after the loop
+  int kt = 0;
+  for (; kt + 4 <= nk; kt += 4) {
     step(IC<0>{}, kt);
     step(IC<1>{}, kt + 1);
     step(IC<2>{}, kt + 2);
     step(IC<3>{}, kt + 3);
   }
+  if (kt < nk) step(IC<0>{}, kt);
+  if (kt + 1 < nk) step(IC<1>{}, kt + 1);
+  if (kt + 2 < nk) step(IC<2>{}, kt + 2);
 
   // ---- epilogue (after the tail): each wave stages its fp32 accumulators in its own LDS region, then writes whole
   //      16-byte row chunks (8 columns). Staged row r keeps its 4-float groups XOR-permuted by one
@@ -714,8 +751,8 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
       }
     }
     __syncthreads();
-    compute(s0);
-    if (tsteps > 1) compute(s1);
+    compute(s0, no_side);
+    if (tsteps > 1) compute(s1, no_side);
   }
 
   lds_barrier();  // every wave is done reading the K-tile stages
