@@ -473,11 +473,13 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
   constexpr int B_CPT = BN * BKT / 8 / NT;
   constexpr int CPR_A = BKT / 8;
   constexpr int CPR_B = (BL == LAYOUT_KX) ? BN / 8 : BKT / 8;
-  constexpr int LDS_BYTES = 2 * STAGE * (int)sizeof(bf16_t);
+  // LDS: two K-tile stages, reused afterwards for the fp32 staging of every wave's accumulators
+  constexpr int SMEM_ELEMS = std::max(2 * STAGE, NW * TM * TN * 32 * 32 * 2);
+  constexpr int LDS_BYTES = SMEM_ELEMS * (int)sizeof(bf16_t);
   static_assert(A_CPT * NT * 8 == A_ELEMS && B_CPT * NT * 8 == BN * BKT, "tile/thread mismatch");
   static_assert(!DUAL || TN % 2 == 0, "dual epilogue needs an even TN");
   static_assert(BL == LAYOUT_XK || CPR_B >= 4, "KX tiles need >= 4 chunks per row");
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) bf16_t smem[SMEM_ELEMS];
 #ifdef MOE_GEMM_BOUNDS_CHECK
   auto lds = [&](bf16_t* p, int bytes) -> bf16_t* {
     return smem + lchk((int)((char*)p - (char*)smem), bytes, LDS_BYTES) / 2;
@@ -665,7 +667,7 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
   constexpr int WR = TM * 32, WC = TN * 32;   // rows and columns of a wave's tile
   constexpr int CH = WC / 8;                  // 8-column chunks per staged row
   constexpr int PER = WR * CH / 64;           // chunks per lane
-  static_assert(NW * WR * WC * (int)sizeof(float) <= LDS_BYTES, "staging fits the LDS stages");
+  static_assert(NW * WR * WC * (int)sizeof(float) <= LDS_BYTES, "staging fits the LDS buffer");
   static_assert((WR * CH) % 64 == 0, "whole chunks per lane");
   auto sidx = [](int r, int c) { return r * WC + (c ^ (((r >> (WC >= 64 ? 0 : 1)) & 1) << 2)); };
   const int wrow0 = row0 + wm * WR;
@@ -1170,6 +1172,13 @@ hipError_t dispatch_gm_mfma(const GemmArgs& a, int rows_bound, hipStream_t strea
   }
 }
 
+// Wave columns of the expert-projection workgroups (2: 128 x 128 tiles, two workgroups per CU;
+// 4: 128 x 256 tiles, one workgroup of eight waves per CU).
+#ifndef MOE_RING_WN
+#define MOE_RING_WN 4
+#endif
+constexpr int kRingWN = MOE_RING_WN;
+
 // Deep-prefetch kernel (grouped launches).
 template <int WM, int WN, int TM, int TN, int BL, int EPI>
 hipError_t launch_gm_ring(const GemmArgs& a, int rows_bound, hipStream_t stream) {
@@ -1225,16 +1234,16 @@ hipError_t gemm_gm_launch(const GemmArgs& a, int b_layout, int epi, int out_f32,
   if (a.tail != TAIL_NONE) {  // the expert projections
     if (out_f32) return hipErrorInvalidValue;
     if (b_layout == LAYOUT_KX) {
-      if (epi == EPI_SWIGLU) return launch_gm_ring<2, 2, 2, 2, LAYOUT_KX, EPI_SWIGLU>(a, rows_bound, stream);
-      if (epi == EPI_STORE) return launch_gm_ring<2, 2, 2, 2, LAYOUT_KX, EPI_STORE>(a, rows_bound, stream);
+      if (epi == EPI_SWIGLU) return launch_gm_ring<2, kRingWN, 2, 2, LAYOUT_KX, EPI_SWIGLU>(a, rows_bound, stream);
+      if (epi == EPI_STORE) return launch_gm_ring<2, kRingWN, 2, 2, LAYOUT_KX, EPI_STORE>(a, rows_bound, stream);
       if (epi == EPI_SWIGLU_BWD)  // output-major weights
-        return launch_gm_ring<2, 2, 2, 2, LAYOUT_KX, EPI_SWIGLU_BWD>(a, rows_bound, stream);
+        return launch_gm_ring<2, kRingWN, 2, 2, LAYOUT_KX, EPI_SWIGLU_BWD>(a, rows_bound, stream);
     } else {
-      if (epi == EPI_STORE) return launch_gm_ring<2, 2, 2, 2, LAYOUT_XK, EPI_STORE>(a, rows_bound, stream);
+      if (epi == EPI_STORE) return launch_gm_ring<2, kRingWN, 2, 2, LAYOUT_XK, EPI_STORE>(a, rows_bound, stream);
       if (epi == EPI_SWIGLU_BWD)
-        return launch_gm_ring<2, 2, 2, 2, LAYOUT_XK, EPI_SWIGLU_BWD>(a, rows_bound, stream);
+        return launch_gm_ring<2, kRingWN, 2, 2, LAYOUT_XK, EPI_SWIGLU_BWD>(a, rows_bound, stream);
       if (epi == EPI_SWIGLU)  // output-major weights
-        return launch_gm_ring<2, 2, 2, 2, LAYOUT_XK, EPI_SWIGLU>(a, rows_bound, stream);
+        return launch_gm_ring<2, kRingWN, 2, 2, LAYOUT_XK, EPI_SWIGLU>(a, rows_bound, stream);
     }
     return hipErrorInvalidValue;
   }
