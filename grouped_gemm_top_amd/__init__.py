@@ -18,6 +18,7 @@ __all__ = [
     "moe_bwd_ws_bytes", "moe_route", "moe_lora_forward", "moe_lora_backward",
     "MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP",
     "MOE_FLAG_REFERENCE_GEMM", "MOE_FLAG_RSLORA", "MOE_FLAG_WEIGHTS_OUT_IN", "MOE_FLAG_MERGED", "MOE_FLAG_RECOMPUTE",
+    "MOE_FLAG_FUSED_GU_LORA",
     "moe_peft_merge", "moe_timing_enable", "moe_timing_read",
 ]
 
@@ -31,6 +32,7 @@ MOE_FLAG_RSLORA = 2
 MOE_FLAG_WEIGHTS_OUT_IN = 4
 MOE_FLAG_MERGED = 8
 MOE_FLAG_RECOMPUTE = 16
+MOE_FLAG_FUSED_GU_LORA = 32
 
 
 class MoeShape(ctypes.Structure):

@@ -71,6 +71,8 @@ inline float lora_scale(const moe_shape& s) {
 inline bool out_in(const moe_shape& s) { return (s.flags & MOE_FLAG_WEIGHTS_OUT_IN) != 0; }
 inline bool merged(const moe_shape& s) { return (s.flags & MOE_FLAG_MERGED) != 0; }
 inline bool recompute(const moe_shape& s) { return (s.flags & MOE_FLAG_RECOMPUTE) != 0; }
+// one LoRA pair on the fused gate/up projection: A [E, m, r] in A_g, B [E, r, 2n] in B_g
+inline bool fused_gu(const moe_shape& s) { return (s.flags & MOE_FLAG_FUSED_GU_LORA) != 0; }
 inline long pairs(const moe_shape& s) { return (long)s.s * s.k; }
 inline int nblocks(const moe_shape& s) { return (s.s + kRouteBlockTokens - 1) / kRouteBlockTokens; }
 
@@ -114,8 +116,9 @@ size_t fwd_factor_layout(const moe_shape& s, void* base, FwdFactors* ff) {
   Carve c(base);
   const size_t es = esize(s), fac = (out_in(s) && !merged(s)) ? 1 : 0;
   FwdFactors f;
-  f.Bt_g = c.bytes(fac * s.E * s.r * s.n * es);
-  f.Bt_u = c.bytes(fac * s.E * s.r * s.n * es);
+  const size_t gu_halves = fused_gu(s) ? 2 : 1;  // fused: B^T [2n, r] per expert, all in Bt_g
+  f.Bt_g = c.bytes(fac * gu_halves * s.E * s.r * s.n * es);
+  f.Bt_u = c.bytes(fac * (2 - gu_halves) * s.E * s.r * s.n * es);
   f.Bt_d = c.bytes(fac * s.E * s.r * s.m * es);
   if (ff) *ff = f;
   return align_up(c.off, 256);
@@ -157,7 +160,7 @@ moe_status check_shape(const moe_shape* sp) {
   if ((s.renormalize != 0 && s.renormalize != 1) || (s.router_grad != 0 && s.router_grad != 1))
     return MOE_ERR_INVALID_ARG;
   if (s.flags & ~(MOE_FLAG_REFERENCE_GEMM | MOE_FLAG_RSLORA | MOE_FLAG_WEIGHTS_OUT_IN | MOE_FLAG_MERGED |
-                  MOE_FLAG_RECOMPUTE))
+                  MOE_FLAG_RECOMPUTE | MOE_FLAG_FUSED_GU_LORA))
     return MOE_ERR_INVALID_ARG;
   if (!std::isfinite(s.alpha)) return MOE_ERR_INVALID_ARG;
   if (s.m % 64 || s.n % 64) return MOE_ERR_UNSUPPORTED;
@@ -172,6 +175,16 @@ moe_status check_shape(const moe_shape* sp) {
 inline bool ptr_ok(const void* p, size_t count) {
   if (count == 0) return true;
   return p != nullptr && ((uintptr_t)p & 15u) == 0;
+}
+
+// The LoRA factors (or, with a fused gate/up pair, A in A_g and B [E, r, 2n] in B_g; A_u, B_u unused).
+inline bool lora_ptrs_ok(const moe_shape& s, const void* A_g, const void* B_g, const void* A_u,
+                         const void* B_u, const void* A_d, const void* B_d) {
+  const size_t E = s.E, m = s.m, n = s.n, r = s.r;
+  const bool fz = fused_gu(s);
+  return ptr_ok(A_g, E * m * r) && ptr_ok(B_g, E * r * n * (fz ? 2 : 1)) &&
+         (fz || (ptr_ok(A_u, E * m * r) && ptr_ok(B_u, E * r * n))) && ptr_ok(A_d, E * n * r) &&
+         ptr_ok(B_d, E * r * m);
 }
 
 #define HIP_TRY_STATUS(x)           \
@@ -368,9 +381,14 @@ moe_status forward_experts(const moe_shape& s, const void* X, const int32_t* exp
   const int ref = (s.flags & MOE_FLAG_REFERENCE_GEMM) ? 1 : 0;
   const float c = lora_scale(s);
   const int Pi = (int)P;
+  const bool fz = fused_gu(s);
   if (out_in(s) && !merged(s)) {  // [E, r, n] -> [E, n, r] and [E, r, m] -> [E, m, r]
-    STAGE(ST_FWD_GATE_UP, launch_transpose(s.dtype, B_g, ff.Bt_g, s.r, s.n, s.E, hs));
-    STAGE(ST_FWD_GATE_UP, launch_transpose(s.dtype, B_u, ff.Bt_u, s.r, s.n, s.E, hs));
+    if (fz) {                     // [E, r, 2n] -> [E, 2n, r]
+      STAGE(ST_FWD_GATE_UP, launch_transpose(s.dtype, B_g, ff.Bt_g, s.r, 2 * s.n, s.E, hs));
+    } else {
+      STAGE(ST_FWD_GATE_UP, launch_transpose(s.dtype, B_g, ff.Bt_g, s.r, s.n, s.E, hs));
+      STAGE(ST_FWD_GATE_UP, launch_transpose(s.dtype, B_u, ff.Bt_u, s.r, s.n, s.E, hs));
+    }
     STAGE(ST_FWD_DOWN, launch_transpose(s.dtype, B_d, ff.Bt_d, s.r, s.m, s.E, hs));
   }
 
@@ -383,8 +401,15 @@ moe_status forward_experts(const moe_shape& s, const void* X, const int32_t* exp
 
   // The grouped row i of every expert GEMM is pair perm[i]; its activation row is X[perm[i] / k],
   // gathered by the GEMM kernels (no permuted copy of X is written).
-  // Tc_gu = c * Xp [A_g | A_u]
-  if (!merged(s)) {
+  // Tc_gu = c * Xp [A_g | A_u]  (fused pair: Tc = c * Xp A, P x r)
+  if (!merged(s) && fz) {
+    GemmArgs a = base;
+    a.N = s.r; a.K = s.m;
+    a.A = X; a.lda = s.m; a.arow = perm; a.arow_div = s.k;
+    a.B = A_g; a.ldb = s.r; a.bstride = (long)m * r;
+    a.C = f.Tgu; a.ldc = s.r; a.scale = c;
+    STAGE(ST_FWD_T_GU, gemm_gm_launch(a, LAYOUT_KX, EPI_STORE, 0, s.dtype, Pi, ref, hs));
+  } else if (!merged(s)) {
     GemmArgs a = base;
     a.N = s.r; a.K = s.m;
     a.A = X; a.lda = s.m; a.arow = perm; a.arow_div = s.k;
@@ -411,6 +436,16 @@ moe_status forward_experts(const moe_shape& s, const void* X, const int32_t* exp
       a.TB0 = B_g; a.TB1 = B_u; a.ldtb = s.n;
     }
     a.tbstride = (long)r * n;
+    if (fz && !merged(s)) {  // [g | u] tails Tc [B_g-part | B_u-part] with one shared Tc
+      a.tail = TAIL_SHARED;
+      a.lda2 = s.r;
+      a.tbstride = (long)r * 2 * n;
+      if (out_in(s)) {  // B^T [E, 2n, r]: the up rows start n rows in
+        a.TB0 = ff.Bt_g; a.TB1 = (const char*)ff.Bt_g + n * r * esize(s); a.ldtb = s.r;
+      } else {          // B [E, r, 2n]: the up columns start n columns in
+        a.TB0 = B_g; a.TB1 = (const char*)B_g + n * esize(s); a.ldtb = 2 * s.n;
+      }
+    }
     a.C = f.gu; a.ldc = 2 * s.n; a.cup = s.n;
     a.H = f.h; a.ldh = s.n;
     STAGE(ST_FWD_GATE_UP, gemm_gm_launch(a, out_in(s) ? LAYOUT_XK : LAYOUT_KX, EPI_SWIGLU, 0, s.dtype, Pi,
@@ -456,9 +491,7 @@ moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t
       !ptr_ok(expert_off, E + 1) || !ptr_ok(perm, P) || !ptr_ok(inv_perm, P) ||
       !ptr_ok(W_gu, E * m * 2 * n) || !ptr_ok(W_d, E * n * m) || !ptr_ok(Y, (size_t)s.s * m))
     return MOE_ERR_INVALID_ARG;
-  if (!merged(s) && (!ptr_ok(A_g, E * m * r) || !ptr_ok(B_g, E * r * n) || !ptr_ok(A_u, E * m * r) ||
-                     !ptr_ok(B_u, E * r * n) || !ptr_ok(A_d, E * n * r) || !ptr_ok(B_d, E * r * m)))
-    return MOE_ERR_INVALID_ARG;
+  if (!merged(s) && !lora_ptrs_ok(s, A_g, B_g, A_u, B_u, A_d, B_d)) return MOE_ERR_INVALID_ARG;
   if (!route_state || ((uintptr_t)route_state & 255u)) return MOE_ERR_INVALID_ARG;
   const size_t need_saved = fwd_layout(s, nullptr, nullptr);
   const size_t need_fac = fwd_factor_layout(s, nullptr, nullptr);
@@ -494,9 +527,8 @@ moe_status moe_peft_merge(const moe_shape* shape, const void* W_gu, const void* 
   if (st != MOE_OK) return st;
   const moe_shape& s = *shape;
   const size_t E = s.E, m = s.m, n = s.n, r = s.r;
-  if (!ptr_ok(W_gu, E * m * 2 * n) || !ptr_ok(W_d, E * n * m) || !ptr_ok(A_g, E * m * r) ||
-      !ptr_ok(B_g, E * r * n) || !ptr_ok(A_u, E * m * r) || !ptr_ok(B_u, E * r * n) ||
-      !ptr_ok(A_d, E * n * r) || !ptr_ok(B_d, E * r * m) || !ptr_ok(W_gu_merged, E * m * 2 * n) ||
+  if (!ptr_ok(W_gu, E * m * 2 * n) || !ptr_ok(W_d, E * n * m) ||
+      !lora_ptrs_ok(s, A_g, B_g, A_u, B_u, A_d, B_d) || !ptr_ok(W_gu_merged, E * m * 2 * n) ||
       !ptr_ok(W_d_merged, E * n * m) || W_gu_merged == W_gu || W_d_merged == W_d)
     return MOE_ERR_INVALID_ARG;
   hipStream_t hs = (hipStream_t)stream;
@@ -504,10 +536,15 @@ moe_status moe_peft_merge(const moe_shape* shape, const void* W_gu, const void* 
   const bool kx = !out_in(s);
   const long ld_gu = kx ? 2L * n : (long)m, ld_d = kx ? (long)m : (long)n;
   // gate columns [0, n) and up columns [n, 2n) of W_gu (K = m), then W_d (K = n, N = m)
-  HIP_TRY(launch_merge(s.dtype, kx, W_gu, A_g, B_g, W_gu_merged, s.E, s.m, s.n, s.r, ld_gu, 0,
-                       (long)m * 2 * n, c, hs));
-  HIP_TRY(launch_merge(s.dtype, kx, W_gu, A_u, B_u, W_gu_merged, s.E, s.m, s.n, s.r, ld_gu, (long)n,
-                       (long)m * 2 * n, c, hs));
+  if (fused_gu(s)) {  // one pair over all 2n columns
+    HIP_TRY(launch_merge(s.dtype, kx, W_gu, A_g, B_g, W_gu_merged, s.E, s.m, 2 * s.n, s.r, ld_gu, 0,
+                         (long)m * 2 * n, c, hs));
+  } else {
+    HIP_TRY(launch_merge(s.dtype, kx, W_gu, A_g, B_g, W_gu_merged, s.E, s.m, s.n, s.r, ld_gu, 0,
+                         (long)m * 2 * n, c, hs));
+    HIP_TRY(launch_merge(s.dtype, kx, W_gu, A_u, B_u, W_gu_merged, s.E, s.m, s.n, s.r, ld_gu, (long)n,
+                         (long)m * 2 * n, c, hs));
+  }
   HIP_TRY(launch_merge(s.dtype, kx, W_d, A_d, B_d, W_d_merged, s.E, s.n, s.m, s.r, ld_d, 0,
                        (long)n * m, c, hs));
   return MOE_OK;
@@ -532,10 +569,10 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
   if (!ptr_ok(dY, (size_t)s.s * m) || !ptr_ok(X, (size_t)s.s * m) || !ptr_ok(W_r, m * E) ||
       !ptr_ok(topk_idx, P) || !ptr_ok(topk_w, P) || !ptr_ok(expert_off, E + 1) ||
       !ptr_ok(perm, P) || !ptr_ok(inv_perm, P) || !ptr_ok(W_gu, E * m * 2 * n) ||
-      !ptr_ok(W_d, E * n * m) || !ptr_ok(A_g, E * m * r) || !ptr_ok(B_g, E * r * n) ||
-      !ptr_ok(A_u, E * m * r) || !ptr_ok(B_u, E * r * n) || !ptr_ok(A_d, E * n * r) ||
-      !ptr_ok(B_d, E * r * m) || !ptr_ok(dX, (size_t)s.s * m) || !ptr_ok(dA_g, E * m * r) ||
-      !ptr_ok(dB_g, E * r * n) || !ptr_ok(dA_u, E * m * r) || !ptr_ok(dB_u, E * r * n) ||
+      !ptr_ok(W_d, E * n * m) || !lora_ptrs_ok(s, A_g, B_g, A_u, B_u, A_d, B_d) ||
+      !ptr_ok(dX, (size_t)s.s * m) || !ptr_ok(dA_g, E * m * r) ||
+      !ptr_ok(dB_g, E * r * n * (fused_gu(s) ? 2 : 1)) ||
+      (!fused_gu(s) && (!ptr_ok(dA_u, E * m * r) || !ptr_ok(dB_u, E * r * n))) ||
       !ptr_ok(dA_d, E * n * r) || !ptr_ok(dB_d, E * r * m))
     return MOE_ERR_INVALID_ARG;
   if (!route_state || ((uintptr_t)route_state & 255u)) return MOE_ERR_INVALID_ARG;
@@ -550,9 +587,11 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
   hipStream_t hs = (hipStream_t)stream;
   if (s.s == 0) {
     HIP_TRY(launch_zero(dA_g, E * m * r, hs));
-    HIP_TRY(launch_zero(dA_u, E * m * r, hs));
-    HIP_TRY(launch_zero(dB_g, E * r * n, hs));
-    HIP_TRY(launch_zero(dB_u, E * r * n, hs));
+    HIP_TRY(launch_zero(dB_g, E * r * n * (fused_gu(s) ? 2 : 1), hs));
+    if (!fused_gu(s)) {
+      HIP_TRY(launch_zero(dA_u, E * m * r, hs));
+      HIP_TRY(launch_zero(dB_u, E * r * n, hs));
+    }
     HIP_TRY(launch_zero(dA_d, E * n * r, hs));
     HIP_TRY(launch_zero(dB_d, E * r * m, hs));
     return MOE_OK;
@@ -650,8 +689,16 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
     gk_prep(a);
     STAGE(ST_BWD_GRAD_D, gemm_gk_launch(a, s.dtype, ref, Pi, hs));
   }
-  // Uc_gu = c * [dg B_g^T | du B_u^T]
-  {
+  const bool fz = fused_gu(s);
+  // Uc_gu = c * [dg B_g^T | du B_u^T]  (fused pair: Uc = c * [dg | du] B^T, one product over 2n)
+  if (fz) {
+    GemmArgs a = base;
+    a.N = s.r; a.K = 2 * s.n;
+    a.A = b.dgu; a.lda = 2 * s.n;
+    a.B = B_g; a.ldb = 2 * s.n; a.bstride = (long)r * 2 * n;
+    a.C = b.Ugu; a.ldc = s.r; a.scale = c;
+    STAGE(ST_BWD_U_GU, gemm_gm_launch(a, LAYOUT_XK, EPI_STORE, 0, s.dtype, Pi, ref, hs));
+  } else {
     GemmArgs a = base;
     a.N = s.r; a.K = s.n;
     a.A = b.dgu; a.lda = 2 * s.n;
@@ -669,14 +716,14 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
     a.N = s.m; a.K = 2 * s.n;
     a.A = b.dgu; a.lda = 2 * s.n;
     a.B = W_gu; a.ldb = out_in(s) ? s.m : 2 * s.n; a.bstride = (long)m * 2 * n;
-    a.tail = TAIL_STACKED; a.r2a = s.r;
-    a.TA = b.Ugu; a.lda2 = 2 * s.r;
+    a.tail = fz ? TAIL_SINGLE : TAIL_STACKED; a.r2a = s.r;
+    a.TA = b.Ugu; a.lda2 = fz ? s.r : 2 * s.r;
     if (out_in(s)) {  // A_g, A_u [E, m, r] -> [E, r, m]
       STAGE(ST_BWD_GATE_UP, launch_transpose(s.dtype, A_g, b.At_g, s.m, s.r, s.E, hs));
-      STAGE(ST_BWD_GATE_UP, launch_transpose(s.dtype, A_u, b.At_u, s.m, s.r, s.E, hs));
-      a.TB0 = b.At_g; a.TB1 = b.At_u; a.ldtb = s.m;
+      if (!fz) STAGE(ST_BWD_GATE_UP, launch_transpose(s.dtype, A_u, b.At_u, s.m, s.r, s.E, hs));
+      a.TB0 = b.At_g; a.TB1 = fz ? nullptr : b.At_u; a.ldtb = s.m;
     } else {
-      a.TB0 = A_g; a.TB1 = A_u; a.ldtb = s.r;
+      a.TB0 = A_g; a.TB1 = fz ? nullptr : A_u; a.ldtb = s.r;
     }
     a.tbstride = (long)m * r;
     a.C = b.dXp; a.ldc = s.m;
@@ -684,7 +731,23 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
                                          hs));
   }
   // dA_g | dA_u = Xp^T [Uc_g | Uc_u] ;  dB_g = Tc_g^T dg, dB_u = Tc_u^T du
-  {
+  if (fz) {  // dA = Xp^T Uc ;  dB = Tc^T [dg | du]
+    GemmArgs a = base;
+    a.M = s.m; a.N = s.r;
+    a.A = X; a.lda = s.m; a.arow = perm; a.arow_div = s.k;
+    a.B = b.Ugu; a.ldb = s.r;
+    a.C = dA_g; a.ldc = s.r; a.cstride = (long)m * r;
+    gk_prep(a);
+    STAGE(ST_BWD_GRAD_GU, gemm_gk_launch(a, s.dtype, ref, Pi, hs));
+    GemmArgs bg = base;
+    bg.M = 2 * s.n; bg.N = s.r;
+    bg.A = b.dgu; bg.lda = 2 * s.n;
+    bg.B = f.Tgu; bg.ldb = s.r;
+    bg.C = dB_g; bg.ldc = 2 * s.n; bg.cstride = (long)r * 2 * n; bg.ctrans = 1;
+    gk_prep(bg);
+    STAGE(ST_BWD_GRAD_GU, gemm_gk_launch(bg, s.dtype, ref, Pi, hs));
+    if (n_gk) STAGE(ST_BWD_GRAD_GU, gemm_gk_reduce(gk_jobs, n_gk, Pi, hs));
+  } else {
     GemmArgs a = base;
     a.M = s.m; a.N = 2 * s.r;
     a.A = X; a.lda = s.m; a.arow = perm; a.arow_div = s.k;

@@ -30,6 +30,8 @@ enum TailMode : int {
   TAIL_BLOCKDIAG = 2,  // dual: tail rows [0, r2a) feed gate columns from source 0,
                        //       rows [r2a, 2 r2a) feed up columns from source 1
   TAIL_STACKED = 3,    // tail rows [0, r2a) from source 0, [r2a, 2 r2a) from source 1
+  TAIL_SHARED = 4,     // dual: the r2a tail rows feed gate columns from source 0 and up columns
+                       //       from source 1 (one low-rank input shared by both halves)
 };
 
 struct GemmArgs {

@@ -336,10 +336,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gm_mfma(GemmArgs a, int tidx, co
   // ---- Split-LoRA tail: TAIL_STEPS more K tiles [TA | 0] . [TB ; 0], zero-filled via registers
   if constexpr (TAIL) {
     const int r2 = a.r2a;
-    const int K2 = (a.tail == TAIL_SINGLE) ? r2 : 2 * r2;
+    const int K2 = (a.tail == TAIL_SINGLE || a.tail == TAIL_SHARED) ? r2 : 2 * r2;
     const i32x4_t zero = {0, 0, 0, 0};
     const bf16_t* T0 = (const bf16_t*)a.TB0 + (long)e * a.tbstride;
-    const bf16_t* T1 = a.TB1 ? (const bf16_t*)a.TB1 + (long)e * a.tbstride : nullptr;
+    const bf16_t* T1 = a.TB1 ? (const bf16_t*)a.TB1 + (long)e * a.tbstride : T0;
     static_for<TAIL_STEPS>([&](auto tc) {
       constexpr int ts = decltype(tc)::value;
       bf16_t* sA = smem + ts * STAGE;
@@ -362,6 +362,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gm_mfma(GemmArgs a, int tidx, co
           const int jj = min(j0 + x - half * BNH, a.N - 8);
           if (a.tail == TAIL_SINGLE) {
             if (kk < r2) src = T0 + (long)kk * a.ldtb + jj;
+          } else if (a.tail == TAIL_SHARED) {
+            if (kk < r2) src = (half ? T1 : T0) + (long)kk * a.ldtb + jj;
           } else if (a.tail == TAIL_BLOCKDIAG) {
             if (half == 0 && kk < r2) src = T0 + (long)kk * a.ldtb + jj;
             else if (half == 1 && kk >= r2 && kk < 2 * r2) src = T1 + (long)(kk - r2) * a.ldtb + jj;
@@ -376,6 +378,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gm_mfma(GemmArgs a, int tidx, co
           const int jj = min(j0 + x - half * BNH, a.N - 1);
           if (a.tail == TAIL_SINGLE) {
             if (k8 < r2) src = T0 + (long)jj * a.ldtb + k8;
+          } else if (a.tail == TAIL_SHARED) {
+            if (k8 < r2) src = (half ? T1 : T0) + (long)jj * a.ldtb + k8;
           } else if (a.tail == TAIL_BLOCKDIAG) {
             if (half == 0 && k8 < r2) src = T0 + (long)jj * a.ldtb + k8;
             else if (half == 1 && k8 >= r2 && k8 < 2 * r2) src = T1 + (long)jj * a.ldtb + (k8 - r2);
@@ -704,7 +708,7 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
   if (a.tail != TAIL_NONE) {
     lds_barrier();  // every wave is done with both stages
     const int r2 = a.r2a;
-    const int K2 = (a.tail == TAIL_SINGLE) ? r2 : 2 * r2;
+    const int K2 = (a.tail == TAIL_SINGLE || a.tail == TAIL_SHARED) ? r2 : 2 * r2;
     const int tsteps = (K2 + BKT - 1) / BKT;
     const i32x4_t zero = {0, 0, 0, 0};
     const bf16_t* T0 = (const bf16_t*)a.TB0 + (long)e * a.tbstride;
@@ -727,6 +731,8 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
           const int jj = min(j0 + x - half * BNH, a.N - 8);
           if (a.tail == TAIL_SINGLE) {
             if (kk < r2) src = T0 + (long)kk * a.ldtb + jj;
+          } else if (a.tail == TAIL_SHARED) {
+            if (kk < r2) src = (half ? T1 : T0) + (long)kk * a.ldtb + jj;
           } else if (a.tail == TAIL_BLOCKDIAG) {
             if (half == 0 && kk < r2) src = T0 + (long)kk * a.ldtb + jj;
             else if (half == 1 && kk >= r2 && kk < 2 * r2) src = T1 + (long)(kk - r2) * a.ldtb + jj;
@@ -741,6 +747,8 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
           const int jj = min(j0 + x - half * BNH, a.N - 1);
           if (a.tail == TAIL_SINGLE) {
             if (k8 < r2) src = T0 + (long)jj * a.ldtb + k8;
+          } else if (a.tail == TAIL_SHARED) {
+            if (k8 < r2) src = (half ? T1 : T0) + (long)jj * a.ldtb + k8;
           } else if (a.tail == TAIL_BLOCKDIAG) {
             if (half == 0 && k8 < r2) src = T0 + (long)jj * a.ldtb + k8;
             else if (half == 1 && k8 >= r2 && k8 < 2 * r2) src = T1 + (long)jj * a.ldtb + (k8 - r2);
@@ -1048,6 +1056,9 @@ __global__ void gm_simt(GemmArgs a, int b_layout, int total_rows_bound) {
     const T* T1 = a.TB1 ? (const T*)a.TB1 + (long)e * a.tbstride : nullptr;
     if (a.tail == TAIL_SINGLE) {
       for (int q = 0; q < r2; q++) acc0 += to_f(TAr[q]) * opv(T0, b_layout, a.ldtb, jj, q);
+    } else if (a.tail == TAIL_SHARED) {
+      for (int q = 0; q < r2; q++) acc0 += to_f(TAr[q]) * opv(T0, b_layout, a.ldtb, jj, q);
+      for (int q = 0; q < r2; q++) acc1 += to_f(TAr[q]) * opv(T1, b_layout, a.ldtb, jj, q);
     } else if (a.tail == TAIL_BLOCKDIAG) {
       for (int q = 0; q < r2; q++) acc0 += to_f(TAr[q]) * opv(T0, b_layout, a.ldtb, jj, q);
       for (int q = 0; q < r2; q++) acc1 += to_f(TAr[r2 + q]) * opv(T1, b_layout, a.ldtb, jj, q);
@@ -1186,7 +1197,7 @@ hipError_t launch_gm_ring(const GemmArgs& a, int rows_bound, hipStream_t stream)
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32, BNH = DUAL ? BN / 2 : BN;
   if (!a.goff || !a.toff_all || !a.tmap_all || a.K % 64 || a.kchunk) return hipErrorInvalidValue;
   if (a.tail != TAIL_NONE) {
-    const int K2 = a.tail == TAIL_SINGLE ? a.r2a : 2 * a.r2a;
+    const int K2 = (a.tail == TAIL_SINGLE || a.tail == TAIL_SHARED) ? a.r2a : 2 * a.r2a;
     if (K2 <= 0 || K2 > 128 || K2 % 8) return hipErrorInvalidValue;
   }
   const int tidx = tile_table_index(BM);

@@ -60,8 +60,14 @@ def forward(shape, X, rt, W, training=True, Y=None, saved=None, ws=None, stream=
 
 
 def alloc_grads(shape, device) -> dict:
+    """Gradient buffers; with a fused gate/up LoRA pair dA_g is dA [E, m, r], dB_g is dB
+    [E, r, 2n], and there are no dA_u, dB_u."""
     E, m, n, r = shape.E, shape.m, shape.n, shape.r
     f = dict(dtype=torch.float32, device=device)
+    if shape.flags & 32:  # MOE_FLAG_FUSED_GU_LORA
+        return {"dA_g": torch.empty(E, m, r, **f), "dB_g": torch.empty(E, r, 2 * n, **f),
+                "dA_u": None, "dB_u": None,
+                "dA_d": torch.empty(E, n, r, **f), "dB_d": torch.empty(E, r, m, **f)}
     return {"dA_g": torch.empty(E, m, r, **f), "dB_g": torch.empty(E, r, n, **f),
             "dA_u": torch.empty(E, m, r, **f), "dB_u": torch.empty(E, r, n, **f),
             "dA_d": torch.empty(E, n, r, **f), "dB_d": torch.empty(E, r, m, **f)}

@@ -77,6 +77,14 @@ typedef int32_t moe_status;
  * checkpointing: activations are not kept and the forward is recomputed in the backward). With
  * this flag moe_bwd_ws_bytes includes that room; the forward may then run with saved == NULL. */
 #define MOE_FLAG_RECOMPUTE 16
+/* one LoRA pair on the fused gate/up projection instead of one per projection: the adapter targets
+ * the single gate_up_proj tensor (unsloth.ai "Faster MoE" page, section "Faster LoRA MoE
+ * training", the target_modules list of its get_peft_model example), so Delta W_gu = c A B with
+ * A [E, m, r] passed as A_g and B [E, r, 2n] (gate columns [0, n), then up columns [n, 2n), as in
+ * W_gu) passed as B_g. A_u and B_u are not read (may be NULL). moe_lora_backward writes dA [E, m, r]
+ * to dA_g and dB [E, r, 2n] to dB_g and leaves dA_u and dB_u untouched (may be NULL); moe_peft_merge
+ * merges the pair into both halves of W_gu. */
+#define MOE_FLAG_FUSED_GU_LORA 32
 
 typedef struct moe_shape {
   int32_t s;           /* tokens */

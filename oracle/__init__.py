@@ -33,7 +33,8 @@ import numpy as np
 __all__ = [
     "router_logits", "topk_experts", "routing_weights", "group_by_expert", "route",
     "silu", "expert_rows_forward", "expert_rows_backward", "forward", "router_backward",
-    "backward", "forward_tokens", "backward_tokens", "backward_expert",
+    "backward", "forward_tokens", "backward_tokens", "backward_expert", "fused_gate_up_pair",
+    "fused_gate_up_grads",
 ]
 
 
@@ -247,6 +248,29 @@ def forward(X, W: dict, rt: dict, alpha: float, r: int, keep: bool = True, rslor
         Y += w[:, j:j + 1] * o[inv[tok * k + j]]
     saved["o"] = o
     return Y, saved
+
+
+def fused_gate_up_pair(A, B) -> dict:
+    """One LoRA pair on the fused gate/up projection written as the two per-projection pairs.
+
+    [UNS] section "Faster LoRA MoE training": the adapter targets the single gate_up_proj tensor,
+    so Delta W_gu = (alpha/r) A B with A in R^{m x r}, B in R^{r x 2n}. Its gate columns [0, n) are
+    A B[:, :n] and its up columns A B[:, n:], which is the per-projection form with one shared A:
+    A_g = A_u = A, B_g = B[:, :n], B_u = B[:, n:].
+    """
+    B = _f64(B)
+    n = B.shape[-1] // 2
+    A = _f64(A)
+    return {"A_g": A, "A_u": A, "B_g": B[..., :n], "B_u": B[..., n:]}
+
+
+def fused_gate_up_grads(g: dict):
+    """Gradients (dA, dB) of the fused gate/up pair from those of its per-projection form.
+
+    A enters both halves, so its gradient is the sum dA_g + dA_u (chain rule for a parameter used
+    twice); B's gradient is the column concatenation [dB_g | dB_u].
+    """
+    return g["dA_g"] + g["dA_u"], np.concatenate([g["dB_g"], g["dB_u"]], axis=-1)
 
 
 def router_backward(ds, rt: dict, W_r, score: str = "softmax", renormalize: bool = True):

@@ -62,7 +62,7 @@ def shape(**kw):
     (dict(r=0), g.MOE_ERR_INVALID_ARG),
     (dict(dtype=5), g.MOE_ERR_INVALID_ARG),
     (dict(score=3), g.MOE_ERR_INVALID_ARG),
-    (dict(flags=32), g.MOE_ERR_INVALID_ARG),
+    (dict(flags=64), g.MOE_ERR_INVALID_ARG),
     (dict(alpha=float("nan")), g.MOE_ERR_INVALID_ARG),
     (dict(m=200), g.MOE_ERR_UNSUPPORTED),
     (dict(n=100), g.MOE_ERR_UNSUPPORTED),

@@ -28,11 +28,28 @@ def _say(msg):
 FLAG_RSLORA = 2
 FLAG_WEIGHTS_OUT_IN = 4
 FLAG_RECOMPUTE = 16
+FLAG_FUSED_GU = 32
+
+
+def fuse_gate_up(inp):
+    """One LoRA pair on the fused gate/up projection from the generator's draws: A = A_g and
+    B = [B_g | B_u] (E, r, 2n); the per-projection up factors are dropped."""
+    return dict(inp, B_g=torch.cat([inp["B_g"], inp["B_u"]], dim=2).contiguous(), A_u=None, B_u=None)
+
+
+def oracle_weights(inp, flags):
+    if not flags & FLAG_FUSED_GU:
+        return host_weights(inp)
+    W = {k: np64(inp[k]) for k in ("W_gu", "W_d", "A_d", "B_d")}
+    W.update(oracle.fused_gate_up_pair(np64(inp["A_g"]), np64(inp["B_g"])))
+    return W
 
 
 def run_gpu(cfg, device, flags=0, router_grad=True):
     from grouped_gemm_top_amd import layer
     inp = make_inputs(cfg, seed=0, device="cpu", with_grad_output=cfg.backward)
+    if flags & FLAG_FUSED_GU:
+        inp = fuse_gate_up(inp)
     d = {k: (v.to(device) if v is not None else None) for k, v in inp.items()}
     if flags & FLAG_WEIGHTS_OUT_IN:  # the library gets W_gu [E, 2n, m] and W_d [E, m, n]
         d["W_gu"] = d["W_gu"].transpose(1, 2).contiguous()
@@ -81,7 +98,10 @@ def test_layer_parity(name, flags, cuda):
 # weights on the reference kernels
 FLAG_CASES = {"rslora": FLAG_RSLORA, "out_in": FLAG_WEIGHTS_OUT_IN,
               "out_in_rslora": FLAG_WEIGHTS_OUT_IN | FLAG_RSLORA, "out_in_reference": FLAG_WEIGHTS_OUT_IN | 1,
-              "recompute": FLAG_RECOMPUTE, "recompute_out_in": FLAG_RECOMPUTE | FLAG_WEIGHTS_OUT_IN}
+              "recompute": FLAG_RECOMPUTE, "recompute_out_in": FLAG_RECOMPUTE | FLAG_WEIGHTS_OUT_IN,
+              # one LoRA pair on the fused gate/up projection, alone and with the other modes
+              "fused_gu": FLAG_FUSED_GU, "fused_gu_out_in": FLAG_FUSED_GU | FLAG_WEIGHTS_OUT_IN,
+              "fused_gu_recompute": FLAG_FUSED_GU | FLAG_RECOMPUTE, "fused_gu_reference": FLAG_FUSED_GU | 1}
 
 
 @pytest.mark.parametrize("mode", list(FLAG_CASES))
@@ -95,7 +115,7 @@ def _parity(cfg, name, flags, cuda):
          f"r={cfg.r} {cfg.dtype} {cfg.score} backward={cfg.backward}")
     inp, out = run_gpu(cfg, cuda, flags=flags)
     ort = check_routing(cfg, inp, out["rt"])
-    W = host_weights(inp)
+    W = oracle_weights(inp, flags)
     X = np64(inp["X"])
     rs = bool(flags & FLAG_RSLORA)
     Y_ref, saved = oracle.forward(X, W, ort, cfg.alpha, cfg.r, rslora=rs)
@@ -105,7 +125,12 @@ def _parity(cfg, name, flags, cuda):
         g = oracle.backward(np64(inp["dY"]), X, np64(inp["W_r"]), W, ort, cfg.alpha, cfg.r,
                             cfg.score, cfg.renormalize, True, saved, rslora=rs)
         errs["dX"] = rel_err(np64(out["dX"]), g["dX"])
-        for key in GRAD_KEYS:
+        keys = GRAD_KEYS
+        if flags & FLAG_FUSED_GU:  # dA [E, m, r] in dA_g, dB [E, r, 2n] in dB_g
+            g["dA_g"], g["dB_g"] = oracle.fused_gate_up_grads(g)
+            keys = ("dA_g", "dB_g", "dA_d", "dB_d")
+            assert out["dB_g"].shape == (cfg.E, cfg.r, 2 * cfg.n)
+        for key in keys:
             errs[key] = rel_err(np64(out[key]), g[key])
     _say("  rel errors: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     bad = {k: v for k, v in errs.items() if not v <= tol}
@@ -184,3 +209,38 @@ def test_merged_weights_forward(name, out_in, cuda):
     err = rel_err(np64(Y), Y_ref)
     _say(f"  merge err gu {rel_err(got_gu, ref_gu):.2e} d {rel_err(got_d, ref_d):.2e}; Y {err:.2e}")
     assert err <= tol
+
+
+@pytest.mark.parametrize("out_in", [False, True], ids=["x_w", "out_in"])
+def test_merged_weights_fused_gate_up(out_in, cuda):
+    """moe_peft_merge with one fused gate/up pair: W_gu + c A B over all 2n columns."""
+    from grouped_gemm_top_amd import layer, moe_peft_merge
+    cfg = VARIANTS["qwen3_small"]
+    _say(f"[merged fused] qwen3_small out_in={out_in}")
+    flags = FLAG_FUSED_GU | (FLAG_WEIGHTS_OUT_IN if out_in else 0)
+    inp = fuse_gate_up(make_inputs(cfg, seed=0, device="cpu", with_grad_output=False))
+    d = {k: (v.to(cuda) if v is not None else None) for k, v in inp.items()}
+    if out_in:
+        d["W_gu"] = d["W_gu"].transpose(1, 2).contiguous()
+        d["W_d"] = d["W_d"].transpose(1, 2).contiguous()
+    shape = layer.shape_of(cfg, flags=flags)
+    Wm_gu, Wm_d = torch.empty_like(d["W_gu"]), torch.empty_like(d["W_d"])
+    moe_peft_merge(shape, d["W_gu"], d["W_d"], d["A_g"], d["B_g"], None, None, d["A_d"], d["B_d"],
+                   Wm_gu, Wm_d)
+    torch.cuda.synchronize()
+    W = oracle_weights(inp, flags)
+    c = cfg.alpha / cfg.r
+    ref_gu = np64(inp["W_gu"]) + c * np64(inp["A_g"]) @ np64(inp["B_g"])
+    got_gu = np64(Wm_gu)
+    if out_in:
+        got_gu = got_gu.transpose(0, 2, 1)
+    err = rel_err(got_gu, ref_gu)
+    rt = layer.route(shape, d["X"], d["W_r"], d["router_bias"])
+    dm = dict(d, W_gu=Wm_gu, W_d=Wm_d, A_g=None, B_g=None, A_u=None, B_u=None, A_d=None, B_d=None)
+    Y, _ = layer.forward(layer.shape_of(cfg, flags=flags | 8), d["X"], rt, dm, training=False)
+    torch.cuda.synchronize()
+    ort = check_routing(cfg, inp, rt)
+    Y_ref, _ = oracle.forward(np64(inp["X"]), W, ort, cfg.alpha, cfg.r, keep=False)
+    yerr = rel_err(np64(Y), Y_ref)
+    _say(f"  merge err gu {err:.2e}; Y {yerr:.2e}")
+    assert err <= TOL[cfg.dtype] and yerr <= TOL[cfg.dtype]

@@ -336,3 +336,58 @@ def test_sampled_outputs_equal_full_layer():
             ge = oracle.backward_expert(e, dY, X, W, rt, alpha, r)
             for key, v in ge.items():
                 np.testing.assert_allclose(v, g[key][e], rtol=1e-12, atol=1e-14)
+
+
+# ------------------------------------------------------------------ fused gate/up LoRA pair
+
+def test_fused_gate_up_pair_equals_dense_merge():
+    """One pair on gate_up_proj: y equals the per-token loop over W_gu + c A B (2n columns at once)."""
+    rng = np.random.default_rng(41)
+    s, m, n, E, k, r, alpha = 20, 8, 6, 3, 2, 2, 5.0
+    c = alpha / r
+    X, W_r, W, _ = _rand_layer(rng, s, m, n, E, k, r)
+    A = rng.normal(0, 0.5, (E, m, r))
+    B = rng.normal(0, 0.5, (E, r, 2 * n))
+    W.update(oracle.fused_gate_up_pair(A, B))
+    rt = oracle.route(oracle.router_logits(X, W_r), k, E)
+    Y, _ = oracle.forward(X, W, rt, alpha, r, keep=False)
+    ref = np.zeros((s, m))
+    for t in range(s):
+        for j in range(k):
+            e = rt["idx"][t, j]
+            gu = X[t] @ (W["W_gu"][e] + c * A[e] @ B[e])
+            h = _silu(gu[:n]) * gu[n:]
+            ref[t] += rt["w"][t, j] * (h @ (W["W_d"][e] + c * W["A_d"][e] @ W["B_d"][e]))
+    np.testing.assert_allclose(Y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_fused_gate_up_grads_match_central_finite_differences():
+    """dA, dB of the fused pair (summed / concatenated from the per-projection gradients) equal fp64
+    central differences of the loss taken with respect to the fused A and B themselves."""
+    rng = np.random.default_rng(43)
+    s, m, n, E, k, r, alpha = 6, 8, 4, 3, 2, 2, 3.0
+    X, W_r, W, dY = _rand_layer(rng, s, m, n, E, k, r)
+    A = rng.normal(0, 0.5, (E, m, r))
+    B = rng.normal(0, 0.5, (E, r, 2 * n))
+    rt = oracle.route(oracle.router_logits(X, W_r), k, E)
+
+    def loss():
+        Wf = dict(W, **oracle.fused_gate_up_pair(A, B))
+        Y, _ = oracle.forward(X, Wf, rt, alpha, r, keep=False)
+        return float(np.sum(dY * Y))
+
+    g = oracle.backward(dY, X, W_r, dict(W, **oracle.fused_gate_up_pair(A, B)), rt, alpha, r)
+    dA, dB = oracle.fused_gate_up_grads(g)
+    h = 1e-6
+    for arr, got in ((A, dA), (B, dB)):
+        fd = np.zeros_like(arr)
+        for i in np.ndindex(arr.shape):
+            old = arr[i]
+            arr[i] = old + h
+            lp = loss()
+            arr[i] = old - h
+            lm = loss()
+            arr[i] = old
+            fd[i] = (lp - lm) / (2 * h)
+        assert got.shape == arr.shape
+        assert np.max(np.abs(got - fd)) <= 1e-6 * max(np.max(np.abs(fd)), 1e-3)
