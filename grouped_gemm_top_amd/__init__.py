@@ -20,6 +20,8 @@ __all__ = [
     "MOE_FLAG_REFERENCE_GEMM", "MOE_FLAG_RSLORA", "MOE_FLAG_WEIGHTS_OUT_IN", "MOE_FLAG_MERGED", "MOE_FLAG_RECOMPUTE",
     "MOE_FLAG_FUSED_GU_LORA",
     "moe_peft_merge", "moe_timing_enable", "moe_timing_read",
+    "moe_shared_saved_bytes", "moe_shared_fwd_ws_bytes", "moe_shared_bwd_ws_bytes",
+    "moe_shared_forward", "moe_shared_backward",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoelora.so")
@@ -67,6 +69,11 @@ _SIGNATURES = {
     "moe_lora_forward": (_I32, [_SHAPE] + [_P] * 17 + [_SZ, _P, _SZ, _P]),
     "moe_lora_backward": (_I32, [_SHAPE] + [_P] * 18 + [_SZ] + [_P] * 8 + [_SZ, _P]),
     "moe_peft_merge": (_I32, [_SHAPE] + [_P] * 11),
+    "moe_shared_saved_bytes": (_SZ, [_SHAPE]),
+    "moe_shared_fwd_ws_bytes": (_SZ, [_SHAPE, _I32]),
+    "moe_shared_bwd_ws_bytes": (_SZ, [_SHAPE]),
+    "moe_shared_forward": (_I32, [_SHAPE] + [_P] * 11 + [_SZ, _P, _SZ, _P]),
+    "moe_shared_backward": (_I32, [_SHAPE] + [_P] * 11 + [_SZ] + [_P] * 8 + [_SZ, _P]),
     "moe_timing_enable": (_I32, [_I32]),
     "moe_timing_stage_count": (_I32, []),
     "moe_timing_stage_name": (ctypes.c_char_p, [_I32]),
@@ -188,6 +195,36 @@ def moe_lora_backward(shape, dY, X, W_r, topk_idx, topk_w, expert_off, perm, inv
         _nbytes(saved), _ptr(dX), _ptr(dA_g), _ptr(dB_g), _ptr(dA_u), _ptr(dB_u), _ptr(dA_d),
         _ptr(dB_d), _ptr(ws), _nbytes(ws), _stream(stream))
     _check(st, "moe_lora_backward")
+
+
+def moe_shared_saved_bytes(shape: MoeShape) -> int:
+    return int(lib().moe_shared_saved_bytes(ctypes.byref(shape)))
+
+
+def moe_shared_fwd_ws_bytes(shape: MoeShape, with_saved: bool) -> int:
+    return int(lib().moe_shared_fwd_ws_bytes(ctypes.byref(shape), int(bool(with_saved))))
+
+
+def moe_shared_bwd_ws_bytes(shape: MoeShape) -> int:
+    return int(lib().moe_shared_bwd_ws_bytes(ctypes.byref(shape)))
+
+
+def moe_shared_forward(shape, X, W_gu, W_d, A_g, B_g, A_u, B_u, A_d, B_d, Y, saved, ws, stream=None):
+    st = lib().moe_shared_forward(
+        ctypes.byref(shape), _ptr(X), _ptr(W_gu), _ptr(W_d), _ptr(A_g), _ptr(B_g), _ptr(A_u),
+        _ptr(B_u), _ptr(A_d), _ptr(B_d), _ptr(Y), _ptr(saved), _nbytes(saved), _ptr(ws),
+        _nbytes(ws), _stream(stream))
+    _check(st, "moe_shared_forward")
+
+
+def moe_shared_backward(shape, dY, X, W_gu, W_d, A_g, B_g, A_u, B_u, A_d, B_d, saved, dX, dA_g, dB_g,
+                        dA_u, dB_u, dA_d, dB_d, ws, stream=None):
+    st = lib().moe_shared_backward(
+        ctypes.byref(shape), _ptr(dY), _ptr(X), _ptr(W_gu), _ptr(W_d), _ptr(A_g), _ptr(B_g),
+        _ptr(A_u), _ptr(B_u), _ptr(A_d), _ptr(B_d), _ptr(saved), _nbytes(saved), _ptr(dX),
+        _ptr(dA_g), _ptr(dB_g), _ptr(dA_u), _ptr(dB_u), _ptr(dA_d), _ptr(dB_d), _ptr(ws),
+        _nbytes(ws), _stream(stream))
+    _check(st, "moe_shared_backward")
 
 
 def moe_timing_enable(on: bool) -> None:

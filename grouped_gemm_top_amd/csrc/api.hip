@@ -94,7 +94,9 @@ size_t route_layout(const moe_shape& s, void* base, RouteState* rs) {
   return align_up(c.off, 256);
 }
 
-size_t fwd_layout(const moe_shape& s, void* base, FwdBufs* fb) {
+// with_o: room for the expert outputs o (the routed layer's combine input; a shared expert adds its
+// output straight into Y and keeps none)
+size_t fwd_layout(const moe_shape& s, void* base, FwdBufs* fb, bool with_o = true) {
   Carve c(base);
   const size_t P = (size_t)pairs(s), es = esize(s);
   FwdBufs f;
@@ -102,7 +104,7 @@ size_t fwd_layout(const moe_shape& s, void* base, FwdBufs* fb) {
   f.h = c.bytes(P * s.n * es);
   f.Tgu = c.bytes(P * 2 * s.r * es);
   f.Td = c.bytes(P * s.r * es);
-  f.o = c.bytes(P * s.m * es);
+  f.o = with_o ? c.bytes(P * s.m * es) : nullptr;
   if (fb) *fb = f;
   return align_up(c.off, 256);
 }
@@ -125,22 +127,24 @@ size_t fwd_factor_layout(const moe_shape& s, void* base, FwdFactors* ff) {
 }
 
 // Backward workspace tail for recomputing the forward's intermediates (MOE_FLAG_RECOMPUTE).
-size_t recompute_bytes(const moe_shape& s) {
-  return recompute(s) ? fwd_layout(s, nullptr, nullptr) + fwd_factor_layout(s, nullptr, nullptr) : 0;
+size_t recompute_bytes(const moe_shape& s, bool with_o = true) {
+  return recompute(s) ? fwd_layout(s, nullptr, nullptr, with_o) + fwd_factor_layout(s, nullptr, nullptr) : 0;
 }
 
-size_t bwd_layout(const moe_shape& s, void* base, BwdBufs* bb) {
+// routed: the combine/router/unpermute buffers (dO, ds, dz, W_r^T, dXp); a shared expert reads dY
+// as its dO and adds its dX straight into the caller's
+size_t bwd_layout(const moe_shape& s, void* base, BwdBufs* bb, bool routed = true) {
   Carve c(base);
-  const size_t P = (size_t)pairs(s), es = esize(s);
+  const size_t P = (size_t)pairs(s), es = esize(s), rt = routed ? 1 : 0;
   BwdBufs b;
-  b.dO = c.bytes(P * s.m * es);
-  b.ds = c.take<float>(P);
-  b.dz = c.take<float>(P);
-  b.WrT = c.bytes((size_t)s.E * s.m * es);
+  b.dO = c.bytes(rt * P * s.m * es);
+  b.ds = c.take<float>(rt * P);
+  b.dz = c.take<float>(rt * P);
+  b.WrT = c.bytes(rt * s.E * s.m * es);
   b.Ud = c.bytes(P * s.r * es);
   b.dgu = c.bytes(P * 2 * s.n * es);
   b.Ugu = c.bytes(P * 2 * s.r * es);
-  b.dXp = c.bytes(P * s.m * es);
+  b.dXp = c.bytes(rt * P * s.m * es);
   b.gkpart = c.take<float>((size_t)gk_part_floats((long)P, s.E, 1, 3L * (s.n + s.m) * s.r));
   const size_t fac = out_in(s) ? 1 : 0;  // the tails then read the factors in the weights' layout
   b.At_d = c.bytes(fac * s.E * s.r * s.n * es);
@@ -371,11 +375,23 @@ moe_status moe_route(const moe_shape* shape, const void* X, const void* W_r,
 // GEMM with its SwiGLU epilogue and the down GEMM, writing gu, h, Tc_gu, Tc_d and o into f (ff:
 // transposed tail factors for output-major weights). Shared by the forward and by a backward that
 // recomputes them.
-moe_status forward_experts(const moe_shape& s, const void* X, const int32_t* expert_off,
-                           const int32_t* perm, const RouteState& rs, const void* W_gu, const void* W_d,
-                           const void* A_g, const void* B_g, const void* A_u, const void* B_u,
-                           const void* A_d, const void* B_d, const FwdBufs& f, const FwdFactors& ff,
-                           hipStream_t hs) {
+// Row grouping of the expert GEMMs: G groups of rows (off[G + 1]); grouped row i reads activation
+// row arow[i] / arow_div of X (arow == nullptr: row i), with the row-tile tables of launch_scan.
+struct Grouping {
+  int G;
+  const int32_t* off;
+  const int32_t* arow;
+  int arow_div;
+  const int* tiles;
+  const int* tmaps;
+};
+
+// The expert MLPs with Split LoRA over the grouped rows. The down projection's output goes to o_dst
+// (overwritten, or added to with accum; not computed when o_dst is null).
+static moe_status forward_experts(const moe_shape& s, const void* X, const Grouping& gr, const void* W_gu,
+                           const void* W_d, const void* A_g, const void* B_g, const void* A_u,
+                           const void* B_u, const void* A_d, const void* B_d, const FwdBufs& f,
+                           const FwdFactors& ff, void* o_dst, int accum, hipStream_t hs) {
   const long P = pairs(s);
   const size_t m = s.m, n = s.n, r = s.r;
   const int ref = (s.flags & MOE_FLAG_REFERENCE_GEMM) ? 1 : 0;
@@ -394,10 +410,10 @@ moe_status forward_experts(const moe_shape& s, const void* X, const int32_t* exp
 
 
   GemmArgs base = gemm_args();
-  base.G = s.E;
-  base.goff = expert_off;
-  base.toff_all = rs.tiles;
-  base.tmap_all = rs.tmaps;
+  base.G = gr.G;
+  base.goff = gr.off;
+  base.toff_all = gr.tiles;
+  base.tmap_all = gr.tmaps;
 
   // The grouped row i of every expert GEMM is pair perm[i]; its activation row is X[perm[i] / k],
   // gathered by the GEMM kernels (no permuted copy of X is written).
@@ -405,14 +421,14 @@ moe_status forward_experts(const moe_shape& s, const void* X, const int32_t* exp
   if (!merged(s) && fz) {
     GemmArgs a = base;
     a.N = s.r; a.K = s.m;
-    a.A = X; a.lda = s.m; a.arow = perm; a.arow_div = s.k;
+    a.A = X; a.lda = s.m; a.arow = gr.arow; a.arow_div = gr.arow_div;
     a.B = A_g; a.ldb = s.r; a.bstride = (long)m * r;
     a.C = f.Tgu; a.ldc = s.r; a.scale = c;
     STAGE(ST_FWD_T_GU, gemm_gm_launch(a, LAYOUT_KX, EPI_STORE, 0, s.dtype, Pi, ref, hs));
   } else if (!merged(s)) {
     GemmArgs a = base;
     a.N = s.r; a.K = s.m;
-    a.A = X; a.lda = s.m; a.arow = perm; a.arow_div = s.k;
+    a.A = X; a.lda = s.m; a.arow = gr.arow; a.arow_div = gr.arow_div;
     a.B = A_g; a.Bu = A_u; a.ldb = s.r; a.bstride = (long)m * r;
     a.C = f.Tgu; a.ldc = 2 * s.r; a.cup = s.r; a.scale = c;
     STAGE(ST_FWD_T_GU, gemm_gm_launch(a, LAYOUT_KX, EPI_DUAL, 0, s.dtype, Pi, ref, hs));
@@ -421,7 +437,7 @@ moe_status forward_experts(const moe_shape& s, const void* X, const int32_t* exp
   {
     GemmArgs a = base;
     a.N = s.n; a.K = s.m;
-    a.A = X; a.lda = s.m; a.arow = perm; a.arow_div = s.k;
+    a.A = X; a.lda = s.m; a.arow = gr.arow; a.arow_div = gr.arow_div;
     a.B = W_gu; a.bstride = (long)m * 2 * n;
     if (out_in(s)) {  // W_gu [E, 2n, m]: the up half starts n rows in
       a.Bu = (const char*)W_gu + n * m * esize(s); a.ldb = s.m;
@@ -460,8 +476,9 @@ moe_status forward_experts(const moe_shape& s, const void* X, const int32_t* exp
     a.C = f.Td; a.ldc = s.r; a.scale = c;
     STAGE(ST_FWD_T_D, gemm_gm_launch(a, LAYOUT_KX, EPI_STORE, 0, s.dtype, Pi, ref, hs));
   }
-  // o = h W_d + Tc_d B_d
-  {
+  // o = h W_d + Tc_d B_d  (skipped when no destination is given: a recompute that needs only the
+  // intermediates before it)
+  if (o_dst) {
     GemmArgs a = base;
     a.N = s.m; a.K = s.n;
     a.A = f.h; a.lda = s.n;
@@ -469,7 +486,7 @@ moe_status forward_experts(const moe_shape& s, const void* X, const int32_t* exp
     a.tail = merged(s) ? TAIL_NONE : TAIL_SINGLE; a.r2a = s.r;
     a.TA = f.Td; a.lda2 = s.r;
     a.TB0 = out_in(s) ? ff.Bt_d : B_d; a.ldtb = out_in(s) ? s.r : s.m; a.tbstride = (long)r * m;
-    a.C = f.o; a.ldc = s.m;
+    a.C = o_dst; a.ldc = s.m; a.accum = accum;
     STAGE(ST_FWD_DOWN, gemm_gm_launch(a, out_in(s) ? LAYOUT_XK : LAYOUT_KX, EPI_STORE, 0, s.dtype, Pi, ref,
                                       hs));
   }
@@ -513,8 +530,8 @@ moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t
   fwd_layout(s, inter, &f);
   FwdFactors ff;
   fwd_factor_layout(s, (char*)ws + (saved ? 0 : need_saved), &ff);
-  HIP_TRY_STATUS(forward_experts(s, X, expert_off, perm, rs, W_gu, W_d, A_g, B_g, A_u, B_u, A_d, B_d, f,
-                                 ff, hs));
+  const Grouping gr{s.E, expert_off, perm, s.k, rs.tiles, rs.tmaps};
+  HIP_TRY_STATUS(forward_experts(s, X, gr, W_gu, W_d, A_g, B_g, A_u, B_u, A_d, B_d, f, ff, f.o, 0, hs));
   // combine
   STAGE(ST_FWD_COMBINE, launch_combine(s.dtype, f.o, inv_perm, topk_w, Y, s.s, s.k, s.m, hs));
   return MOE_OK;
@@ -549,6 +566,13 @@ moe_status moe_peft_merge(const moe_shape* shape, const void* W_gu, const void* 
                        (long)n * m, c, hs));
   return MOE_OK;
 }
+
+static moe_status backward_experts(const moe_shape& s, const Grouping& gr, const void* X, const void* dO,
+                                   const void* W_gu, const void* W_d, const void* A_g, const void* B_g,
+                                   const void* A_u, const void* B_u, const void* A_d, const void* B_d,
+                                   const FwdBufs& f, const BwdBufs& b, void* dXp_dst, int accum,
+                                   float* dA_g, float* dB_g, float* dA_u, float* dB_u, float* dA_d,
+                                   float* dB_d, hipStream_t hs);
 
 moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void* X,
                              const void* W_r, const int32_t* topk_idx, const float* topk_w,
@@ -598,6 +622,7 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
   }
   RouteState rs;
   route_layout(s, const_cast<void*>(route_state), &rs);
+  const Grouping gr{s.E, expert_off, perm, s.k, rs.tiles, rs.tmaps};
   FwdBufs f;
   BwdBufs b;
   bwd_layout(s, ws, &b);
@@ -606,16 +631,10 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
     FwdFactors ff;
     fwd_layout(s, rbase, &f);
     fwd_factor_layout(s, rbase + fwd_layout(s, nullptr, nullptr), &ff);
-    HIP_TRY_STATUS(forward_experts(s, X, expert_off, perm, rs, W_gu, W_d, A_g, B_g, A_u, B_u, A_d, B_d,
-                                   f, ff, hs));
+    HIP_TRY_STATUS(forward_experts(s, X, gr, W_gu, W_d, A_g, B_g, A_u, B_u, A_d, B_d, f, ff, f.o, 0, hs));
   } else {
     fwd_layout(s, const_cast<void*>(saved), &f);
   }
-  const int ref = (s.flags & MOE_FLAG_REFERENCE_GEMM) ? 1 : 0;
-  const float c = lora_scale(s);
-  const int Pi = (int)P;
-  const size_t es = esize(s);
-
   // combine backward: dO = s_{t,j} dY_t, ds_{t,j} = dY_t . o_{t,j}
   STAGE(ST_BWD_COMBINE, launch_combine_bwd(s.dtype, dY, f.o, inv_perm, topk_w, b.dO, b.ds, s.s, s.k, s.m, hs));
   // router backward: dz on the selected logits; W_r^T rows for the unpermute
@@ -623,6 +642,29 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
     STAGE(ST_BWD_ROUTER, launch_router_bwd(b.ds, topk_w, rs.psel, s.s, s.k, s.score, s.renormalize, b.dz, hs));
     STAGE(ST_BWD_ROUTER, launch_transpose(s.dtype, W_r, b.WrT, s.m, s.E, 1, hs));
   }
+  HIP_TRY_STATUS(backward_experts(s, gr, X, b.dO, W_gu, W_d, A_g, B_g, A_u, B_u, A_d, B_d, f, b, b.dXp, 0,
+                                  dA_g, dB_g, dA_u, dB_u, dA_d, dB_d, hs));
+  // unpermute: dX[t] = sum_j dXp[inv[t k + j]] (+ sum_j dz[t,j] W_r[:, idx[t,j]])
+  STAGE(ST_BWD_UNPERMUTE, launch_unpermute(s.dtype, b.dXp, inv_perm, s.router_grad ? b.dz : nullptr, topk_idx,
+                           b.WrT, dX, s.s, s.k, s.m, hs));
+  return MOE_OK;
+}
+
+// Backward of the expert MLPs over the grouped rows, from dO (the gradient at the down
+// projection's output, one row per grouped row): the LoRA-factor gradients, and the gradient at
+// the grouped activation rows written to dXp_dst (overwritten, or added to with accum).
+static moe_status backward_experts(const moe_shape& s, const Grouping& gr, const void* X, const void* dO,
+                                   const void* W_gu, const void* W_d, const void* A_g, const void* B_g,
+                                   const void* A_u, const void* B_u, const void* A_d, const void* B_d,
+                                   const FwdBufs& f, const BwdBufs& b, void* dXp_dst, int accum,
+                                   float* dA_g, float* dB_g, float* dA_u, float* dB_u, float* dA_d,
+                                   float* dB_d, hipStream_t hs) {
+  const long P = pairs(s);
+  const size_t m = s.m, n = s.n, r = s.r;
+  const int ref = (s.flags & MOE_FLAG_REFERENCE_GEMM) ? 1 : 0;
+  const float c = lora_scale(s);
+  const int Pi = (int)P;
+  const size_t es = esize(s);
 
   // LoRA-factor gradients (K-grouped launches): an expert longer than one row chunk leaves fp32
   // partials in its launch's region of b.gkpart, and one reduce after the last of them completes all
@@ -639,16 +681,16 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
   };
 
   GemmArgs base = gemm_args();
-  base.G = s.E;
-  base.goff = expert_off;
-  base.toff_all = rs.tiles;
-  base.tmap_all = rs.tmaps;
+  base.G = gr.G;
+  base.goff = gr.off;
+  base.toff_all = gr.tiles;
+  base.tmap_all = gr.tmaps;
 
   // Uc_d = c * dO B_d^T
   {
     GemmArgs a = base;
     a.N = s.r; a.K = s.m;
-    a.A = b.dO; a.lda = s.m;
+    a.A = dO; a.lda = s.m;
     a.B = B_d; a.ldb = s.m; a.bstride = (long)r * m;
     a.C = b.Ud; a.ldc = s.r; a.scale = c;
     STAGE(ST_BWD_U_D, gemm_gm_launch(a, LAYOUT_XK, EPI_STORE, 0, s.dtype, Pi, ref, hs));
@@ -657,7 +699,7 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
   {
     GemmArgs a = base;
     a.N = s.n; a.K = s.m;
-    a.A = b.dO; a.lda = s.m;
+    a.A = dO; a.lda = s.m;
     a.B = W_d; a.ldb = out_in(s) ? s.n : s.m; a.bstride = (long)n * m;
     a.tail = TAIL_SINGLE; a.r2a = s.r;
     a.TA = b.Ud; a.lda2 = s.r;
@@ -683,7 +725,7 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
     gk_prep(a);
     STAGE(ST_BWD_GRAD_D, gemm_gk_launch(a, s.dtype, ref, Pi, hs));
     a.M = s.m; a.N = s.r;
-    a.A = b.dO; a.lda = s.m;
+    a.A = dO; a.lda = s.m;
     a.B = f.Td; a.ldb = s.r;
     a.C = dB_d; a.ldc = s.m; a.cstride = (long)r * m; a.ctrans = 1;
     gk_prep(a);
@@ -726,7 +768,7 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
       a.TB0 = A_g; a.TB1 = fz ? nullptr : A_u; a.ldtb = s.r;
     }
     a.tbstride = (long)m * r;
-    a.C = b.dXp; a.ldc = s.m;
+    a.C = dXp_dst; a.ldc = s.m; a.accum = accum;
     STAGE(ST_BWD_GATE_UP, gemm_gm_launch(a, out_in(s) ? LAYOUT_KX : LAYOUT_XK, EPI_STORE, 0, s.dtype, Pi, ref,
                                          hs));
   }
@@ -734,7 +776,7 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
   if (fz) {  // dA = Xp^T Uc ;  dB = Tc^T [dg | du]
     GemmArgs a = base;
     a.M = s.m; a.N = s.r;
-    a.A = X; a.lda = s.m; a.arow = perm; a.arow_div = s.k;
+    a.A = X; a.lda = s.m; a.arow = gr.arow; a.arow_div = gr.arow_div;
     a.B = b.Ugu; a.ldb = s.r;
     a.C = dA_g; a.ldc = s.r; a.cstride = (long)m * r;
     gk_prep(a);
@@ -750,7 +792,7 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
   } else {
     GemmArgs a = base;
     a.M = s.m; a.N = 2 * s.r;
-    a.A = X; a.lda = s.m; a.arow = perm; a.arow_div = s.k;
+    a.A = X; a.lda = s.m; a.arow = gr.arow; a.arow_div = gr.arow_div;
     a.B = b.Ugu; a.ldb = 2 * s.r;
     a.C = dA_g; a.C1 = dA_u; a.nsplit = s.r; a.ldc = s.r; a.cstride = (long)m * r;
     gk_prep(a);
@@ -769,11 +811,9 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
     STAGE(ST_BWD_GRAD_GU, gemm_gk_launch(bg, s.dtype, ref, Pi, hs));
     if (n_gk) STAGE(ST_BWD_GRAD_GU, gemm_gk_reduce(gk_jobs, n_gk, Pi, hs));
   }
-  // unpermute: dX[t] = sum_j dXp[inv[t k + j]] (+ sum_j dz[t,j] W_r[:, idx[t,j]])
-  STAGE(ST_BWD_UNPERMUTE, launch_unpermute(s.dtype, b.dXp, inv_perm, s.router_grad ? b.dz : nullptr, topk_idx,
-                           b.WrT, dX, s.s, s.k, s.m, hs));
   return MOE_OK;
 }
+
 
 moe_status moe_timing_enable(int32_t on) {
   std::lock_guard<std::mutex> lk(g_timing.mu);
@@ -810,6 +850,152 @@ moe_status moe_timing_read(double* total_ms, int64_t* counts, int32_t nstages) {
     g_timing.count[i] = 0;
   }
   return st;
+}
+
+
+// ---------------------------------------------------------------- shared expert
+// A dense SwiGLU expert with its own Split-LoRA pairs, applied to every token and added to the
+// routed layer's output. Internally one group of s rows (E = 1, k = 1, no gather, no combine).
+
+static moe_status shared_shape(const moe_shape* sp, moe_shape* out) {
+  if (!sp) return MOE_ERR_INVALID_ARG;
+  moe_shape c = *sp;
+  // E, k and the router fields do not apply; check the rest under a valid routed stand-in
+  c.E = 8;
+  c.k = 1;
+  c.score = MOE_SCORE_SOFTMAX;
+  c.renormalize = 1;
+  c.router_grad = 0;
+  const moe_status st = check_shape(&c);
+  if (st != MOE_OK) return st;
+  if (merged(c)) return MOE_ERR_UNSUPPORTED;
+  c.E = 1;
+  *out = c;
+  return MOE_OK;
+}
+
+// off [2], the tile tables [kNumTileSizes][2] and the row tile -> group maps of the single group
+static size_t one_group_layout(const moe_shape& sh, void* base, Grouping* gr) {
+  Carve c(base);
+  int* off = c.take<int>(2);
+  int* tiles = c.take<int>((size_t)kNumTileSizes * 2);
+  int* tmaps = c.take<int>((size_t)tile_map_offset(kNumTileSizes, sh.s, 1));
+  if (gr) *gr = Grouping{1, off, nullptr, 1, tiles, tmaps};
+  return align_up(c.off, 256);
+}
+
+size_t moe_shared_saved_bytes(const moe_shape* shape) {
+  moe_shape sh;
+  if (shared_shape(shape, &sh) != MOE_OK) return 0;
+  return fwd_layout(sh, nullptr, nullptr, false);
+}
+
+size_t moe_shared_fwd_ws_bytes(const moe_shape* shape, int32_t with_saved) {
+  moe_shape sh;
+  if (shared_shape(shape, &sh) != MOE_OK) return 0;
+  return one_group_layout(sh, nullptr, nullptr) + fwd_factor_layout(sh, nullptr, nullptr) +
+         (with_saved ? 0 : fwd_layout(sh, nullptr, nullptr, false));
+}
+
+size_t moe_shared_bwd_ws_bytes(const moe_shape* shape) {
+  moe_shape sh;
+  if (shared_shape(shape, &sh) != MOE_OK) return 0;
+  return one_group_layout(sh, nullptr, nullptr) + bwd_layout(sh, nullptr, nullptr, false) +
+         recompute_bytes(sh, false);
+}
+
+moe_status moe_shared_forward(const moe_shape* shape, const void* X, const void* W_gu, const void* W_d,
+                              const void* A_g, const void* B_g, const void* A_u, const void* B_u,
+                              const void* A_d, const void* B_d, void* Y, void* saved, size_t saved_bytes,
+                              void* ws, size_t ws_bytes, void* stream) {
+  moe_shape s;
+  moe_status st = shared_shape(shape, &s);
+  if (st != MOE_OK) return st;
+  const size_t m = s.m, n = s.n;
+  if (!ptr_ok(X, (size_t)s.s * m) || !ptr_ok(W_gu, m * 2 * n) || !ptr_ok(W_d, n * m) ||
+      !lora_ptrs_ok(s, A_g, B_g, A_u, B_u, A_d, B_d) || !ptr_ok(Y, (size_t)s.s * m))
+    return MOE_ERR_INVALID_ARG;
+  const size_t need_tab = one_group_layout(s, nullptr, nullptr);
+  const size_t need_saved = fwd_layout(s, nullptr, nullptr, false);
+  const size_t need_fac = fwd_factor_layout(s, nullptr, nullptr);
+  const size_t need_ws = need_tab + need_fac + (saved ? 0 : need_saved);
+  if (saved) {
+    if ((uintptr_t)saved & 255u) return MOE_ERR_INVALID_ARG;
+    if (saved_bytes < need_saved) return MOE_ERR_WORKSPACE;
+  }
+  if (ws_bytes < need_ws) return MOE_ERR_WORKSPACE;
+  if (!ws || ((uintptr_t)ws & 255u)) return MOE_ERR_INVALID_ARG;
+  if (s.s == 0) return MOE_OK;
+  hipStream_t hs = (hipStream_t)stream;
+  Grouping gr;
+  one_group_layout(s, ws, &gr);
+  HIP_TRY(launch_one_group_tables(s.s, const_cast<int*>(gr.off), const_cast<int*>(gr.tiles),
+                                  const_cast<int*>(gr.tmaps), hs));
+  FwdFactors ff;
+  fwd_factor_layout(s, (char*)ws + need_tab, &ff);
+  FwdBufs f;
+  fwd_layout(s, saved ? saved : (char*)ws + need_tab + need_fac, &f, false);
+  return forward_experts(s, X, gr, W_gu, W_d, A_g, B_g, A_u, B_u, A_d, B_d, f, ff, Y, 1, hs);
+}
+
+moe_status moe_shared_backward(const moe_shape* shape, const void* dY, const void* X, const void* W_gu,
+                               const void* W_d, const void* A_g, const void* B_g, const void* A_u,
+                               const void* B_u, const void* A_d, const void* B_d, const void* saved,
+                               size_t saved_bytes, void* dX, float* dA_g, float* dB_g, float* dA_u,
+                               float* dB_u, float* dA_d, float* dB_d, void* ws, size_t ws_bytes,
+                               void* stream) {
+  moe_shape s;
+  moe_status st = shared_shape(shape, &s);
+  if (st != MOE_OK) return st;
+  const size_t m = s.m, n = s.n, r = s.r;
+  const bool fz = fused_gu(s);
+  if (!ptr_ok(dY, (size_t)s.s * m) || !ptr_ok(X, (size_t)s.s * m) || !ptr_ok(W_gu, m * 2 * n) ||
+      !ptr_ok(W_d, n * m) || !lora_ptrs_ok(s, A_g, B_g, A_u, B_u, A_d, B_d) ||
+      !ptr_ok(dX, (size_t)s.s * m) || !ptr_ok(dA_g, m * r) || !ptr_ok(dB_g, r * n * (fz ? 2 : 1)) ||
+      (!fz && (!ptr_ok(dA_u, m * r) || !ptr_ok(dB_u, r * n))) || !ptr_ok(dA_d, n * r) ||
+      !ptr_ok(dB_d, r * m))
+    return MOE_ERR_INVALID_ARG;
+  const bool redo = !saved;
+  if (redo && !recompute(s)) return MOE_ERR_INVALID_ARG;
+  if (saved && ((uintptr_t)saved & 255u)) return MOE_ERR_INVALID_ARG;
+  if (saved && saved_bytes < fwd_layout(s, nullptr, nullptr, false)) return MOE_ERR_WORKSPACE;
+  const size_t need_tab = one_group_layout(s, nullptr, nullptr);
+  const size_t bwd_bytes = bwd_layout(s, nullptr, nullptr, false);
+  const size_t need_ws = need_tab + bwd_bytes + (redo ? recompute_bytes(s, false) : 0);
+  if (ws_bytes < need_ws) return MOE_ERR_WORKSPACE;
+  if (!ws || ((uintptr_t)ws & 255u)) return MOE_ERR_INVALID_ARG;
+  hipStream_t hs = (hipStream_t)stream;
+  if (s.s == 0) {  // no rows: zero gradients, dX unchanged
+    HIP_TRY(launch_zero(dA_g, m * r, hs));
+    HIP_TRY(launch_zero(dB_g, r * n * (fz ? 2 : 1), hs));
+    if (!fz) {
+      HIP_TRY(launch_zero(dA_u, m * r, hs));
+      HIP_TRY(launch_zero(dB_u, r * n, hs));
+    }
+    HIP_TRY(launch_zero(dA_d, n * r, hs));
+    HIP_TRY(launch_zero(dB_d, r * m, hs));
+    return MOE_OK;
+  }
+  Grouping gr;
+  one_group_layout(s, ws, &gr);
+  HIP_TRY(launch_one_group_tables(s.s, const_cast<int*>(gr.off), const_cast<int*>(gr.tiles),
+                                  const_cast<int*>(gr.tmaps), hs));
+  BwdBufs b;
+  bwd_layout(s, (char*)ws + need_tab, &b, false);
+  FwdBufs f;
+  if (redo) {
+    char* rbase = (char*)ws + need_tab + bwd_bytes;
+    FwdFactors ff;
+    fwd_layout(s, rbase, &f, false);
+    fwd_factor_layout(s, rbase + fwd_layout(s, nullptr, nullptr, false), &ff);
+    // the recomputed down projection output is not needed: it goes to the scratch gradient rows
+    HIP_TRY_STATUS(forward_experts(s, X, gr, W_gu, W_d, A_g, B_g, A_u, B_u, A_d, B_d, f, ff, nullptr, 0, hs));
+  } else {
+    fwd_layout(s, const_cast<void*>(saved), &f, false);
+  }
+  // dO = dY (weight 1, no permutation); dX += the expert's input gradient
+  return backward_experts(s, gr, X, dY, W_gu, W_d, A_g, B_g, A_u, B_u, A_d, B_d, f, b, dX, 1, dA_g, dB_g,
+                          dA_u, dB_u, dA_d, dB_d, hs);
 }
 
 }  // extern "C"

@@ -73,6 +73,8 @@ struct GemmArgs {
   float scale;
   const float* bias; // EPI_STORE: per-column bias (fp32) or nullptr; added by K split 0 only
   int kchunk;        // GM without groups or tail: gridDim.y K splits of kchunk each (0: one split)
+  int accum;         // GM, EPI_STORE, deep-prefetch and reference kernels: C += result instead of C =
+                     //   (the other kernels reject it)
   long csplit;       //   elements between the outputs of consecutive K splits
   void* H;           // EPI_SWIGLU: silu(gate)*up output
   long ldh;

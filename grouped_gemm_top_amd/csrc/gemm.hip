@@ -825,8 +825,10 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
         float f[8];
         rd8(r, c8, f);
         if constexpr (EPI == EPI_STORE) {
+          float prev[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+          if (a.accum) unpack8(ld16(GCHK(C + (long)grow * a.ldc + gcol, 16)), prev);
 #pragma unroll
-          for (int j = 0; j < 8; j++) f[j] = a.scale * f[j] + (a.bias ? a.bias[gcol + j] : 0.0f);
+          for (int j = 0; j < 8; j++) f[j] = a.scale * f[j] + (a.bias ? a.bias[gcol + j] : 0.0f) + prev[j];
           *reinterpret_cast<i32x4_t*>(GCHK(C + (long)grow * a.ldc + gcol, 16)) = pack8(f);
         } else {  // EPI_SWIGLU_BWD: f = dh; dg = dh u s (1 + g (1 - s)), du = dh silu(g)
           float g[8], uu[8], dg[8], du[8];
@@ -1069,7 +1071,8 @@ __global__ void gm_simt(GemmArgs a, int b_layout, int total_rows_bound) {
   }
   OutT* C = (OutT*)a.C;
   if (EPI == EPI_STORE) {
-    C[(long)row * a.ldc + jj] = from_f<OutT>(a.scale * acc0 + (a.bias ? a.bias[jj] : 0.0f));
+    const float prev = a.accum ? to_f(C[(long)row * a.ldc + jj]) : 0.0f;
+    C[(long)row * a.ldc + jj] = from_f<OutT>(a.scale * acc0 + (a.bias ? a.bias[jj] : 0.0f) + prev);
   } else if (EPI == EPI_DUAL) {
     C[(long)row * a.ldc + jj] = from_f<OutT>(a.scale * acc0);
     C[(long)row * a.ldc + a.cup + jj] = from_f<OutT>(a.scale * acc1);
@@ -1117,6 +1120,7 @@ struct TileCfg {
 
 template <typename Cfg, int BL, int EPI, typename OutT, bool TAIL>
 hipError_t launch_gm_mfma_t(const GemmArgs& a, int rows_bound, hipStream_t stream) {
+  if (a.accum) return hipErrorInvalidValue;
   constexpr bool DUAL = (EPI == EPI_DUAL || EPI == EPI_SWIGLU);
   constexpr int BNH = DUAL ? Cfg::BN / 2 : Cfg::BN;
   auto kern = gm_mfma<Cfg::WM, Cfg::WN, Cfg::TM, Cfg::TN, Cfg::BKT, Cfg::S, BL, EPI, OutT, TAIL>;

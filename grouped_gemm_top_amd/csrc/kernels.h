@@ -18,6 +18,9 @@ hipError_t launch_hist_rank(const int* idx, int s, int k, int E, int* blk_hist, 
 // Expert offsets, per-block bases and row-tile tables from the block histograms (one workgroup).
 hipError_t launch_scan(const int* blk_hist, int nb, int E, int P, int* blk_base, int* off,
                        int* tile_tables, int* tile_maps, hipStream_t st);
+// The tables of a single group of `rows` rows (a dense expert applied to every token): off = [0, rows],
+// the row-tile tables of launch_scan for G = 1, and zeroed row tile -> group maps.
+hipError_t launch_one_group_tables(int rows, int* off, int* tile_tables, int* tile_maps, hipStream_t st);
 // perm / inv / row token from the bases and ranks.
 hipError_t launch_scatter(const int* idx, const int* rank, const int* blk_base, int s, int k, int E,
                           int* perm, int* inv, int* row_tok, hipStream_t st);

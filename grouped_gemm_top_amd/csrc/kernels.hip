@@ -509,6 +509,23 @@ __global__ __launch_bounds__(256) void merge_xk_kernel(const T* __restrict__ W, 
   Wo[off] = from_f<T>(to_f(W[off]) + c * acc);
 }
 
+__global__ void one_group_tables_kernel(int rows, int* off, int* tiles, int* maps, long nmaps) {
+  const int t = threadIdx.x;
+  if (blockIdx.x == 0) {
+    if (t == 0) {
+      off[0] = 0;
+      off[1] = rows;
+    }
+    if (t < kNumTileSizes) {
+      const int bm = kTileSizes[t];
+      const int n = (rows + bm - 1) / bm;
+      tiles[t * 2] = 0;
+      tiles[t * 2 + 1] = t == kGkChunkTable ? max(1, n) : n;  // as launch_scan: >= 1 chunk per group
+    }
+  }
+  for (long i = (long)blockIdx.x * blockDim.x + t; i < nmaps; i += (long)gridDim.x * blockDim.x) maps[i] = 0;
+}
+
 __global__ void zero_kernel(int* p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
     p[i] = 0;
@@ -606,6 +623,14 @@ hipError_t launch_unpermute(int dtype, const void* dXp, const int* inv, const fl
   else
     hipLaunchKernelGGL(unpermute_kernel<float>, dim3(s), dim3(256), 0, st, (const float*)dXp, inv, dz,
                        idx, (const float*)WrT, (float*)dX, k, m);
+  return hipGetLastError();
+}
+
+hipError_t launch_one_group_tables(int rows, int* off, int* tile_tables, int* tile_maps, hipStream_t st) {
+  const long nmaps = tile_map_offset(kNumTileSizes, rows, 1);
+  const long blocks = std::min<long>((nmaps + 255) / 256, 1024);
+  hipLaunchKernelGGL(one_group_tables_kernel, dim3((unsigned)std::max<long>(blocks, 1)), dim3(256), 0, st, rows,
+                     off, tile_tables, tile_maps, nmaps);
   return hipGetLastError();
 }
 

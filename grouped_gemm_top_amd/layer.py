@@ -1,4 +1,4 @@
-"""Buffer allocation around the three C-ABI calls (torch provides device memory and the stream).
+"""Buffer allocation around the C-ABI calls (torch provides device memory and the stream).
 
 Nothing here computes any part of the layer: each helper allocates the output and scratch
 tensors the C ABI expects and makes one call into libmoelora.
@@ -8,9 +8,12 @@ from __future__ import annotations
 import torch
 
 from . import (make_shape, moe_bwd_ws_bytes, moe_fwd_saved_bytes, moe_fwd_ws_bytes,
-               moe_lora_backward, moe_lora_forward, moe_route, moe_route_state_bytes)
+               moe_lora_backward, moe_lora_forward, moe_route, moe_route_state_bytes,
+               moe_shared_backward, moe_shared_bwd_ws_bytes, moe_shared_forward,
+               moe_shared_fwd_ws_bytes, moe_shared_saved_bytes)
 
-__all__ = ["shape_of", "alloc_route", "route", "forward", "backward", "alloc_grads"]
+__all__ = ["shape_of", "alloc_route", "route", "forward", "backward", "alloc_grads", "shared_forward",
+           "shared_grads", "shared_backward"]
 
 
 def shape_of(cfg, router_grad=True, flags=0, s=None):
@@ -88,3 +91,41 @@ def backward(shape, dY, X, W_r, rt, W, saved, dX=None, grads=None, ws=None, stre
                       grads["dA_g"], grads["dB_g"], grads["dA_u"], grads["dB_u"], grads["dA_d"],
                       grads["dB_d"], ws, stream)
     return dX, grads
+
+
+def shared_forward(shape, X, W, Y, training=True, saved=None, ws=None, stream=None):
+    """Y += the shared expert's output (W: W_gu [m, 2n], W_d [n, m] and the LoRA factors of one
+    expert). Returns the saved buffer (None when not training)."""
+    dev = X.device
+    if training and saved is None:
+        saved = _bytes(moe_shared_saved_bytes(shape), dev)
+    if ws is None:
+        ws = _bytes(moe_shared_fwd_ws_bytes(shape, saved is not None), dev)
+    moe_shared_forward(shape, X, W["W_gu"], W["W_d"], W["A_g"], W["B_g"], W.get("A_u"), W.get("B_u"),
+                       W["A_d"], W["B_d"], Y, saved, ws, stream)
+    return saved
+
+
+def shared_grads(shape, device) -> dict:
+    """Gradient buffers of the shared expert's LoRA factors (fp32)."""
+    m, n, r = shape.m, shape.n, shape.r
+    f = dict(dtype=torch.float32, device=device)
+    if shape.flags & 32:  # MOE_FLAG_FUSED_GU_LORA
+        return {"dA_g": torch.empty(m, r, **f), "dB_g": torch.empty(r, 2 * n, **f), "dA_u": None,
+                "dB_u": None, "dA_d": torch.empty(n, r, **f), "dB_d": torch.empty(r, m, **f)}
+    return {"dA_g": torch.empty(m, r, **f), "dB_g": torch.empty(r, n, **f),
+            "dA_u": torch.empty(m, r, **f), "dB_u": torch.empty(r, n, **f),
+            "dA_d": torch.empty(n, r, **f), "dB_d": torch.empty(r, m, **f)}
+
+
+def shared_backward(shape, dY, X, W, saved, dX, grads=None, ws=None, stream=None):
+    """dX += the shared expert's input gradient; returns the LoRA-factor gradients."""
+    dev = X.device
+    if grads is None:
+        grads = shared_grads(shape, dev)
+    if ws is None:
+        ws = _bytes(moe_shared_bwd_ws_bytes(shape), dev)
+    moe_shared_backward(shape, dY, X, W["W_gu"], W["W_d"], W["A_g"], W["B_g"], W.get("A_u"),
+                        W.get("B_u"), W["A_d"], W["B_d"], saved, dX, grads["dA_g"], grads["dB_g"],
+                        grads["dA_u"], grads["dB_u"], grads["dA_d"], grads["dB_d"], ws, stream)
+    return grads

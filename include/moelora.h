@@ -188,6 +188,42 @@ moe_status moe_peft_merge(const moe_shape* shape, const void* W_gu, const void* 
                           const void* B_d, void* W_gu_merged, void* W_d_merged, void* stream);
 
 /*
+ * Shared expert -- a dense SwiGLU expert that every token passes through, beside the routed ones,
+ * with its output added to theirs (the DeepSeek-MoE-style layer of GLM 4.7 Flash: 64 routed experts
+ * and 1 shared expert; unsloth.ai "Faster MoE" page, section "GLM 4.7 Benchmarks"). Its three
+ * projections carry their own Split-LoRA pairs:
+ *     [g | u] = X W_gu + c [(X A_g) B_g | (X A_u) B_u],  h = silu(g) * u,
+ *     Y += h W_d + c (h A_d) B_d
+ * shape: s, m, n (the shared expert's intermediate size), r, alpha, dtype and the flags RSLORA,
+ * WEIGHTS_OUT_IN, FUSED_GU_LORA, RECOMPUTE, REFERENCE_GEMM apply; E, k, score, renormalize and
+ * router_grad are not read. MERGED is MOE_ERR_UNSUPPORTED. Weights are those of one expert:
+ * W_gu [m, 2n], W_d [n, m] (or output-major), A_g, A_u [m, r], B_g, B_u [r, n], A_d [n, r],
+ * B_d [r, m] (fused gate/up pair: A [m, r] in A_g, B [r, 2n] in B_g).
+ *
+ * moe_shared_forward: Y [s, m] += the expert's output (call it on the Y of moe_lora_forward).
+ *     saved (>= moe_shared_saved_bytes, 256-byte aligned) keeps gu, h and the low-rank products for
+ *     the backward; NULL for inference. ws >= moe_shared_fwd_ws_bytes(shape, saved != NULL).
+ * moe_shared_backward: dX [s, m] += the expert's input gradient (call it on the dX of
+ *     moe_lora_backward); dA_*, dB_* (fp32, shaped like the factors) are overwritten. dO = dY.
+ *     saved from moe_shared_forward, or NULL with MOE_FLAG_RECOMPUTE.
+ *     ws >= moe_shared_bwd_ws_bytes. With s == 0 the gradients are zeroed and dX is untouched.
+ * Both are asynchronous on `stream`; errors as for the routed calls (nothing is enqueued).
+ */
+size_t moe_shared_saved_bytes(const moe_shape* shape);
+size_t moe_shared_fwd_ws_bytes(const moe_shape* shape, int32_t with_saved);
+size_t moe_shared_bwd_ws_bytes(const moe_shape* shape);
+moe_status moe_shared_forward(const moe_shape* shape, const void* X, const void* W_gu, const void* W_d,
+                              const void* A_g, const void* B_g, const void* A_u, const void* B_u,
+                              const void* A_d, const void* B_d, void* Y, void* saved, size_t saved_bytes,
+                              void* ws, size_t ws_bytes, void* stream);
+moe_status moe_shared_backward(const moe_shape* shape, const void* dY, const void* X, const void* W_gu,
+                               const void* W_d, const void* A_g, const void* B_g, const void* A_u,
+                               const void* B_u, const void* A_d, const void* B_d, const void* saved,
+                               size_t saved_bytes, void* dX, float* dA_g, float* dB_g, float* dA_u,
+                               float* dB_u, float* dA_d, float* dB_d, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/*
  * Stage timing (diagnostics, off by default). While enabled, every call records a hipEvent pair on
  * its stream around each kernel stage (host-side state in the library; no device memory).
  * moe_timing_read waits for the recorded events, writes per-stage summed milliseconds and counts

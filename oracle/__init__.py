@@ -34,7 +34,7 @@ __all__ = [
     "router_logits", "topk_experts", "routing_weights", "group_by_expert", "route",
     "silu", "expert_rows_forward", "expert_rows_backward", "forward", "router_backward",
     "backward", "forward_tokens", "backward_tokens", "backward_expert", "fused_gate_up_pair",
-    "fused_gate_up_grads",
+    "fused_gate_up_grads", "shared_expert_forward", "shared_expert_backward",
 ]
 
 
@@ -271,6 +271,26 @@ def fused_gate_up_grads(g: dict):
     twice); B's gradient is the column concatenation [dB_g | dB_u].
     """
     return g["dA_g"] + g["dA_u"], np.concatenate([g["dB_g"], g["dB_u"]], axis=-1)
+
+
+def _single_expert(W1: dict) -> dict:
+    return _expert({k: _f64(v)[None] for k, v in W1.items()}, 0)
+
+
+def shared_expert_forward(X, W1: dict, alpha: float, r: int, rslora: bool = False) -> dict:
+    """A shared expert: one SwiGLU expert with Split LoRA that every token passes through, its
+    output added to the routed experts' ([UNS] section "GLM 4.7 Benchmarks": GLM 4.7 Flash has 64
+    routed experts and 1 shared expert, DeepSeek-MoE style). W1 holds one expert's weights
+    (W_gu [m, 2n], W_d [n, m], A_*, B_*). Returns the intermediates; "o" is the contribution to Y.
+    """
+    return expert_rows_forward(X, _single_expert(W1), lora_scale(alpha, r, rslora))
+
+
+def shared_expert_backward(dY, X, W1: dict, alpha: float, r: int, fwd: dict | None = None,
+                           rslora: bool = False) -> dict:
+    """Gradients of the shared expert: its output adds to Y with weight 1, so dO = dY for every
+    token; "dX" is its contribution to the input gradient."""
+    return expert_rows_backward(X, dY, _single_expert(W1), lora_scale(alpha, r, rslora), fwd)
 
 
 def router_backward(ds, rt: dict, W_r, score: str = "softmax", renormalize: bool = True):

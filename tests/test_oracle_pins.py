@@ -391,3 +391,40 @@ def test_fused_gate_up_grads_match_central_finite_differences():
             fd[i] = (lp - lm) / (2 * h)
         assert got.shape == arr.shape
         assert np.max(np.abs(got - fd)) <= 1e-6 * max(np.max(np.abs(fd)), 1e-3)
+
+
+# ------------------------------------------------------------------------------ shared expert
+
+def test_shared_expert_is_the_routed_layer_with_one_expert_and_plain_mlp():
+    """The shared expert equals the routed layer with E = k = 1 (weight 1 for every token), and the
+    textbook SwiGLU MLP on merged weights; its gradients match fp64 central differences."""
+    rng = np.random.default_rng(47)
+    s, m, n, r, alpha = 7, 8, 4, 2, 3.0
+    c = alpha / r
+    X, W_r, W, dY = _rand_layer(rng, s, m, n, 1, 1, r)
+    W1 = {k: v[0] for k, v in W.items()}
+    f = oracle.shared_expert_forward(X, W1, alpha, r)
+    rt = oracle.route(oracle.router_logits(X, W_r), 1, 1)
+    Y, _ = oracle.forward(X, W, rt, alpha, r, keep=False)
+    np.testing.assert_allclose(f["o"], Y, rtol=1e-13, atol=1e-13)
+    Wg, Wu, Wd = _merged(W, 0, c)
+    dense = (_silu(X @ Wg) * (X @ Wu)) @ Wd
+    np.testing.assert_allclose(f["o"], dense, rtol=1e-12, atol=1e-12)
+    g = oracle.shared_expert_backward(dY, X, W1, alpha, r)
+    h = 1e-6
+
+    def loss():
+        return float(np.sum(dY * oracle.shared_expert_forward(X, W1, alpha, r)["o"]))
+
+    for key, arr in (("dX", X), ("dA_g", W1["A_g"]), ("dB_u", W1["B_u"]), ("dA_d", W1["A_d"]),
+                     ("dB_d", W1["B_d"])):
+        fd = np.zeros_like(arr)
+        for i in np.ndindex(arr.shape):
+            old = arr[i]
+            arr[i] = old + h
+            lp = loss()
+            arr[i] = old - h
+            lm = loss()
+            arr[i] = old
+            fd[i] = (lp - lm) / (2 * h)
+        assert np.max(np.abs(g[key] - fd)) <= 1e-6 * max(np.max(np.abs(fd)), 1e-3), key
