@@ -53,11 +53,11 @@ struct FwdBufs {
 };
 
 struct BwdBufs {
-  void* dO;
   float* ds;
   float* dz;
   void* WrT;
   void *Ud, *dgu, *Ugu, *dXp;
+  void *Udw, *Tdw;  // routed rows: w * Uc_d and w * Tc_d (the routing weight of each row's pair)
   float* gkpart;  // partial LoRA-factor gradients of experts longer than one row chunk, one region
                   // per gradient launch (outputs n x r, m x r, m x 2r, n x r, n x r)
   void *At_d, *At_g, *At_u;  // output-major base weights only: A_d, A_g, A_u per expert transposed
@@ -131,13 +131,14 @@ size_t recompute_bytes(const moe_shape& s, bool with_o = true) {
   return recompute(s) ? fwd_layout(s, nullptr, nullptr, with_o) + fwd_factor_layout(s, nullptr, nullptr) : 0;
 }
 
-// routed: the combine/router/unpermute buffers (dO, ds, dz, W_r^T, dXp); a shared expert reads dY
-// as its dO and adds its dX straight into the caller's
+// routed: the router/unpermute buffers (ds, dz, W_r^T, dXp) and the row-weighted low-rank
+// products; a shared expert adds its dX straight into the caller's. Both read dY itself as the
+// gradient at the expert outputs (the routed rows gather it and apply their routing weight), so no
+// dO = w dY rows are written.
 size_t bwd_layout(const moe_shape& s, void* base, BwdBufs* bb, bool routed = true) {
   Carve c(base);
   const size_t P = (size_t)pairs(s), es = esize(s), rt = routed ? 1 : 0;
   BwdBufs b;
-  b.dO = c.bytes(rt * P * s.m * es);
   b.ds = c.take<float>(rt * P);
   b.dz = c.take<float>(rt * P);
   b.WrT = c.bytes(rt * s.E * s.m * es);
@@ -145,6 +146,8 @@ size_t bwd_layout(const moe_shape& s, void* base, BwdBufs* bb, bool routed = tru
   b.dgu = c.bytes(P * 2 * s.n * es);
   b.Ugu = c.bytes(P * 2 * s.r * es);
   b.dXp = c.bytes(rt * P * s.m * es);
+  b.Udw = c.bytes(rt * P * s.r * es);
+  b.Tdw = c.bytes(rt * P * s.r * es);
   b.gkpart = c.take<float>((size_t)gk_part_floats((long)P, s.E, 1, 3L * (s.n + s.m) * s.r));
   const size_t fac = out_in(s) ? 1 : 0;  // the tails then read the factors in the weights' layout
   b.At_d = c.bytes(fac * s.E * s.r * s.n * es);
@@ -375,6 +378,14 @@ moe_status moe_route(const moe_shape* shape, const void* X, const void* W_r,
 // GEMM with its SwiGLU epilogue and the down GEMM, writing gu, h, Tc_gu, Tc_d and o into f (ff:
 // transposed tail factors for output-major weights). Shared by the forward and by a backward that
 // recomputes them.
+// Routed rows' view of dY: grouped row i holds pair p = pair[i] of token p / k, with weight w[p]; the
+// gradient at its expert output is w[p] dY[p / k].
+struct RowWeights {
+  const int32_t* pair;
+  int k;
+  const float* w;
+};
+
 // Row grouping of the expert GEMMs: G groups of rows (off[G + 1]); grouped row i reads activation
 // row arow[i] / arow_div of X (arow == nullptr: row i), with the row-tile tables of launch_scan.
 struct Grouping {
@@ -568,7 +579,8 @@ moe_status moe_peft_merge(const moe_shape* shape, const void* W_gu, const void* 
 }
 
 static moe_status backward_experts(const moe_shape& s, const Grouping& gr, const void* X, const void* dO,
-                                   const void* W_gu, const void* W_d, const void* A_g, const void* B_g,
+                                   const RowWeights* rw, const void* W_gu, const void* W_d, const void* A_g,
+                                   const void* B_g,
                                    const void* A_u, const void* B_u, const void* A_d, const void* B_d,
                                    const FwdBufs& f, const BwdBufs& b, void* dXp_dst, int accum,
                                    float* dA_g, float* dB_g, float* dA_u, float* dB_u, float* dA_d,
@@ -635,14 +647,17 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
   } else {
     fwd_layout(s, const_cast<void*>(saved), &f);
   }
-  // combine backward: dO = s_{t,j} dY_t, ds_{t,j} = dY_t . o_{t,j}
-  STAGE(ST_BWD_COMBINE, launch_combine_bwd(s.dtype, dY, f.o, inv_perm, topk_w, b.dO, b.ds, s.s, s.k, s.m, hs));
-  // router backward: dz on the selected logits; W_r^T rows for the unpermute
+  // router backward: ds_{t,j} = dY_t . o_{t,j} (the combine's gradient in the routing weights), then
+  // dz on the selected logits; W_r^T rows for the unpermute. The gradient at the expert outputs,
+  // dO = s_{t,j} dY_t, is never written: the expert GEMMs gather dY rows and apply s_{t,j}.
   if (s.router_grad) {
+    STAGE(ST_BWD_COMBINE, launch_combine_bwd(s.dtype, dY, f.o, inv_perm, topk_w, nullptr, b.ds, s.s, s.k, s.m,
+                                             hs));
     STAGE(ST_BWD_ROUTER, launch_router_bwd(b.ds, topk_w, rs.psel, s.s, s.k, s.score, s.renormalize, b.dz, hs));
     STAGE(ST_BWD_ROUTER, launch_transpose(s.dtype, W_r, b.WrT, s.m, s.E, 1, hs));
   }
-  HIP_TRY_STATUS(backward_experts(s, gr, X, b.dO, W_gu, W_d, A_g, B_g, A_u, B_u, A_d, B_d, f, b, b.dXp, 0,
+  const RowWeights rw{perm, s.k, topk_w};
+  HIP_TRY_STATUS(backward_experts(s, gr, X, dY, &rw, W_gu, W_d, A_g, B_g, A_u, B_u, A_d, B_d, f, b, b.dXp, 0,
                                   dA_g, dB_g, dA_u, dB_u, dA_d, dB_d, hs));
   // unpermute: dX[t] = sum_j dXp[inv[t k + j]] (+ sum_j dz[t,j] W_r[:, idx[t,j]])
   STAGE(ST_BWD_UNPERMUTE, launch_unpermute(s.dtype, b.dXp, inv_perm, s.router_grad ? b.dz : nullptr, topk_idx,
@@ -650,11 +665,13 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
   return MOE_OK;
 }
 
-// Backward of the expert MLPs over the grouped rows, from dO (the gradient at the down
-// projection's output, one row per grouped row): the LoRA-factor gradients, and the gradient at
-// the grouped activation rows written to dXp_dst (overwritten, or added to with accum).
+// Backward of the expert MLPs over the grouped rows, from dO, the gradient at the down projection's
+// output: one row per grouped row, or with rw the rows of dY that rw maps each grouped row to, times
+// the row's weight. Computes the LoRA-factor gradients, and the gradient at the grouped activation
+// rows written to dXp_dst (overwritten, or added to with accum).
 static moe_status backward_experts(const moe_shape& s, const Grouping& gr, const void* X, const void* dO,
-                                   const void* W_gu, const void* W_d, const void* A_g, const void* B_g,
+                                   const RowWeights* rw, const void* W_gu, const void* W_d, const void* A_g,
+                                   const void* B_g,
                                    const void* A_u, const void* B_u, const void* A_d, const void* B_d,
                                    const FwdBufs& f, const BwdBufs& b, void* dXp_dst, int accum,
                                    float* dA_g, float* dB_g, float* dA_u, float* dB_u, float* dA_d,
@@ -686,20 +703,24 @@ static moe_status backward_experts(const moe_shape& s, const Grouping& gr, const
   base.toff_all = gr.tiles;
   base.tmap_all = gr.tmaps;
 
-  // Uc_d = c * dO B_d^T
+  // Uc_d = c * dO B_d^T. Routed rows: the product of the gathered dY rows without the weight (for the
+  // down projection's tail, whose output is weighted as a whole), and w * that in b.Udw (for dA_d).
   {
     GemmArgs a = base;
     a.N = s.r; a.K = s.m;
     a.A = dO; a.lda = s.m;
+    if (rw) { a.arow = rw->pair; a.arow_div = rw->k; a.wval = rw->w; a.C2 = b.Udw; }
     a.B = B_d; a.ldb = s.m; a.bstride = (long)r * m;
     a.C = b.Ud; a.ldc = s.r; a.scale = c;
     STAGE(ST_BWD_U_D, gemm_gm_launch(a, LAYOUT_XK, EPI_STORE, 0, s.dtype, Pi, ref, hs));
   }
-  // dh = dO W_d^T + Uc_d A_d^T, then SwiGLU backward -> dgu = [dg | du]
+  // dh = dO W_d^T + Uc_d A_d^T, then SwiGLU backward -> dgu = [dg | du]. Routed rows:
+  // dh = w (dY W_d^T + Uc A_d^T) from the gathered dY rows.
   {
     GemmArgs a = base;
     a.N = s.n; a.K = s.m;
     a.A = dO; a.lda = s.m;
+    if (rw) { a.arow = rw->pair; a.arow_div = rw->k; a.wval = rw->w; a.wscale = 1; }
     a.B = W_d; a.ldb = out_in(s) ? s.n : s.m; a.bstride = (long)n * m;
     a.tail = TAIL_SINGLE; a.r2a = s.r;
     a.TA = b.Ud; a.lda2 = s.r;
@@ -715,18 +736,24 @@ static moe_status backward_experts(const moe_shape& s, const Grouping& gr, const
     STAGE(ST_BWD_DOWN, gemm_gm_launch(a, out_in(s) ? LAYOUT_KX : LAYOUT_XK, EPI_SWIGLU_BWD, 0, s.dtype, Pi,
                                       ref, hs));
   }
-  // dA_d = h^T Uc_d ;  dB_d = Tc_d^T dO  (computed as (dO^T Tc_d)^T)
+  // dA_d = h^T Uc_d ;  dB_d = Tc_d^T dO  (computed as (dO^T Tc_d)^T; routed rows: as
+  // (dY_rows^T (w Tc_d))^T)
   {
     GemmArgs a = base;
     a.M = s.n; a.N = s.r;
     a.A = f.h; a.lda = s.n;
-    a.B = b.Ud; a.ldb = s.r;
+    a.B = rw ? b.Udw : b.Ud; a.ldb = s.r;
     a.C = dA_d; a.ldc = s.r; a.cstride = (long)n * r;
     gk_prep(a);
     STAGE(ST_BWD_GRAD_D, gemm_gk_launch(a, s.dtype, ref, Pi, hs));
     a.M = s.m; a.N = s.r;
     a.A = dO; a.lda = s.m;
     a.B = f.Td; a.ldb = s.r;
+    if (rw) {
+      STAGE(ST_BWD_GRAD_D, launch_row_weight(s.dtype, f.Td, rw->pair, rw->w, b.Tdw, P, s.r, hs));
+      a.arow = rw->pair; a.arow_div = rw->k;
+      a.B = b.Tdw;
+    }
     a.C = dB_d; a.ldc = s.m; a.cstride = (long)r * m; a.ctrans = 1;
     gk_prep(a);
     STAGE(ST_BWD_GRAD_D, gemm_gk_launch(a, s.dtype, ref, Pi, hs));
@@ -994,8 +1021,8 @@ moe_status moe_shared_backward(const moe_shape* shape, const void* dY, const voi
     fwd_layout(s, const_cast<void*>(saved), &f, false);
   }
   // dO = dY (weight 1, no permutation); dX += the expert's input gradient
-  return backward_experts(s, gr, X, dY, W_gu, W_d, A_g, B_g, A_u, B_u, A_d, B_d, f, b, dX, 1, dA_g, dB_g,
-                          dA_u, dB_u, dA_d, dB_d, hs);
+  return backward_experts(s, gr, X, dY, nullptr, W_gu, W_d, A_g, B_g, A_u, B_u, A_d, B_d, f, b, dX, 1, dA_g,
+                          dB_g, dA_u, dB_u, dA_d, dB_d, hs);
 }
 
 }  // extern "C"

@@ -75,6 +75,11 @@ struct GemmArgs {
   int kchunk;        // GM without groups or tail: gridDim.y K splits of kchunk each (0: one split)
   int accum;         // GM, EPI_STORE, deep-prefetch and reference kernels: C += result instead of C =
                      //   (the other kernels reject it)
+  // Row weights (deep-prefetch and reference kernels): grouped row i's weight is wval[arow[i]] (the
+  // routing weight of the pair the row holds).
+  const float* wval;
+  void* C2;          // EPI_STORE: also store the row-weighted result here (same layout as C)
+  int wscale;        // EPI_SWIGLU_BWD: dh = row weight * scale * acc before the SwiGLU backward
   long csplit;       //   elements between the outputs of consecutive K splits
   void* H;           // EPI_SWIGLU: silu(gate)*up output
   long ldh;

@@ -830,13 +830,20 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
 #pragma unroll
           for (int j = 0; j < 8; j++) f[j] = a.scale * f[j] + (a.bias ? a.bias[gcol + j] : 0.0f) + prev[j];
           *reinterpret_cast<i32x4_t*>(GCHK(C + (long)grow * a.ldc + gcol, 16)) = pack8(f);
+          if (a.C2) {  // the row-weighted copy
+            const float wr = a.wval[a.arow[grow]];
+#pragma unroll
+            for (int j = 0; j < 8; j++) f[j] *= wr;
+            *reinterpret_cast<i32x4_t*>(GCHK((bf16_t*)a.C2 + (long)grow * a.ldc + gcol, 16)) = pack8(f);
+          }
         } else {  // EPI_SWIGLU_BWD: f = dh; dg = dh u s (1 + g (1 - s)), du = dh silu(g)
           float g[8], uu[8], dg[8], du[8];
           unpack8(gch[i], g);
           unpack8(uch[i], uu);
+          const float sc = a.wscale ? a.scale * a.wval[a.arow[grow]] : a.scale;
 #pragma unroll
           for (int j = 0; j < 8; j++) {
-            const float dh = a.scale * f[j];
+            const float dh = sc * f[j];
             const float sg = 1.0f / (1.0f + __expf(-g[j]));
             dg[j] = dh * uu[j] * sg * (1.0f + g[j] * (1.0f - sg));
             du[j] = dh * g[j] * sg;
@@ -916,17 +923,19 @@ __global__ __launch_bounds__(WM * WN * 64) void gk_mfma(GemmArgs a, const int* t
       for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
   const i32x4_t zero = {0, 0, 0, 0};
 
-  auto gload = [&](int k0) {
+  // Left-operand source rows of a K tile (-1 past the group's end). With a row gather they come
+  // from a.arow, so they are fetched one tile ahead of the data that uses them.
+  auto gidx = [&](int k0, long* src) {
 #pragma unroll
     for (int u = 0; u < A_PT; u++) {
       const int row = k0 + (tid + u * NT) / CPR_A;
-      if (row < ke) {
-        const long src = a.arow ? (long)(a.arow[row] / a.arow_div) : (long)row;
-        ra[u] = ld16((const bf16_t*)a.A + src * a.lda + acol[u]);
-      } else {
-        ra[u] = zero;
-      }
+      src[u] = row < ke ? (a.arow ? (long)(a.arow[row] / a.arow_div) : (long)row) : -1;
     }
+  };
+  auto gload = [&](int k0, const long* src) {
+#pragma unroll
+    for (int u = 0; u < A_PT; u++)
+      ra[u] = src[u] >= 0 ? ld16((const bf16_t*)a.A + src[u] * a.lda + acol[u]) : zero;
 #pragma unroll
     for (int u = 0; u < B_PT; u++) {
       const int row = k0 + (tid + u * NT) / CPR_B;
@@ -966,11 +975,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gk_mfma(GemmArgs a, const int* t
 
   const int nk = (ke - kb + BK - 1) / BK;
   if (nk > 0) {
-    gload(kb);
+    long src[A_PT];
+    gidx(kb, src);
+    gload(kb, src);
+    gidx(kb + BK, src);
     sstore(0);
     __syncthreads();
     for (int kt = 0; kt < nk; kt++) {
-      if (kt + 1 < nk) gload(kb + (kt + 1) * BK);
+      if (kt + 1 < nk) {
+        gload(kb + (kt + 1) * BK, src);
+        gidx(kb + (kt + 2) * BK, src);
+      }
       compute(smem + (kt & 1) * STAGE);
       if (kt + 1 < nk) sstore((kt + 1) & 1);
       __syncthreads();
@@ -1072,7 +1087,9 @@ __global__ void gm_simt(GemmArgs a, int b_layout, int total_rows_bound) {
   OutT* C = (OutT*)a.C;
   if (EPI == EPI_STORE) {
     const float prev = a.accum ? to_f(C[(long)row * a.ldc + jj]) : 0.0f;
-    C[(long)row * a.ldc + jj] = from_f<OutT>(a.scale * acc0 + (a.bias ? a.bias[jj] : 0.0f) + prev);
+    const float v = a.scale * acc0 + (a.bias ? a.bias[jj] : 0.0f) + prev;
+    C[(long)row * a.ldc + jj] = from_f<OutT>(v);
+    if (a.C2) ((OutT*)a.C2)[(long)row * a.ldc + jj] = from_f<OutT>(a.wval[a.arow[row]] * v);
   } else if (EPI == EPI_DUAL) {
     C[(long)row * a.ldc + jj] = from_f<OutT>(a.scale * acc0);
     C[(long)row * a.ldc + a.cup + jj] = from_f<OutT>(a.scale * acc1);
@@ -1082,7 +1099,7 @@ __global__ void gm_simt(GemmArgs a, int b_layout, int total_rows_bound) {
     ((OutT*)a.H)[(long)row * a.ldh + jj] = from_f<OutT>(acc0 / (1.0f + expf(-acc0)) * acc1);
   } else {
     const OutT* GU = (const OutT*)a.GU;
-    const float dh = a.scale * acc0;
+    const float dh = (a.wscale ? a.scale * a.wval[a.arow[row]] : a.scale) * acc0;
     const float g = to_f(GU[(long)row * a.ldgu + jj]);
     const float uu = to_f(GU[(long)row * a.ldgu + a.guup + jj]);
     const float sg = 1.0f / (1.0f + expf(-g));
@@ -1120,7 +1137,7 @@ struct TileCfg {
 
 template <typename Cfg, int BL, int EPI, typename OutT, bool TAIL>
 hipError_t launch_gm_mfma_t(const GemmArgs& a, int rows_bound, hipStream_t stream) {
-  if (a.accum) return hipErrorInvalidValue;
+  if (a.accum || a.C2 || a.wscale) return hipErrorInvalidValue;
   constexpr bool DUAL = (EPI == EPI_DUAL || EPI == EPI_SWIGLU);
   constexpr int BNH = DUAL ? Cfg::BN / 2 : Cfg::BN;
   auto kern = gm_mfma<Cfg::WM, Cfg::WN, Cfg::TM, Cfg::TN, Cfg::BKT, Cfg::S, BL, EPI, OutT, TAIL>;

@@ -28,8 +28,8 @@ hipError_t launch_scatter(const int* idx, const int* rank, const int* blk_base, 
 // Y[t] = sum_j w[t,j] o[inv[t k + j]] (fp32 accumulate, slot order).
 hipError_t launch_combine(int dtype, const void* o, const int* inv, const float* w, void* Y, int s,
                           int k, int m, hipStream_t st);
-// For each pair p = t k + j (row i = inv[p] of the grouped order): dO[i] = w[p] dY[t],
-// ds[p] = dY[t] . o[i].
+// For each pair p = t k + j (row i = inv[p] of the grouped order): dO[i] = w[p] dY[t] (skipped when
+// dO is null), ds[p] = dY[t] . o[i].
 hipError_t launch_combine_bwd(int dtype, const void* dY, const void* o, const int* inv,
                               const float* w, void* dO, float* ds, int s, int k, int m,
                               hipStream_t st);
@@ -45,6 +45,9 @@ hipError_t launch_unpermute(int dtype, const void* dXp, const int* inv, const fl
                             hipStream_t st);
 // zero-fill n 32-bit words
 hipError_t launch_zero(void* p, size_t words, hipStream_t st);
+// out[i, :] = w[pair[i]] * in[i, :] (rows x cols, rounded to dtype)
+hipError_t launch_row_weight(int dtype, const void* in, const int* pair, const float* w, void* out, long rows,
+                             int cols, hipStream_t st);
 
 // Wo = W + c A B over one projection block of every expert (see merge_kernel): kx selects the
 // x.W orientation (off = i * ld + j + col0) over the output-major one ((j + col0) * ld + i).
