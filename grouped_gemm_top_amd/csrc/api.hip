@@ -74,6 +74,8 @@ inline bool recompute(const moe_shape& s) { return (s.flags & MOE_FLAG_RECOMPUTE
 // one LoRA pair on the fused gate/up projection: A [E, m, r] in A_g, B [E, r, 2n] in B_g
 inline bool fused_gu(const moe_shape& s) { return (s.flags & MOE_FLAG_FUSED_GU_LORA) != 0; }
 inline long pairs(const moe_shape& s) { return (long)s.s * s.k; }
+// ds of a pair arrives as one partial per 64 columns of the expert intermediate (n % 64 == 0)
+inline int ds_parts(const moe_shape& s) { return s.n / 64; }
 inline int nblocks(const moe_shape& s) { return (s.s + kRouteBlockTokens - 1) / kRouteBlockTokens; }
 
 size_t route_layout(const moe_shape& s, void* base, RouteState* rs) {
@@ -139,7 +141,7 @@ size_t bwd_layout(const moe_shape& s, void* base, BwdBufs* bb, bool routed = tru
   Carve c(base);
   const size_t P = (size_t)pairs(s), es = esize(s), rt = routed ? 1 : 0;
   BwdBufs b;
-  b.ds = c.take<float>(rt * P);
+  b.ds = c.take<float>(rt * P * (ds_parts(s) + 1));  // [ds_parts][P] partials, then ds [P]
   b.dz = c.take<float>(rt * P);
   b.WrT = c.bytes(rt * s.E * s.m * es);
   b.Ud = c.bytes(P * s.r * es);
@@ -212,13 +214,13 @@ inline bool lora_ptrs_ok(const moe_shape& s, const void* A_g, const void* B_g, c
 enum Stage {
   ST_ROUTE_LOGITS, ST_ROUTE_TOPK, ST_ROUTE_HIST, ST_ROUTE_SCAN, ST_ROUTE_SCATTER,
   ST_FWD_T_GU, ST_FWD_GATE_UP, ST_FWD_T_D, ST_FWD_DOWN, ST_FWD_COMBINE,
-  ST_BWD_COMBINE, ST_BWD_ROUTER, ST_BWD_U_D, ST_BWD_DOWN, ST_BWD_GRAD_D, ST_BWD_U_GU,
+  ST_BWD_ROUTER, ST_BWD_U_D, ST_BWD_DOWN, ST_BWD_GRAD_D, ST_BWD_U_GU,
   ST_BWD_GATE_UP, ST_BWD_GRAD_GU, ST_BWD_UNPERMUTE, ST_COUNT
 };
 const char* const kStageNames[ST_COUNT] = {
   "route_logits", "route_topk", "route_hist_rank", "route_scan", "route_scatter",
   "fwd_lora_t_gate_up", "fwd_gate_up", "fwd_lora_t_down", "fwd_down", "fwd_combine",
-  "bwd_combine", "bwd_router", "bwd_lora_u_down", "bwd_down", "bwd_lora_grads_down",
+  "bwd_router", "bwd_lora_u_down", "bwd_down", "bwd_lora_grads_down",
   "bwd_lora_u_gate_up", "bwd_gate_up", "bwd_lora_grads_gate_up", "bwd_unpermute"};
 
 struct Timing {
@@ -308,17 +310,22 @@ size_t moe_route_state_bytes(const moe_shape* shape) {
 
 size_t moe_fwd_saved_bytes(const moe_shape* shape) {
   if (check_shape(shape) != MOE_OK) return 0;
-  return fwd_layout(*shape, nullptr, nullptr);
+  return fwd_layout(*shape, nullptr, nullptr, false);
 }
+
+// The expert outputs o are scratch: only the forward's combine reads them (the backward takes ds from
+// the down projection's backward), so they live in the workspace, not in `saved`.
+inline size_t o_bytes(const moe_shape& s) { return align_up((size_t)pairs(s) * s.m * esize(s), 256); }
 
 size_t moe_fwd_ws_bytes(const moe_shape* shape, int32_t with_saved) {
   if (check_shape(shape) != MOE_OK) return 0;
-  return (with_saved ? 0 : fwd_layout(*shape, nullptr, nullptr)) + fwd_factor_layout(*shape, nullptr, nullptr);
+  const moe_shape& s = *shape;
+  return (with_saved ? o_bytes(s) : fwd_layout(s, nullptr, nullptr, true)) + fwd_factor_layout(s, nullptr, nullptr);
 }
 
 size_t moe_bwd_ws_bytes(const moe_shape* shape) {
   if (check_shape(shape) != MOE_OK) return 0;
-  return bwd_layout(*shape, nullptr, nullptr) + recompute_bytes(*shape);
+  return bwd_layout(*shape, nullptr, nullptr) + recompute_bytes(*shape, false);
 }
 
 moe_status moe_route(const moe_shape* shape, const void* X, const void* W_r,
@@ -384,6 +391,7 @@ struct RowWeights {
   const int32_t* pair;
   int k;
   const float* w;
+  float* ds;  // when set: ds partials of every pair, [ds_parts(s)][P] (see moe_lora_backward)
 };
 
 // Row grouping of the expert GEMMs: G groups of rows (off[G + 1]); grouped row i reads activation
@@ -521,15 +529,14 @@ moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t
     return MOE_ERR_INVALID_ARG;
   if (!merged(s) && !lora_ptrs_ok(s, A_g, B_g, A_u, B_u, A_d, B_d)) return MOE_ERR_INVALID_ARG;
   if (!route_state || ((uintptr_t)route_state & 255u)) return MOE_ERR_INVALID_ARG;
-  const size_t need_saved = fwd_layout(s, nullptr, nullptr);
+  // saved: gu, h and the low-rank products; ws: the expert outputs o (and, for inference, the rest)
+  const size_t need_saved = fwd_layout(s, nullptr, nullptr, false);
+  const size_t need_inter = saved ? o_bytes(s) : fwd_layout(s, nullptr, nullptr, true);
   const size_t need_fac = fwd_factor_layout(s, nullptr, nullptr);
-  const size_t need_ws = (saved ? 0 : need_saved) + need_fac;
-  void* inter = saved;
+  const size_t need_ws = need_inter + need_fac;
   if (saved) {
     if ((uintptr_t)saved & 255u) return MOE_ERR_INVALID_ARG;
     if (saved_bytes < need_saved) return MOE_ERR_WORKSPACE;
-  } else {
-    inter = ws;
   }
   if (ws_bytes < need_ws) return MOE_ERR_WORKSPACE;
   if (need_ws && (!ws || ((uintptr_t)ws & 255u))) return MOE_ERR_INVALID_ARG;
@@ -538,9 +545,14 @@ moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t
   RouteState rs;
   route_layout(s, const_cast<void*>(route_state), &rs);
   FwdBufs f;
-  fwd_layout(s, inter, &f);
+  if (saved) {
+    fwd_layout(s, saved, &f, false);
+    f.o = ws;
+  } else {
+    fwd_layout(s, ws, &f, true);
+  }
   FwdFactors ff;
-  fwd_factor_layout(s, (char*)ws + (saved ? 0 : need_saved), &ff);
+  fwd_factor_layout(s, (char*)ws + need_inter, &ff);
   const Grouping gr{s.E, expert_off, perm, s.k, rs.tiles, rs.tmaps};
   HIP_TRY_STATUS(forward_experts(s, X, gr, W_gu, W_d, A_g, B_g, A_u, B_u, A_d, B_d, f, ff, f.o, 0, hs));
   // combine
@@ -615,9 +627,9 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
   const bool redo = !saved;  // recompute the forward's intermediates
   if (redo && !recompute(s)) return MOE_ERR_INVALID_ARG;
   if (saved && ((uintptr_t)saved & 255u)) return MOE_ERR_INVALID_ARG;
-  if (saved && saved_bytes < fwd_layout(s, nullptr, nullptr)) return MOE_ERR_WORKSPACE;
+  if (saved && saved_bytes < fwd_layout(s, nullptr, nullptr, false)) return MOE_ERR_WORKSPACE;
   const size_t bwd_bytes = bwd_layout(s, nullptr, nullptr);
-  const size_t need_ws = bwd_bytes + (redo ? recompute_bytes(s) : 0);
+  const size_t need_ws = bwd_bytes + (redo ? recompute_bytes(s, false) : 0);
   if (ws_bytes < need_ws) return MOE_ERR_WORKSPACE;
   if (!ws || ((uintptr_t)ws & 255u)) return MOE_ERR_INVALID_ARG;
   hipStream_t hs = (hipStream_t)stream;
@@ -641,24 +653,26 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
   if (redo) {
     char* rbase = (char*)ws + bwd_bytes;
     FwdFactors ff;
-    fwd_layout(s, rbase, &f);
-    fwd_factor_layout(s, rbase + fwd_layout(s, nullptr, nullptr), &ff);
-    HIP_TRY_STATUS(forward_experts(s, X, gr, W_gu, W_d, A_g, B_g, A_u, B_u, A_d, B_d, f, ff, f.o, 0, hs));
+    fwd_layout(s, rbase, &f, false);
+    fwd_factor_layout(s, rbase + fwd_layout(s, nullptr, nullptr, false), &ff);
+    // the intermediates only: the backward needs no expert outputs o
+    HIP_TRY_STATUS(forward_experts(s, X, gr, W_gu, W_d, A_g, B_g, A_u, B_u, A_d, B_d, f, ff, nullptr, 0, hs));
   } else {
-    fwd_layout(s, const_cast<void*>(saved), &f);
+    fwd_layout(s, const_cast<void*>(saved), &f, false);
   }
-  // router backward: ds_{t,j} = dY_t . o_{t,j} (the combine's gradient in the routing weights), then
-  // dz on the selected logits; W_r^T rows for the unpermute. The gradient at the expert outputs,
-  // dO = s_{t,j} dY_t, is never written: the expert GEMMs gather dY rows and apply s_{t,j}.
-  if (s.router_grad) {
-    STAGE(ST_BWD_COMBINE, launch_combine_bwd(s.dtype, dY, f.o, inv_perm, topk_w, nullptr, b.ds, s.s, s.k, s.m,
-                                             hs));
-    STAGE(ST_BWD_ROUTER, launch_router_bwd(b.ds, topk_w, rs.psel, s.s, s.k, s.score, s.renormalize, b.dz, hs));
-    STAGE(ST_BWD_ROUTER, launch_transpose(s.dtype, W_r, b.WrT, s.m, s.E, 1, hs));
-  }
-  const RowWeights rw{perm, s.k, topk_w};
+  // The gradient at the expert outputs, dO = s_{t,j} dY_t, is never written: the expert GEMMs gather
+  // dY rows and apply s_{t,j}. The combine's gradient in the routing weights, ds_{t,j} = dY_t . o_{t,j},
+  // equals h . (dY_t W_d^T + Uc A_d^T) for the row's h (o = h W_d + c (h A_d) B_d), so the down
+  // projection's backward leaves it as partials over 64-column blocks (with the router gradient).
+  const RowWeights rw{perm, s.k, topk_w, s.router_grad ? b.ds : nullptr};
   HIP_TRY_STATUS(backward_experts(s, gr, X, dY, &rw, W_gu, W_d, A_g, B_g, A_u, B_u, A_d, B_d, f, b, b.dXp, 0,
                                   dA_g, dB_g, dA_u, dB_u, dA_d, dB_d, hs));
+  // router backward: dz on the selected logits; W_r^T rows for the unpermute
+  if (s.router_grad) {
+    STAGE(ST_BWD_ROUTER, launch_router_bwd(b.ds, ds_parts(s), b.ds + (size_t)ds_parts(s) * P, topk_w, rs.psel,
+                                           s.s, s.k, s.score, s.renormalize, b.dz, hs));
+    STAGE(ST_BWD_ROUTER, launch_transpose(s.dtype, W_r, b.WrT, s.m, s.E, 1, hs));
+  }
   // unpermute: dX[t] = sum_j dXp[inv[t k + j]] (+ sum_j dz[t,j] W_r[:, idx[t,j]])
   STAGE(ST_BWD_UNPERMUTE, launch_unpermute(s.dtype, b.dXp, inv_perm, s.router_grad ? b.dz : nullptr, topk_idx,
                            b.WrT, dX, s.s, s.k, s.m, hs));
@@ -720,7 +734,10 @@ static moe_status backward_experts(const moe_shape& s, const Grouping& gr, const
     GemmArgs a = base;
     a.N = s.n; a.K = s.m;
     a.A = dO; a.lda = s.m;
-    if (rw) { a.arow = rw->pair; a.arow_div = rw->k; a.wval = rw->w; a.wscale = 1; }
+    if (rw) {
+      a.arow = rw->pair; a.arow_div = rw->k; a.wval = rw->w; a.wscale = 1;
+      a.dspart = rw->ds; a.dsstride = P;
+    }
     a.B = W_d; a.ldb = out_in(s) ? s.n : s.m; a.bstride = (long)n * m;
     a.tail = TAIL_SINGLE; a.r2a = s.r;
     a.TA = b.Ud; a.lda2 = s.r;

@@ -80,6 +80,10 @@ struct GemmArgs {
   const float* wval;
   void* C2;          // EPI_STORE: also store the row-weighted result here (same layout as C)
   int wscale;        // EPI_SWIGLU_BWD: dh = row weight * scale * acc before the SwiGLU backward
+  // EPI_SWIGLU_BWD with row weights: partial dot products of scale * acc (dh before the row
+  // weight) with h = silu(g) u, one per 64 output columns: dspart[(col / 64) * dsstride + arow[i]]
+  float* dspart;
+  long dsstride;
   long csplit;       //   elements between the outputs of consecutive K splits
   void* H;           // EPI_SWIGLU: silu(gate)*up output
   long ldh;

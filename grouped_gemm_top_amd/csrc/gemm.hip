@@ -821,6 +821,7 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
       const int q = lane + 64 * i, r = q / CH, c8 = q % CH;
       const int grow = wrow0 + r;
       const int gcol = j0 + wn * WC + 8 * c8;
+      float hdot = 0.0f;  // SwiGLU backward with dspart: this chunk's share of dh . h
       if (grow < row_end && gcol < a.N) {
         float f[8];
         rd8(r, c8, f);
@@ -847,9 +848,20 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
             const float sg = 1.0f / (1.0f + __expf(-g[j]));
             dg[j] = dh * uu[j] * sg * (1.0f + g[j] * (1.0f - sg));
             du[j] = dh * g[j] * sg;
+            hdot += a.scale * f[j] * (g[j] * sg * uu[j]);
           }
           *reinterpret_cast<i32x4_t*>(GCHK(C + (long)grow * a.ldc + gcol, 16)) = pack8(dg);
           *reinterpret_cast<i32x4_t*>(GCHK(C + (long)grow * a.ldc + a.cup + gcol, 16)) = pack8(du);
+        }
+      }
+      if constexpr (EPI == EPI_SWIGLU_BWD && CH == 8) {
+        if (a.dspart) {  // the 8 chunks of staged row r sit in 8 consecutive lanes
+          hdot += __shfl_xor(hdot, 1, 64);
+          hdot += __shfl_xor(hdot, 2, 64);
+          hdot += __shfl_xor(hdot, 4, 64);
+          const int col0 = j0 + wn * WC;
+          if (c8 == 0 && grow < row_end && col0 < a.N)
+            a.dspart[(long)(col0 / 64) * a.dsstride + a.arow[grow]] = hdot;
         }
       }
     }
@@ -1105,6 +1117,10 @@ __global__ void gm_simt(GemmArgs a, int b_layout, int total_rows_bound) {
     const float sg = 1.0f / (1.0f + expf(-g));
     C[(long)row * a.ldc + jj] = from_f<OutT>(dh * uu * sg * (1.0f + g * (1.0f - sg)));
     C[(long)row * a.ldc + a.cup + jj] = from_f<OutT>(dh * g * sg);
+    if (a.dspart) {  // one wave per 64 columns (N is a multiple of 64 here)
+      const float hd = wave_sum(a.scale * acc0 * (g * sg * uu));
+      if (threadIdx.x == 0) a.dspart[(long)blockIdx.y * a.dsstride + a.arow[row]] = hd;
+    }
   }
 }
 

@@ -28,14 +28,10 @@ hipError_t launch_scatter(const int* idx, const int* rank, const int* blk_base, 
 // Y[t] = sum_j w[t,j] o[inv[t k + j]] (fp32 accumulate, slot order).
 hipError_t launch_combine(int dtype, const void* o, const int* inv, const float* w, void* Y, int s,
                           int k, int m, hipStream_t st);
-// For each pair p = t k + j (row i = inv[p] of the grouped order): dO[i] = w[p] dY[t] (skipped when
-// dO is null), ds[p] = dY[t] . o[i].
-hipError_t launch_combine_bwd(int dtype, const void* dY, const void* o, const int* inv,
-                              const float* w, void* dO, float* ds, int s, int k, int m,
-                              hipStream_t st);
-// dz[t, j] from ds, w, p_sel (softmax or sigmoid, renormalised or not).
-hipError_t launch_router_bwd(const float* ds, const float* w, const float* psel, int s, int k,
-                             int score, int renorm, float* dz, hipStream_t st);
+// ds[p] = sum of the partials ds_part[q * s k + p] over q < nparts (in order of q), then dz[t, j]
+// from ds, w, p_sel (softmax or sigmoid, renormalised or not).
+hipError_t launch_router_bwd(const float* ds_part, int nparts, float* ds, const float* w, const float* psel,
+                             int s, int k, int score, int renorm, float* dz, hipStream_t st);
 // WT[b][c, a] = W[b][a, c] for `batch` consecutive rows x cols matrices
 hipError_t launch_transpose(int dtype, const void* W, void* WT, int rows, int cols, int batch,
                             hipStream_t st);

@@ -320,59 +320,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ o, c
 }
 // One block per token: dO[inv[t k + j]] = w[t k + j] dY_t and ds[t k + j] = dY_t . o[inv[t k + j]]
 // for its k pairs, so that dY_t is read once.
-template <typename T>
-__global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ dY, const T* __restrict__ o,
-                                                          const int* __restrict__ inv,
-                                                          const float* __restrict__ w, T* __restrict__ dO,
-                                                          float* __restrict__ ds, int k, int m) {
-  constexpr int V = Vec8<T>::N;
-  __shared__ float red[4][kRowGroup];
-  const long t = blockIdx.x;
-  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  for (int j0 = 0; j0 < k; j0 += kRowGroup) {
-    long row[kRowGroup];
-    float wj[kRowGroup], dot[kRowGroup];
-#pragma unroll
-    for (int jj = 0; jj < kRowGroup; jj++) {
-      dot[jj] = 0.0f;
-      if (j0 + jj < k) {
-        row[jj] = inv[t * k + j0 + jj];
-        wj[jj] = w[t * k + j0 + jj];
-      }
-    }
-    for (int c = threadIdx.x; c * V < m; c += blockDim.x) {
-      float fy[V], fo[kRowGroup][V];
-      Vec8<T>::load(dY + t * m + c * V, fy);
-#pragma unroll
-      for (int jj = 0; jj < kRowGroup; jj++)
-        if (j0 + jj < k) Vec8<T>::load(o + row[jj] * m + c * V, fo[jj]);
-#pragma unroll
-      for (int jj = 0; jj < kRowGroup; jj++) {
-        if (j0 + jj < k) {
-          float out[V];
-#pragma unroll
-          for (int q = 0; q < V; q++) {
-            dot[jj] += fy[q] * fo[jj][q];
-            out[q] = wj[jj] * fy[q];
-          }
-          if (dO) Vec8<T>::store(dO + row[jj] * m + c * V, out);
-        }
-      }
-    }
-#pragma unroll
-    for (int jj = 0; jj < kRowGroup; jj++) {
-      const float d = wave_sum(dot[jj]);
-      if ((threadIdx.x & 63) == 0) red[wave][jj] = d;
-    }
-    __syncthreads();
-    if (threadIdx.x < kRowGroup && j0 + (int)threadIdx.x < k) {
-      float sum = 0.0f;
-      for (int q = 0; q < nw; q++) sum += red[q][threadIdx.x];
-      ds[t * k + j0 + threadIdx.x] = sum;
-    }
-    __syncthreads();
-  }
+// ds[p] = sum over q < nparts of part[q * P + p], added in order of q
+__global__ void ds_reduce_kernel(const float* __restrict__ part, int nparts, long P, float* __restrict__ ds) {
+  const long p = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= P) return;
+  float v = 0.0f;
+  for (int q = 0; q < nparts; q++) v += part[q * P + p];
+  ds[p] = v;
 }
+
 __global__ void router_bwd_kernel(const float* __restrict__ ds, const float* __restrict__ w,
                                   const float* __restrict__ psel, int s, int k, int score, int renorm,
                                   float* __restrict__ dz) {
@@ -590,22 +546,12 @@ hipError_t launch_combine(int dtype, const void* o, const int* inv, const float*
   return hipGetLastError();
 }
 
-hipError_t launch_combine_bwd(int dtype, const void* dY, const void* o, const int* inv,
-                              const float* w, void* dO, float* ds, int s, int k, int m,
-                              hipStream_t st) {
+hipError_t launch_router_bwd(const float* ds_part, int nparts, float* ds, const float* w, const float* psel,
+                             int s, int k, int score, int renorm, float* dz, hipStream_t st) {
   if (s <= 0) return hipSuccess;
-  if (dtype)
-    hipLaunchKernelGGL(combine_bwd_kernel<bf16_t>, dim3(s), dim3(256), 0, st, (const bf16_t*)dY,
-                       (const bf16_t*)o, inv, w, (bf16_t*)dO, ds, k, m);
-  else
-    hipLaunchKernelGGL(combine_bwd_kernel<float>, dim3(s), dim3(256), 0, st, (const float*)dY,
-                       (const float*)o, inv, w, (float*)dO, ds, k, m);
-  return hipGetLastError();
-}
-
-hipError_t launch_router_bwd(const float* ds, const float* w, const float* psel, int s, int k,
-                             int score, int renorm, float* dz, hipStream_t st) {
-  if (s <= 0) return hipSuccess;
+  const long P = (long)s * k;
+  hipLaunchKernelGGL(ds_reduce_kernel, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, st, ds_part, nparts, P,
+                     ds);
   hipLaunchKernelGGL(router_bwd_kernel, dim3((s + 255) / 256), dim3(256), 0, st, ds, w, psel, s, k,
                      score, renorm, dz);
   return hipGetLastError();

@@ -94,8 +94,10 @@ def test_sizes_grow_with_tokens_and_dtype():
     a, b = shape(s=512), shape(s=1024)
     for fn in (g.moe_route_state_bytes, g.moe_fwd_saved_bytes, g.moe_bwd_ws_bytes):
         assert 0 < fn(a) < fn(b)
-    assert g.moe_fwd_ws_bytes(a, True) == 0
-    assert g.moe_fwd_ws_bytes(a, False) == g.moe_fwd_saved_bytes(a)
+    # the expert outputs o (P x m, only the forward's combine reads them) live in the workspace
+    o_bytes = a.s * a.k * a.m * (2 if a.dtype == g.MOE_DTYPE["bf16"] else 4)
+    assert g.moe_fwd_ws_bytes(a, True) == o_bytes
+    assert g.moe_fwd_ws_bytes(a, False) == g.moe_fwd_saved_bytes(a) + o_bytes
     assert g.moe_fwd_saved_bytes(shape(dtype="f32")) > g.moe_fwd_saved_bytes(shape())
 
 
