@@ -925,7 +925,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gk_mfma(GemmArgs a, const int* t
 #pragma unroll
   for (int u = 0; u < B_PT; u++) bcol[u] = min(nt * BN + ((tid + u * NT) % CPR_B) * 8, a.N - 8);
 
-  i32x4_t ra[A_PT], rb[B_PT];
+  i32x4_t ra[2][A_PT], rb[2][B_PT];  // two register slots: loads run two K tiles ahead
   f32x16_t acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; i++)
@@ -935,37 +935,42 @@ __global__ __launch_bounds__(WM * WN * 64) void gk_mfma(GemmArgs a, const int* t
       for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
   const i32x4_t zero = {0, 0, 0, 0};
 
-  // Left-operand source rows of a K tile (-1 past the group's end). With a row gather they come
-  // from a.arow, so they are fetched one tile ahead of the data that uses them.
-  auto gidx = [&](int k0, long* src) {
+  // Every load is issued unconditionally (rows past the group's end read its last row, so the
+  // compiler's load counting is the same on every path); those rows are zeroed when copied to LDS.
+  // Left-operand source rows of a K tile: with a row gather they come from a.arow, so they are
+  // fetched one tile ahead of the data that uses them.
+  // (the gathered index is divided only when used, so the index load is not waited for here)
+  auto gidx = [&](int k0, int* src) {
 #pragma unroll
     for (int u = 0; u < A_PT; u++) {
-      const int row = k0 + (tid + u * NT) / CPR_A;
-      src[u] = row < ke ? (a.arow ? (long)(a.arow[row] / a.arow_div) : (long)row) : -1;
+      const int row = min(k0 + (tid + u * NT) / CPR_A, ke - 1);
+      src[u] = a.arow ? a.arow[row] : row;
     }
   };
-  auto gload = [&](int k0, const long* src) {
+  auto gload = [&](int k0, const int* src, i32x4_t* ra_, i32x4_t* rb_) {
 #pragma unroll
-    for (int u = 0; u < A_PT; u++)
-      ra[u] = src[u] >= 0 ? ld16((const bf16_t*)a.A + src[u] * a.lda + acol[u]) : zero;
+    for (int u = 0; u < A_PT; u++) {
+      const long srow = a.arow ? (long)(src[u] / a.arow_div) : (long)src[u];
+      ra_[u] = ld16((const bf16_t*)a.A + srow * a.lda + acol[u]);
+    }
 #pragma unroll
     for (int u = 0; u < B_PT; u++) {
-      const int row = k0 + (tid + u * NT) / CPR_B;
-      rb[u] = row < ke ? ld16((const bf16_t*)a.B + (long)row * a.ldb + bcol[u]) : zero;
+      const int row = min(k0 + (tid + u * NT) / CPR_B, ke - 1);
+      rb_[u] = ld16((const bf16_t*)a.B + (long)row * a.ldb + bcol[u]);
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int k0, int buf, const i32x4_t* ra, const i32x4_t* rb) {
     bf16_t* sA = smem + buf * STAGE;
     bf16_t* sB = sA + A_ELEMS;
 #pragma unroll
     for (int u = 0; u < A_PT; u++) {
       const int c = tid + u * NT;
-      *reinterpret_cast<i32x4_t*>(sA + (c / CPR_A) * LDA + (c % CPR_A) * 8) = ra[u];
+      *reinterpret_cast<i32x4_t*>(sA + (c / CPR_A) * LDA + (c % CPR_A) * 8) = k0 + c / CPR_A < ke ? ra[u] : zero;
     }
 #pragma unroll
     for (int u = 0; u < B_PT; u++) {
       const int c = tid + u * NT;
-      *reinterpret_cast<i32x4_t*>(sB + (c / CPR_B) * LDB + (c % CPR_B) * 8) = rb[u];
+      *reinterpret_cast<i32x4_t*>(sB + (c / CPR_B) * LDB + (c % CPR_B) * 8) = k0 + c / CPR_B < ke ? rb[u] : zero;
     }
   };
   auto compute = [&](const bf16_t* sA) {
@@ -985,21 +990,33 @@ __global__ __launch_bounds__(WM * WN * 64) void gk_mfma(GemmArgs a, const int* t
     }
   };
 
+  // Tile kt lives in LDS buffer kt & 1 and arrives through register slot kt & 1; its loads are issued
+  // two tiles ahead (while tile kt - 2 is multiplied), its row indices three tiles ahead.
   const int nk = (ke - kb + BK - 1) / BK;
   if (nk > 0) {
-    long src[A_PT];
-    gidx(kb, src);
-    gload(kb, src);
-    gidx(kb + BK, src);
-    sstore(0);
+    // src[j]: rows of the next tile of parity j. Each step issues its index loads before its data
+    // loads, so waiting for the indices never waits for the data still in flight.
+    int src[2][A_PT];
+    gidx(kb, src[0]);
+    gidx(kb + BK, src[1]);
+    gload(kb, src[0], ra[0], rb[0]);
+    gidx(kb + 2 * BK, src[0]);
+    gload(kb + BK, src[1], ra[1], rb[1]);
+    sstore(kb, 0, ra[0], rb[0]);
     __syncthreads();
-    for (int kt = 0; kt < nk; kt++) {
-      if (kt + 1 < nk) {
-        gload(kb + (kt + 1) * BK, src);
-        gidx(kb + (kt + 2) * BK, src);
-      }
-      compute(smem + (kt & 1) * STAGE);
-      if (kt + 1 < nk) sstore((kt + 1) & 1);
+    for (int kt = 0; kt < nk; kt += 2) {
+      // tile kt (buffer 0); slot 0 is free, slot 1 holds tile kt + 1 (all rows past ke once kt + 1 >= nk)
+      gidx(kb + (kt + 3) * BK, src[1]);
+      gload(kb + (kt + 2) * BK, src[0], ra[0], rb[0]);
+      compute(smem);
+      sstore(kb + (kt + 1) * BK, 1, ra[1], rb[1]);
+      __syncthreads();
+      if (kt + 1 >= nk) break;
+      // tile kt + 1 (buffer 1); slot 1 is free, slot 0 holds tile kt + 2
+      gidx(kb + (kt + 4) * BK, src[0]);
+      gload(kb + (kt + 3) * BK, src[1], ra[1], rb[1]);
+      compute(smem + STAGE);
+      sstore(kb + (kt + 2) * BK, 0, ra[0], rb[0]);
       __syncthreads();
     }
   }
