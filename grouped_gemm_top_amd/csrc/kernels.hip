@@ -318,8 +318,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ o, c
     Vec8<T>::store(Y + t * m + c * V, acc);
   }
 }
-// One block per token: dO[inv[t k + j]] = w[t k + j] dY_t and ds[t k + j] = dY_t . o[inv[t k + j]]
-// for its k pairs, so that dY_t is read once.
 // ds[p] = sum over q < nparts of part[q * P + p], added in order of q
 __global__ void ds_reduce_kernel(const float* __restrict__ part, int nparts, long P, float* __restrict__ ds) {
   const long p = (long)blockIdx.x * blockDim.x + threadIdx.x;
