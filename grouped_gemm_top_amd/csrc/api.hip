@@ -141,7 +141,7 @@ size_t bwd_layout(const moe_shape& s, void* base, BwdBufs* bb, bool routed = tru
   Carve c(base);
   const size_t P = (size_t)pairs(s), es = esize(s), rt = routed ? 1 : 0;
   BwdBufs b;
-  b.ds = c.take<float>(rt * P * (ds_parts(s) + 1));  // [ds_parts][P] partials, then ds [P]
+  b.ds = c.take<float>(rt * P * ds_parts(s));  // [ds_parts][P] partials
   b.dz = c.take<float>(rt * P);
   b.WrT = c.bytes(rt * s.E * s.m * es);
   b.Ud = c.bytes(P * s.r * es);
@@ -669,8 +669,8 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
                                   dA_g, dB_g, dA_u, dB_u, dA_d, dB_d, hs));
   // router backward: dz on the selected logits; W_r^T rows for the unpermute
   if (s.router_grad) {
-    STAGE(ST_BWD_ROUTER, launch_router_bwd(b.ds, ds_parts(s), b.ds + (size_t)ds_parts(s) * P, topk_w, rs.psel,
-                                           s.s, s.k, s.score, s.renormalize, b.dz, hs));
+    STAGE(ST_BWD_ROUTER, launch_router_bwd(b.ds, ds_parts(s), topk_w, rs.psel, s.s, s.k, s.score, s.renormalize,
+                                           b.dz, hs));
     STAGE(ST_BWD_ROUTER, launch_transpose(s.dtype, W_r, b.WrT, s.m, s.E, 1, hs));
   }
   // unpermute: dX[t] = sum_j dXp[inv[t k + j]] (+ sum_j dz[t,j] W_r[:, idx[t,j]])

@@ -29,9 +29,9 @@ hipError_t launch_scatter(const int* idx, const int* rank, const int* blk_base, 
 hipError_t launch_combine(int dtype, const void* o, const int* inv, const float* w, void* Y, int s,
                           int k, int m, hipStream_t st);
 // ds[p] = sum of the partials ds_part[q * s k + p] over q < nparts (in order of q), then dz[t, j]
-// from ds, w, p_sel (softmax or sigmoid, renormalised or not).
-hipError_t launch_router_bwd(const float* ds_part, int nparts, float* ds, const float* w, const float* psel,
-                             int s, int k, int score, int renorm, float* dz, hipStream_t st);
+// from ds, w, p_sel (softmax or sigmoid, renormalised or not). k <= 1024.
+hipError_t launch_router_bwd(const float* ds_part, int nparts, const float* w, const float* psel, int s, int k,
+                             int score, int renorm, float* dz, hipStream_t st);
 // WT[b][c, a] = W[b][a, c] for `batch` consecutive rows x cols matrices
 hipError_t launch_transpose(int dtype, const void* W, void* WT, int rows, int cols, int batch,
                             hipStream_t st);

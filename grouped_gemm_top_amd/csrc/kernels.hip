@@ -318,21 +318,28 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ o, c
     Vec8<T>::store(Y + t * m + c * V, acc);
   }
 }
-// ds[p] = sum over q < nparts of part[q * P + p], added in order of q
-__global__ void ds_reduce_kernel(const float* __restrict__ part, int nparts, long P, float* __restrict__ ds) {
-  const long p = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (p >= P) return;
-  float v = 0.0f;
-  for (int q = 0; q < nparts; q++) v += part[q * P + p];
-  ds[p] = v;
-}
-
-__global__ void router_bwd_kernel(const float* __restrict__ ds, const float* __restrict__ w,
-                                  const float* __restrict__ psel, int s, int k, int score, int renorm,
-                                  float* __restrict__ dz) {
-  const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= s) return;
-  const float* dst = ds + t * k;
+// One block per group of whole tokens (256 / k of them): the block first adds up the ds partials of its
+// pairs (ds[p] = sum over q < nparts of part[q * P + p], in order of q; coalesced over p), then one
+// thread per token forms dz.
+constexpr int kRouterMaxK = 1024;
+__global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict__ part, int nparts,
+                                                         const float* __restrict__ w,
+                                                         const float* __restrict__ psel, int s, int k,
+                                                         int score, int renorm, float* __restrict__ dz) {
+  __shared__ float dsh[kRouterMaxK > 256 ? kRouterMaxK : 256];
+  const int TB = max(1, 256 / k);
+  const long t0 = (long)blockIdx.x * TB;
+  const int ntok = (int)min((long)TB, (long)s - t0);
+  const long P = (long)s * k, p0 = t0 * k;
+  for (int i = threadIdx.x; i < ntok * k; i += blockDim.x) {
+    float v = 0.0f;
+    for (int q = 0; q < nparts; q++) v += part[q * P + p0 + i];
+    dsh[i] = v;
+  }
+  __syncthreads();
+  if ((int)threadIdx.x >= ntok) return;
+  const long t = t0 + threadIdx.x;
+  const float* dst = dsh + threadIdx.x * k;
   const float* wt = w + t * k;
   const float* pt = psel + t * k;
   float wds = 0.0f, S = 0.0f;
@@ -544,14 +551,13 @@ hipError_t launch_combine(int dtype, const void* o, const int* inv, const float*
   return hipGetLastError();
 }
 
-hipError_t launch_router_bwd(const float* ds_part, int nparts, float* ds, const float* w, const float* psel,
-                             int s, int k, int score, int renorm, float* dz, hipStream_t st) {
+hipError_t launch_router_bwd(const float* ds_part, int nparts, const float* w, const float* psel, int s, int k,
+                             int score, int renorm, float* dz, hipStream_t st) {
   if (s <= 0) return hipSuccess;
-  const long P = (long)s * k;
-  hipLaunchKernelGGL(ds_reduce_kernel, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, st, ds_part, nparts, P,
-                     ds);
-  hipLaunchKernelGGL(router_bwd_kernel, dim3((s + 255) / 256), dim3(256), 0, st, ds, w, psel, s, k,
-                     score, renorm, dz);
+  if (k > kRouterMaxK) return hipErrorInvalidValue;
+  const int TB = std::max(1, 256 / k);
+  hipLaunchKernelGGL(router_bwd_kernel, dim3((unsigned)((s + TB - 1) / TB)), dim3(256), 0, st, ds_part, nparts, w,
+                     psel, s, k, score, renorm, dz);
   return hipGetLastError();
 }
 
