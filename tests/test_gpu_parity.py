@@ -14,7 +14,7 @@ import torch
 import oracle
 from helpers import (LOGIT_TOL, TOL, VARIANTS, WEIGHT_TOL, host_weights, np64, oracle_route_from,
                      rel_err)
-from synth import make_inputs
+from synth import config, make_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -244,3 +244,39 @@ def test_merged_weights_fused_gate_up(out_in, cuda):
     yerr = rel_err(np64(Y), Y_ref)
     _say(f"  merge err gu {err:.2e}; Y {yerr:.2e}")
     assert err <= TOL[cfg.dtype] and yerr <= TOL[cfg.dtype]
+
+
+# Degenerate and extreme shapes of the routing: every expert chosen by every token, one expert per
+# token, a single token, the largest expert count (most experts empty), and sigmoid scores without
+# renormalisation (the router gradient then has no coupling between a token's slots).
+EDGE = {
+    "k_equals_E": config("qwen3_30b_a3b", s=64, m=128, n=64, E=8, k=8),
+    "k_one": config("qwen3_30b_a3b", s=200, m=128, n=64, E=16, k=1),
+    "one_token": config("qwen3_30b_a3b", s=1, m=128, n=64, E=8, k=2),
+    "max_experts": config("qwen3_30b_a3b", s=300, m=128, n=64, E=1024, k=4),
+    "sigmoid_no_renorm": config("deepseek_v3", s=256, m=128, n=64, E=16, k=4, renormalize=False),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_edge_shapes(name, cuda):
+    _parity(EDGE[name], name, 0, cuda)
+
+
+def test_empty_batch(cuda):
+    """s == 0: every call succeeds, nothing is written but the gradients, which are zeroed."""
+    from grouped_gemm_top_amd import layer
+    cfg = config("qwen3_30b_a3b", s=0, m=128, n=64, E=8, k=2)
+    _say("[edge] empty batch")
+    inp = make_inputs(cfg, seed=0, device="cpu", with_grad_output=True)
+    d = {k: (v.to(cuda) if v is not None else None) for k, v in inp.items()}
+    shape = layer.shape_of(cfg)
+    rt = layer.route(shape, d["X"], d["W_r"], d["router_bias"])
+    Y, saved = layer.forward(shape, d["X"], rt, d)
+    grads = {k: torch.full(v.shape, 7.0, device=cuda) for k, v in layer.alloc_grads(shape, cuda).items()}
+    dX, grads = layer.backward(shape, d["dY"], d["X"], d["W_r"], rt, d, saved, grads=grads)
+    torch.cuda.synchronize()
+    assert Y.shape == (0, cfg.m) and dX.shape == (0, cfg.m)
+    assert torch.all(rt["expert_off"] == 0)
+    for key, v in grads.items():
+        assert torch.all(v == 0), key
