@@ -170,6 +170,9 @@ def main():
                     help="run every GEMM with the plain SIMT kernels (diagnostics)")
     ap.add_argument("--recompute", action="store_true",
                     help="keep no forward intermediates: the backward recomputes them")
+    ap.add_argument("--shared-expert", type=int, default=0, metavar="N",
+                    help="add a shared expert of intermediate size N (a dense Split-LoRA SwiGLU "
+                         "expert on every token, added into Y and dX) to every step")
     ap.add_argument("--crossover", action="store_true",
                     help="only time the forward with Split LoRA against the materialised PEFT form "
                          "(merge W + cAB, then plain expert GEMMs) over a sweep of token counts, "
@@ -225,10 +228,32 @@ def main():
     dX = torch.empty_like(X)
     grads = layer.alloc_grads(shape, dev)
 
+    sh = None
+    if args.shared_expert:  # one expert's weights (expert 0 of a draw with its own seed and shapes)
+        sh_cfg = config(args.workload, n=args.shared_expert, E=8, k=1)
+        sh_inp = make_inputs(sh_cfg, seed=1, device=dev, with_grad_output=False)
+        sh_shape = layer.shape_of(sh_cfg, flags=flags)
+        sh = {
+            "cfg": sh_cfg, "shape": sh_shape,
+            "W": {k: sh_inp[k][0].contiguous() for k in ("W_gu", "W_d", "A_g", "B_g", "A_u", "B_u", "A_d", "B_d")},
+            "saved": None if args.recompute else torch.empty(max(1, g.moe_shared_saved_bytes(sh_shape)),
+                                                             dtype=torch.uint8, device=dev),
+            "fws": torch.empty(max(1, g.moe_shared_fwd_ws_bytes(sh_shape, not args.recompute)),
+                               dtype=torch.uint8, device=dev),
+            "bws": torch.empty(max(1, g.moe_shared_bwd_ws_bytes(sh_shape)), dtype=torch.uint8, device=dev),
+            "grads": layer.shared_grads(sh_shape, dev),
+        }
+        log(f"[bench] shared expert: n={args.shared_expert}")
+
     def step():
         layer.route(shape, X, Wr, bias, bufs=rt)
         layer.forward(shape, X, rt, inp, training=not args.recompute, Y=Y, saved=saved, ws=fws)
+        if sh:
+            layer.shared_forward(sh["shape"], X, sh["W"], Y, training=not args.recompute, saved=sh["saved"],
+                                 ws=sh["fws"])
         layer.backward(shape, dY, X, Wr, rt, inp, saved, dX=dX, grads=grads, ws=bws)
+        if sh:
+            layer.shared_backward(sh["shape"], dY, X, sh["W"], sh["saved"], dX, grads=sh["grads"], ws=sh["bws"])
 
     for _ in range(args.warmup):
         step()
@@ -259,7 +284,11 @@ def main():
         log(f"[bench]   {k:24s} {v * 1e3:9.1f} us/step")
 
     flops = accounting.gemm_flops(cfg.s, cfg.m, cfg.n, cfg.E, cfg.k, cfg.r, backward=True)
-    tflops = flops["total"] / (ms * 1e-3) / 1e12
+    total_flops = flops["total"]
+    if sh:  # the shared expert: the expert arithmetic of the layer with one expert per token, no router
+        sf = accounting.gemm_flops(cfg.s, cfg.m, args.shared_expert, 1, 1, cfg.r, backward=True)
+        total_flops += sf["fwd_gemm"] + sf["bwd_gemm"]
+    tflops = total_flops / (ms * 1e-3) / 1e12
     cnt = np.diff(rt["expert_off"].cpu().numpy())
     b = 2 if cfg.dtype == "bf16" else 4
     dom = max(GEMM_STAGES, key=lambda st: per_step.get(st, 0.0))
@@ -300,7 +329,8 @@ def main():
         "config": {"workload": cfg.name, "s": cfg.s, "m": cfg.m, "n": cfg.n, "E": cfg.E,
                    "k": cfg.k, "r": cfg.r, "alpha": cfg.alpha, "router": cfg.score,
                    "step": "route+forward+backward" + (" (backward recomputes the forward)"
-                                                        if args.recompute else ""),
+                                                        if args.recompute else "")
+                           + (f" + shared expert n={args.shared_expert}" if sh else ""),
                    "gemm": "reference-simt" if args.reference_gemm else "mfma"},
         "tflops": round(tflops, 2),
         "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),

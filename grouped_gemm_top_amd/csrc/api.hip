@@ -74,6 +74,9 @@ inline bool recompute(const moe_shape& s) { return (s.flags & MOE_FLAG_RECOMPUTE
 // one LoRA pair on the fused gate/up projection: A [E, m, r] in A_g, B [E, r, 2n] in B_g
 inline bool fused_gu(const moe_shape& s) { return (s.flags & MOE_FLAG_FUSED_GU_LORA) != 0; }
 inline long pairs(const moe_shape& s) { return (long)s.s * s.k; }
+// Rows per chunk of the LoRA-gradient reductions: a shared expert's single group (E == 1 internally,
+// and never empty when reduced) takes small chunks so that its reductions fill the chip.
+inline int gk_chunk_rows(const moe_shape& s) { return s.E == 1 ? kGkChunkSmall : kGkChunk; }
 // ds of a pair arrives as one partial per 64 columns of the expert intermediate (n % 64 == 0)
 inline int ds_parts(const moe_shape& s) { return s.n / 64; }
 inline int nblocks(const moe_shape& s) { return (s.s + kRouteBlockTokens - 1) / kRouteBlockTokens; }
@@ -150,7 +153,7 @@ size_t bwd_layout(const moe_shape& s, void* base, BwdBufs* bb, bool routed = tru
   b.dXp = c.bytes(rt * P * s.m * es);
   b.Udw = c.bytes(rt * P * s.r * es);
   b.Tdw = c.bytes(rt * P * s.r * es);
-  b.gkpart = c.take<float>((size_t)gk_part_floats((long)P, s.E, 1, 3L * (s.n + s.m) * s.r));
+  b.gkpart = c.take<float>((size_t)gk_part_floats((long)P, s.E, 1, 3L * (s.n + s.m) * s.r, gk_chunk_rows(s)));
   const size_t fac = out_in(s) ? 1 : 0;  // the tails then read the factors in the weights' layout
   b.At_d = c.bytes(fac * s.E * s.r * s.n * es);
   b.At_g = c.bytes(fac * s.E * s.r * s.m * es);
@@ -707,7 +710,8 @@ static moe_status backward_experts(const moe_shape& s, const Grouping& gr, const
     a.gkpart = nullptr;
     if (!chunked) return;
     a.gkpart = gk_next;
-    gk_next += gk_part_floats((long)P, s.E, a.M, a.N);
+    a.gkchunk = gk_chunk_rows(s);
+    gk_next += gk_part_floats((long)P, s.E, a.M, a.N, a.gkchunk);
     gk_jobs[n_gk++] = a;
   };
 

@@ -90,7 +90,9 @@ struct GemmArgs {
   const void* GU;    // EPI_SWIGLU_BWD: saved [g | u]
   long ldgu;
   long guup;         // column offset of u in GU
-  float* gkpart;     // GK: fp32 partial products of groups longer than one chunk, [chunk][M][N]
+  float* gkpart;
+  int gkchunk;       // GK with gkpart: rows per chunk, kGkChunk (also 0) or kGkChunkSmall. The small chunk
+                     //   table gives a group without rows no chunk: only for groups that all have rows     // GK: fp32 partial products of groups longer than one chunk, [chunk][M][N]
                      // (gk_part_floats); nullptr: one workgroup reduces a whole group
 };
 
@@ -110,6 +112,14 @@ constexpr int kTileSizes[kNumTileSizes] = {32, 64, 128, 256, 1024};
 constexpr int kGkChunkTable = 4;
 constexpr int kGkChunk = 1024;
 static_assert(kTileSizes[kGkChunkTable] == kGkChunk, "chunk table");
+// Smaller chunks for few large groups (a shared expert: one group of every token), whose 1024-row
+// chunks would leave most of the chip idle.
+constexpr int kGkChunkSmallTable = 3;
+constexpr int kGkChunkSmall = 256;
+static_assert(kTileSizes[kGkChunkSmallTable] == kGkChunkSmall, "small chunk table");
+__host__ __device__ inline int gk_chunk_table(int gkchunk) {
+  return gkchunk == kGkChunkSmall ? kGkChunkSmallTable : kGkChunkTable;
+}
 int tile_table_index(int bm);
 // Row-tile -> group maps: map i has room for rows_bound / kTileSizes[i] + G entries (a row tile
 // never spans two groups, so there are at most that many tiles); maps are stored back to back.
@@ -123,6 +133,9 @@ __host__ __device__ inline long tile_map_offset(int i, long rows_bound, int G) {
 // Floats of GemmArgs::gkpart needed by a K-grouped launch with output M x N.
 inline long gk_part_floats(long rows_bound, int G, long M, long N) {
   return tile_map_capacity(kGkChunkTable, rows_bound, G) * M * N;
+}
+inline long gk_part_floats(long rows_bound, int G, long M, long N, int gkchunk) {
+  return tile_map_capacity(gk_chunk_table(gkchunk), rows_bound, G) * M * N;
 }
 // Completes chunked K-grouped launches (made with gkpart): for every job and every group with
 // several chunks, C_e = scale * (sum of the group's chunk partials, in chunk order). Up to

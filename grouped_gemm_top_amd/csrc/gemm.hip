@@ -882,7 +882,7 @@ __device__ inline void gk_store(const GemmArgs& a, int e, int row, int col, floa
 // K-grouped MFMA GEMM: C_e = scale * L[rows_e]^T . R[rows_e]; both operands stored with the output
 // axis contiguous, so both fragments come from transposing LDS reads.
 // Without a.gkpart, one workgroup per output tile reduces all rows of its group. With it, work
-// units are (chunk of kGkChunk group rows, output tile), listed by the chunk table (toffc: chunk
+// units are (chunk of kGkChunk, or kGkChunkSmall, group rows, output tile), listed by the chunk table (toffc: chunk
 // prefix sums per group, tmapc: chunk -> group; an empty group has one empty chunk). A group of
 // one chunk stores its result directly; the chunks of a longer group store fp32 partials, which
 // gk_reduce adds up in chunk order after the launch.
@@ -911,8 +911,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gk_mfma(GemmArgs a, const int* t
     e = tmapc[u0];
     c0 = toffc[e];
     nch = toffc[e + 1] - c0;
-    kb = a.goff[e] + (u0 - c0) * kGkChunk;
-    ke = min(kb + kGkChunk, a.goff[e + 1]);
+    const int chunk = a.gkchunk == kGkChunkSmall ? kGkChunkSmall : kGkChunk;
+    kb = a.goff[e] + (u0 - c0) * chunk;
+    ke = min(kb + chunk, a.goff[e + 1]);
   } else {
     e = u0;
     kb = a.goff[e];
@@ -1237,12 +1238,23 @@ hipError_t dispatch_gm_mfma(const GemmArgs& a, int rows_bound, hipStream_t strea
   }
 }
 
-// Wave columns of the expert-projection workgroups (2: 128 x 128 tiles, two workgroups per CU;
-// 4: 128 x 256 tiles, one workgroup of eight waves per CU).
-#ifndef MOE_RING_WN
-#define MOE_RING_WN 4
-#endif
-constexpr int kRingWN = MOE_RING_WN;
+// The expert projections (GEMMs with a Split-LoRA tail) with WN wave columns per workgroup
+// (2: 128 x 128 tiles, two workgroups per CU; 4: 128 x 256 tiles, one workgroup of eight waves per CU).
+template <int WN>
+hipError_t launch_expert_projection(const GemmArgs& a, int b_layout, int epi, int rows_bound, hipStream_t stream) {
+  if (b_layout == LAYOUT_KX) {
+    if (epi == EPI_SWIGLU) return launch_gm_ring<2, WN, 2, 2, LAYOUT_KX, EPI_SWIGLU>(a, rows_bound, stream);
+    if (epi == EPI_STORE) return launch_gm_ring<2, WN, 2, 2, LAYOUT_KX, EPI_STORE>(a, rows_bound, stream);
+    if (epi == EPI_SWIGLU_BWD)  // output-major weights
+      return launch_gm_ring<2, WN, 2, 2, LAYOUT_KX, EPI_SWIGLU_BWD>(a, rows_bound, stream);
+  } else {
+    if (epi == EPI_STORE) return launch_gm_ring<2, WN, 2, 2, LAYOUT_XK, EPI_STORE>(a, rows_bound, stream);
+    if (epi == EPI_SWIGLU_BWD) return launch_gm_ring<2, WN, 2, 2, LAYOUT_XK, EPI_SWIGLU_BWD>(a, rows_bound, stream);
+    if (epi == EPI_SWIGLU)  // output-major weights
+      return launch_gm_ring<2, WN, 2, 2, LAYOUT_XK, EPI_SWIGLU>(a, rows_bound, stream);
+  }
+  return hipErrorInvalidValue;
+}
 
 // Deep-prefetch kernel (grouped launches).
 template <int WM, int WN, int TM, int TN, int BL, int EPI>
@@ -1298,19 +1310,10 @@ hipError_t gemm_gm_launch(const GemmArgs& a, int b_layout, int epi, int out_f32,
   }
   if (a.tail != TAIL_NONE) {  // the expert projections
     if (out_f32) return hipErrorInvalidValue;
-    if (b_layout == LAYOUT_KX) {
-      if (epi == EPI_SWIGLU) return launch_gm_ring<2, kRingWN, 2, 2, LAYOUT_KX, EPI_SWIGLU>(a, rows_bound, stream);
-      if (epi == EPI_STORE) return launch_gm_ring<2, kRingWN, 2, 2, LAYOUT_KX, EPI_STORE>(a, rows_bound, stream);
-      if (epi == EPI_SWIGLU_BWD)  // output-major weights
-        return launch_gm_ring<2, kRingWN, 2, 2, LAYOUT_KX, EPI_SWIGLU_BWD>(a, rows_bound, stream);
-    } else {
-      if (epi == EPI_STORE) return launch_gm_ring<2, kRingWN, 2, 2, LAYOUT_XK, EPI_STORE>(a, rows_bound, stream);
-      if (epi == EPI_SWIGLU_BWD)
-        return launch_gm_ring<2, kRingWN, 2, 2, LAYOUT_XK, EPI_SWIGLU_BWD>(a, rows_bound, stream);
-      if (epi == EPI_SWIGLU)  // output-major weights
-        return launch_gm_ring<2, kRingWN, 2, 2, LAYOUT_XK, EPI_SWIGLU>(a, rows_bound, stream);
-    }
-    return hipErrorInvalidValue;
+    // 128 x 256 tiles, one eight-wave workgroup per CU. (128 x 128 tiles, two workgroups per CU, were
+    // measured too: slower on the routed layers, and on a shared expert's few large launches no faster
+    // in sum.)
+    return launch_expert_projection<4>(a, b_layout, epi, rows_bound, stream);
   }
   if (out_f32) {
     if (epi != EPI_STORE) return hipErrorInvalidValue;
@@ -1351,9 +1354,11 @@ hipError_t gemm_gk_launch(const GemmArgs& a, int dtype, int reference, int rows_
   long units = (long)a.G * tiles;
   if (a.gkpart) {
     if (!a.toff_all || !a.tmap_all || rows_bound < 0) return hipErrorInvalidValue;
-    toffc = a.toff_all + kGkChunkTable * (a.G + 1);
-    tmapc = a.tmap_all + tile_map_offset(kGkChunkTable, rows_bound, a.G);
-    units = tile_map_capacity(kGkChunkTable, rows_bound, a.G) * tiles;
+    if (a.gkchunk != 0 && a.gkchunk != kGkChunk && a.gkchunk != kGkChunkSmall) return hipErrorInvalidValue;
+    const int tab = gk_chunk_table(a.gkchunk);
+    toffc = a.toff_all + tab * (a.G + 1);
+    tmapc = a.tmap_all + tile_map_offset(tab, rows_bound, a.G);
+    units = tile_map_capacity(tab, rows_bound, a.G) * tiles;
   }
   const long blocks = (units + 7) / 8 * 8;
   if (blocks > 0)
@@ -1369,14 +1374,16 @@ hipError_t gemm_gk_reduce(const GemmArgs* jobs, int njobs, int rows_bound, hipSt
   long mn = 0;
   for (int i = 0; i < kGkMaxJobs; i++) j.job[i] = jobs[i < njobs ? i : 0];
   for (int i = 0; i < njobs; i++) {
-    if (!jobs[i].gkpart || !jobs[i].toff_all || jobs[i].G != jobs[0].G) return hipErrorInvalidValue;
+    if (!jobs[i].gkpart || !jobs[i].toff_all || jobs[i].G != jobs[0].G ||
+        gk_chunk_table(jobs[i].gkchunk) != gk_chunk_table(jobs[0].gkchunk))
+      return hipErrorInvalidValue;
     mn = std::max(mn, (long)jobs[i].M * jobs[i].N);
   }
   if (jobs[0].G <= 0 || mn <= 0) return hipSuccess;
   if (jobs[0].G > kGkMaxGroups) return hipErrorInvalidValue;
   const unsigned bx = (unsigned)std::min<long>((mn + 255) / 256, 256);
   hipLaunchKernelGGL(gk_reduce, dim3(bx, (unsigned)njobs), dim3(256), 0, stream, j,
-                     (const int*)(jobs[0].toff_all + kGkChunkTable * (jobs[0].G + 1)));
+                     (const int*)(jobs[0].toff_all + gk_chunk_table(jobs[0].gkchunk) * (jobs[0].G + 1)));
   (void)rows_bound;
   return hipGetLastError();
 }
