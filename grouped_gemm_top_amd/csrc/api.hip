@@ -788,16 +788,16 @@ static moe_status backward_experts(const moe_shape& s, const Grouping& gr, const
     a.B = B_g; a.ldb = 2 * s.n; a.bstride = (long)r * 2 * n;
     a.C = b.Ugu; a.ldc = s.r; a.scale = c;
     STAGE(ST_BWD_U_GU, gemm_gm_launch(a, LAYOUT_XK, EPI_STORE, 0, s.dtype, Pi, ref, hs));
-  } else {
+  } else {  // the gate and up products are independent: one launch runs both
     GemmArgs a = base;
     a.N = s.r; a.K = s.n;
     a.A = b.dgu; a.lda = 2 * s.n;
     a.B = B_g; a.ldb = s.n; a.bstride = (long)r * n;
     a.C = b.Ugu; a.ldc = 2 * s.r; a.scale = c;
-    STAGE(ST_BWD_U_GU, gemm_gm_launch(a, LAYOUT_XK, EPI_STORE, 0, s.dtype, Pi, ref, hs));
-    a.A = (const char*)b.dgu + n * es;
-    a.B = B_u;
-    a.C = (char*)b.Ugu + r * es;
+    a.nbatch = 2;
+    a.bA = (const char*)b.dgu + n * es;
+    a.bB = B_u;
+    a.bC = (char*)b.Ugu + r * es;
     STAGE(ST_BWD_U_GU, gemm_gm_launch(a, LAYOUT_XK, EPI_STORE, 0, s.dtype, Pi, ref, hs));
   }
   // dXp = dgu W_gu^T + Uc_g A_g^T + Uc_u A_u^T

@@ -495,6 +495,11 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
+  if (blockIdx.y) {  // the second problem of a batched launch
+    a.A = a.bA;
+    a.B = a.bB;
+    a.C = a.bC;
+  }
 
   // ---- which (group, row tile, column tile)
   const int tilesN = (a.N + BNH - 1) / BNH;
@@ -1071,6 +1076,11 @@ __device__ inline float opv(const T* base, int layout, long ld, int x, int kk) {
 template <typename T, typename OutT, int EPI>
 __global__ void gm_simt(GemmArgs a, int b_layout, int total_rows_bound) {
   constexpr bool DUAL = (EPI == EPI_DUAL || EPI == EPI_SWIGLU);
+  if (blockIdx.z) {  // the second problem of a batched launch
+    a.A = a.bA;
+    a.B = a.bB;
+    a.C = a.bC;
+  }
   const int row = blockIdx.x;
   const int jj = blockIdx.y * blockDim.x + threadIdx.x;
   if (jj >= a.N) return;
@@ -1171,7 +1181,7 @@ struct TileCfg {
 
 template <typename Cfg, int BL, int EPI, typename OutT, bool TAIL>
 hipError_t launch_gm_mfma_t(const GemmArgs& a, int rows_bound, hipStream_t stream) {
-  if (a.accum || a.C2 || a.wscale) return hipErrorInvalidValue;
+  if (a.accum || a.C2 || a.wscale || a.nbatch > 1) return hipErrorInvalidValue;
   constexpr bool DUAL = (EPI == EPI_DUAL || EPI == EPI_SWIGLU);
   constexpr int BNH = DUAL ? Cfg::BN / 2 : Cfg::BN;
   auto kern = gm_mfma<Cfg::WM, Cfg::WN, Cfg::TM, Cfg::TN, Cfg::BKT, Cfg::S, BL, EPI, OutT, TAIL>;
@@ -1273,8 +1283,9 @@ hipError_t launch_gm_ring(const GemmArgs& a, int rows_bound, hipStream_t stream)
   if (units <= 0) return hipSuccess;
   const long blocks = (units + 7) / 8 * 8;
   const int* tmap = a.tmap_all + tile_map_offset(tidx, rows_bound, a.G);
-  hipLaunchKernelGGL((gm_ring<WM, WN, TM, TN, BL, EPI>), dim3((unsigned)blocks), dim3(WM * WN * 64), 0,
-                     stream, a, tidx, tmap);
+  if (a.nbatch > 2 || (a.nbatch == 2 && (!a.bA || !a.bB || !a.bC))) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gm_ring<WM, WN, TM, TN, BL, EPI>), dim3((unsigned)blocks, a.nbatch == 2 ? 2u : 1u),
+                     dim3(WM * WN * 64), 0, stream, a, tidx, tmap);
   return hipGetLastError();
 }
 
@@ -1282,8 +1293,9 @@ template <typename T, typename OutT, int EPI>
 hipError_t launch_gm_simt(const GemmArgs& a, int b_layout, int rows_bound, hipStream_t stream) {
   const int rows = a.goff ? rows_bound : a.M;
   if (rows <= 0 || a.N <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gm_simt<T, OutT, EPI>), dim3(rows, (a.N + 63) / 64), dim3(64), 0, stream, a,
-                     b_layout, rows_bound);
+  if (a.nbatch > 2 || (a.nbatch == 2 && (!a.bA || !a.bB || !a.bC))) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gm_simt<T, OutT, EPI>), dim3(rows, (a.N + 63) / 64, a.nbatch == 2 ? 2 : 1), dim3(64), 0,
+                     stream, a, b_layout, rows_bound);
   return hipGetLastError();
 }
 
