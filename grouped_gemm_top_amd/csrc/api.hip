@@ -845,17 +845,20 @@ static moe_status backward_experts(const moe_shape& s, const Grouping& gr, const
     a.C = dA_g; a.C1 = dA_u; a.nsplit = s.r; a.ldc = s.r; a.cstride = (long)m * r;
     gk_prep(a);
     STAGE(ST_BWD_GRAD_GU, gemm_gk_launch(a, s.dtype, ref, Pi, hs));
+    // dB_g and dB_u have the same shape: one launch runs both (each with its own partials)
     GemmArgs bg = base;
     bg.M = s.n; bg.N = s.r;
     bg.A = b.dgu; bg.lda = 2 * s.n;
     bg.B = f.Tgu; bg.ldb = 2 * s.r;
     bg.C = dB_g; bg.ldc = s.n; bg.cstride = (long)r * n; bg.ctrans = 1;
+    GemmArgs bu = bg;
+    bu.A = (const char*)b.dgu + n * es;
+    bu.B = (const char*)f.Tgu + r * es;
+    bu.C = dB_u;
     gk_prep(bg);
-    STAGE(ST_BWD_GRAD_GU, gemm_gk_launch(bg, s.dtype, ref, Pi, hs));
-    bg.A = (const char*)b.dgu + n * es;
-    bg.B = (const char*)f.Tgu + r * es;
-    bg.C = dB_u;
-    gk_prep(bg);
+    gk_prep(bu);
+    bg.nbatch = 2;
+    bg.bA = bu.A; bg.bB = bu.B; bg.bC = bu.C; bg.bgkpart = bu.gkpart;
     STAGE(ST_BWD_GRAD_GU, gemm_gk_launch(bg, s.dtype, ref, Pi, hs));
     if (n_gk) STAGE(ST_BWD_GRAD_GU, gemm_gk_reduce(gk_jobs, n_gk, Pi, hs));
   }

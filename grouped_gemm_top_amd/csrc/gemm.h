@@ -90,12 +90,14 @@ struct GemmArgs {
   const void* GU;    // EPI_SWIGLU_BWD: saved [g | u]
   long ldgu;
   long guup;         // column offset of u in GU
-  // GM deep-prefetch kernel: nbatch == 2 runs a second, independent problem of the same shape and
-  // grouping in the same launch (gridDim.y = 2), with operands bA, bB and output bC
+  // nbatch == 2 runs a second, independent problem of the same shape and grouping in the same
+  // launch (GM deep-prefetch and reference kernels, and GK), with operands bA, bB, output bC and
+  // (GK) partials bgkpart
   int nbatch;
   const void* bA;
   const void* bB;
   void* bC;
+  float* bgkpart;
   float* gkpart;
   int gkchunk;       // GK with gkpart: rows per chunk, kGkChunk (also 0) or kGkChunkSmall. The small chunk
                      //   table gives a group without rows no chunk: only for groups that all have rows     // GK: fp32 partial products of groups longer than one chunk, [chunk][M][N]

@@ -903,6 +903,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gk_mfma(GemmArgs a, const int* t
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
+  if (blockIdx.y) {  // the second problem of a batched launch
+    a.A = a.bA;
+    a.B = a.bB;
+    a.C = a.bC;
+    a.gkpart = a.bgkpart;
+  }
   const int tilesM = (a.M + BM - 1) / BM, tilesN = (a.N + BN - 1) / BN;
   const int units = a.gkpart ? toffc[a.G] : a.G;
   const int T = xcd_unit(units * tilesM * tilesN);
@@ -1154,7 +1160,12 @@ __global__ void gm_simt(GemmArgs a, int b_layout, int total_rows_bound) {
 
 template <typename T>
 __global__ void gk_simt(GemmArgs a) {
-  const int e = blockIdx.z, row = blockIdx.y;
+  if (blockIdx.z >= (unsigned)a.G) {  // the second problem of a batched launch (groups G..2G-1)
+    a.A = a.bA;
+    a.B = a.bB;
+    a.C = a.bC;
+  }
+  const int e = (int)blockIdx.z - (blockIdx.z >= (unsigned)a.G ? a.G : 0), row = blockIdx.y;
   int col = blockIdx.x * blockDim.x + threadIdx.x;
   if (col >= a.N) return;
   const int kb = a.goff[e], ke = a.goff[e + 1];
@@ -1351,8 +1362,11 @@ hipError_t gemm_gm_launch(const GemmArgs& a, int b_layout, int epi, int out_f32,
 hipError_t gemm_gk_launch(const GemmArgs& a, int dtype, int reference, int rows_bound,
                           hipStream_t stream) {
   if (a.G <= 0 || a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (a.nbatch > 2 || (a.nbatch == 2 && (!a.bA || !a.bB || !a.bC || (a.gkpart && !a.bgkpart))))
+    return hipErrorInvalidValue;
+  const unsigned nb = a.nbatch == 2 ? 2 : 1;
   if (dtype == 0 || reference) {
-    dim3 grid((a.N + 63) / 64, a.M, a.G);
+    dim3 grid((a.N + 63) / 64, a.M, a.G * nb);
     if (dtype == 0) hipLaunchKernelGGL(gk_simt<float>, grid, dim3(64), 0, stream, a);
     else hipLaunchKernelGGL(gk_simt<bf16_t>, grid, dim3(64), 0, stream, a);
     return hipGetLastError();
@@ -1374,7 +1388,7 @@ hipError_t gemm_gk_launch(const GemmArgs& a, int dtype, int reference, int rows_
   }
   const long blocks = (units + 7) / 8 * 8;
   if (blocks > 0)
-    hipLaunchKernelGGL((gk_mfma<WM, WN, TM, TN>), dim3((unsigned)blocks), dim3(WM * WN * 64), 0,
+    hipLaunchKernelGGL((gk_mfma<WM, WN, TM, TN>), dim3((unsigned)blocks, nb), dim3(WM * WN * 64), 0,
                        stream, a, toffc, tmapc);
   return hipGetLastError();
 }
