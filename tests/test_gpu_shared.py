@@ -106,3 +106,44 @@ def test_shared_expert_no_tokens(cuda):
     torch.cuda.synchronize()
     for key, v in grads.items():
         assert torch.all(v == 0), key
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("flags", [0, FLAG_FUSED_GU], ids=["pairs", "fused_gu"])
+def test_shared_expert_fullsize(flags, cuda):
+    """The shared expert at the Qwen3-30B-A3B layer's size (4096 tokens, m 2048, n 768, r 16): every
+    output row and every gradient against the fp64 oracle. Its gradient reductions split the one
+    group into many chunks at this size."""
+    from grouped_gemm_top_amd import layer
+    cfg = config("qwen3_30b_a3b", E=8, k=1)
+    _say(f"[shared fullsize] flags={flags} s={cfg.s} m={cfg.m} n={cfg.n} r={cfg.r}")
+    inp = make_inputs(cfg, seed=0, device="cpu", with_grad_output=True)
+    W1 = {k: inp[k][0].contiguous() for k in WEIGHTS}
+    if flags & FLAG_FUSED_GU:
+        W1["B_g"] = torch.cat([W1["B_g"], W1["B_u"]], dim=1).contiguous()
+        W1["A_u"] = W1["B_u"] = None
+    d = {k: (v.to(cuda) if v is not None else None) for k, v in W1.items()}
+    X, dY = inp["X"].to(cuda), inp["dY"].to(cuda)
+    Y = (X * 2.0 ** -6).contiguous()
+    dX = (dY * 2.0 ** -6).contiguous()
+    Y0, dX0 = np64(Y), np64(dX)
+    shape = layer.shape_of(cfg, flags=flags)
+    saved = layer.shared_forward(shape, X, d, Y)
+    grads = layer.shared_backward(shape, dY, X, d, saved, dX)
+    torch.cuda.synchronize()
+    Wo = {k: np64(v) for k, v in W1.items() if v is not None}
+    if flags & FLAG_FUSED_GU:
+        Wo.update(oracle.fused_gate_up_pair(Wo["A_g"], Wo["B_g"]))
+    Xh, dYh = np64(inp["X"]), np64(inp["dY"])
+    f = oracle.shared_expert_forward(Xh, Wo, cfg.alpha, cfg.r)
+    g = oracle.shared_expert_backward(dYh, Xh, Wo, cfg.alpha, cfg.r, f)
+    errs = {"Y": rel_err(np64(Y), Y0 + f["o"]), "dX": rel_err(np64(dX), dX0 + g["dX"])}
+    keys = ("dA_g", "dB_g", "dA_u", "dB_u", "dA_d", "dB_d")
+    if flags & FLAG_FUSED_GU:
+        g["dA_g"], g["dB_g"] = oracle.fused_gate_up_grads(g)
+        keys = ("dA_g", "dB_g", "dA_d", "dB_d")
+    for key in keys:
+        errs[key] = rel_err(np64(grads[key]), g[key])
+    _say("  rel errors: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    bad = {k: v for k, v in errs.items() if not v <= TOL[cfg.dtype]}
+    assert not bad, f"over tolerance: {bad}"
