@@ -26,7 +26,6 @@ int tile_table_index(int bm) {
 namespace {
 
 constexpr int BK = 64;    // K tile
-constexpr int PADE = 8;   // LDS row padding (elements)
 
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 typedef __attribute__((address_space(3))) bf16_t lds_bf16_t;
@@ -35,22 +34,6 @@ __device__ inline bf16x4_t lds_read_tr(const bf16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)((lds_bf16_t*)p));
 }
 
-// Fragment of a 32x32x16 MFMA operand from an LDS tile whose reduction axis is contiguous
-// (element (x, kk) at tile[x*LD + kk]): lane l holds x0 + l%32, kk = k0 + 8*(l/32) .. +7.
-__device__ inline bf16x8_t frag_xk(const bf16_t* tile, int LD, int x0, int k0, int lane) {
-  return *reinterpret_cast<const bf16x8_t*>(tile + (x0 + (lane & 31)) * LD + k0 + 8 * (lane >> 5));
-}
-
-// Same fragment from a tile whose output axis is contiguous (element (x, kk) at tile[kk*LD + x]).
-// Within each 16-lane group, ds_read_b64_tr_b16 gathers a 4 (kk) x 16 (x) block: lane (b, c) names
-// row b, columns 4c..4c+3, and lane L receives column L of the 4 rows. Two reads give 8 kk values.
-__device__ inline bf16x8_t frag_kx(const bf16_t* tile, int LD, int x0, int k0, int lane) {
-  const int g = lane >> 4, b = (lane >> 2) & 3, c = lane & 3;
-  const bf16_t* p = tile + (k0 + 8 * (g >> 1) + b) * LD + x0 + 16 * (g & 1) + 4 * c;
-  bf16x4_t lo = lds_read_tr(p);
-  bf16x4_t hi = lds_read_tr(p + 4 * LD);
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [0, N).
 template <int N, int I = 0, typename F>
@@ -136,7 +119,9 @@ __device__ inline bf16x8_t frag_xk_s(const bf16_t* tile, int x0, int k0, int lan
   return *reinterpret_cast<const bf16x8_t*>(tile + x * BKT + ((q ^ swz_xk<BKT / 8>(x)) << 3));
 }
 
-// Fragment from a KX tile with X elements per row (chunk q of row k at q ^ swz_kx(k)).
+// Fragment from a KX tile with X elements per row (chunk q of row k at q ^ swz_kx(k)). Within each
+// 16-lane group, ds_read_b64_tr_b16 gathers a 4 (k) x 16 (x) block: lane (b, c) names row b,
+// columns 4c..4c+3, and lane L receives column L of the 4 rows; two reads give 8 k values.
 template <int X>
 __device__ inline bf16x8_t frag_kx_s(const bf16_t* tile, int x0, int k0, int lane) {
   constexpr int CPR = X / 8;
@@ -894,8 +879,9 @@ __device__ inline void gk_store(const GemmArgs& a, int e, int row, int col, floa
 template <int WM, int WN, int TM, int TN>
 __global__ __launch_bounds__(WM * WN * 64) void gk_mfma(GemmArgs a, const int* toffc, const int* tmapc) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32, NT = WM * WN * 64;
-  constexpr int LDA = BM + PADE, LDB = BN + PADE;
-  constexpr int A_ELEMS = BK * LDA, B_ELEMS = BK * LDB, STAGE = A_ELEMS + B_ELEMS;
+  // both operands have the output axis contiguous: unpadded rows of BM (BN) elements, 16-byte chunks
+  // XOR-swizzled by row (swz_kx) so that the transposing fragment reads are free of bank conflicts
+  constexpr int A_ELEMS = BK * BM, B_ELEMS = BK * BN, STAGE = A_ELEMS + B_ELEMS;
   constexpr int CPR_A = BM / 8, CPR_B = BN / 8;
   constexpr int A_PT = BM * BK / 8 / NT, B_PT = BN * BK / 8 / NT;
   static_assert((BM * BK / 8) % NT == 0 && (BN * BK / 8) % NT == 0, "tile/thread mismatch");
@@ -976,13 +962,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gk_mfma(GemmArgs a, const int* t
     bf16_t* sB = sA + A_ELEMS;
 #pragma unroll
     for (int u = 0; u < A_PT; u++) {
-      const int c = tid + u * NT;
-      *reinterpret_cast<i32x4_t*>(sA + (c / CPR_A) * LDA + (c % CPR_A) * 8) = k0 + c / CPR_A < ke ? ra[u] : zero;
+      const int c = tid + u * NT, row = c / CPR_A;
+      *reinterpret_cast<i32x4_t*>(sA + row * BM + (((c % CPR_A) ^ swz_kx<CPR_A>(row)) << 3)) =
+          k0 + row < ke ? ra[u] : zero;
     }
 #pragma unroll
     for (int u = 0; u < B_PT; u++) {
-      const int c = tid + u * NT;
-      *reinterpret_cast<i32x4_t*>(sB + (c / CPR_B) * LDB + (c % CPR_B) * 8) = k0 + c / CPR_B < ke ? rb[u] : zero;
+      const int c = tid + u * NT, row = c / CPR_B;
+      *reinterpret_cast<i32x4_t*>(sB + row * BN + (((c % CPR_B) ^ swz_kx<CPR_B>(row)) << 3)) =
+          k0 + row < ke ? rb[u] : zero;
     }
   };
   auto compute = [&](const bf16_t* sA) {
@@ -991,9 +979,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gk_mfma(GemmArgs a, const int* t
     for (int ks = 0; ks < BK / 16; ks++) {
       bf16x8_t fa[TM], fb[TN];
 #pragma unroll
-      for (int tm = 0; tm < TM; tm++) fa[tm] = frag_kx(sA, LDA, wm * TM * 32 + tm * 32, ks * 16, lane);
+      for (int tm = 0; tm < TM; tm++) fa[tm] = frag_kx_s<BM>(sA, wm * TM * 32 + tm * 32, ks * 16, lane);
 #pragma unroll
-      for (int tn = 0; tn < TN; tn++) fb[tn] = frag_kx(sB, LDB, wn * TN * 32 + tn * 32, ks * 16, lane);
+      for (int tn = 0; tn < TN; tn++) fb[tn] = frag_kx_s<BN>(sB, wn * TN * 32 + tn * 32, ks * 16, lane);
 #pragma unroll
       for (int tm = 0; tm < TM; tm++)
 #pragma unroll
