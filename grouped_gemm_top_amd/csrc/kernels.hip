@@ -40,10 +40,11 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ z, 
       // partials added in split order; loaded 8 at a time so that their loads overlap
       acc = zt[e];
       for (int p0 = 1; p0 < nsplit; p0 += 8) {
+        // loads are unconditional (a split index past the last one reads the last split) so that
+        // they issue back to back; the surplus values are dropped
         float part[8];
 #pragma unroll
-        for (int pp = 0; pp < 8; pp++)
-          part[pp] = (p0 + pp < nsplit) ? zt[(long)(p0 + pp) * split_stride + e] : 0.0f;
+        for (int pp = 0; pp < 8; pp++) part[pp] = zt[(long)min(p0 + pp, nsplit - 1) * split_stride + e];
 #pragma unroll
         for (int pp = 0; pp < 8; pp++)
           if (p0 + pp < nsplit) acc += part[pp];
@@ -146,92 +147,129 @@ __global__ __launch_bounds__(256) void hist_rank_kernel(const int* __restrict__ 
   }
 }
 
-// Exclusive scan over a 1024-thread block; returns the exclusive prefix, *total the sum.
-__device__ int block_exscan_1024(int v, int* sh, int* total) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) sh[wv] = x;
-  __syncthreads();
-  if (wv == 0) {
-    int s2 = lane < 16 ? sh[lane] : 0;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const int y = __shfl_up(s2, o, 64);
-      if (lane >= o) s2 += y;
-    }
-    if (lane < 16) sh[16 + lane] = s2;
-  }
-  __syncthreads();
-  const int base = wv > 0 ? sh[16 + wv - 1] : 0;
-  *total = sh[16 + 15];
-  const int r = base + x - v;
-  __syncthreads();
-  return r;
-}
-
 __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ blk_hist, int nb, int E,
                                                     int P, int* __restrict__ blk_base,
                                                     int* __restrict__ off,
                                                     int* __restrict__ tile_tables,
                                                     int* __restrict__ tile_maps) {
-  __shared__ int sh[32];
-  __shared__ int tsh[1025];
-  const int e = threadIdx.x;
+  constexpr int NV = 1 + kNumTileSizes;  // expert row count, then its row-tile count in every table
+  constexpr int kKeep = 64;              // per-block counts kept in registers up to this many blocks
+  __shared__ int wsum[16][NV];
+  __shared__ int tsh[kNumTileSizes][1025];
+  const int e = threadIdx.x, lane = e & 63, wv = e >> 6;
+  const bool keep = nb <= kKeep;
+  // per-block counts of expert e (one pass; all loads in flight together)
+  int h[kKeep];
   int cnt = 0;
   if (e < E) {
-    for (int b0 = 0; b0 < nb; b0 += 8) {
-      int h[8];
+    if (keep) {
 #pragma unroll
-      for (int bb = 0; bb < 8; bb++) h[bb] = (b0 + bb < nb) ? blk_hist[(long)(b0 + bb) * E + e] : 0;
+      for (int b = 0; b < kKeep; b++) {  // unconditional loads (clamped block index), issued together
+        const int v0 = blk_hist[(long)min(b, nb - 1) * E + e];
+        h[b] = b < nb ? v0 : 0;
+      }
 #pragma unroll
-      for (int bb = 0; bb < 8; bb++) cnt += h[bb];
+      for (int b = 0; b < kKeep; b++) cnt += h[b];
+    } else {
+      for (int b0 = 0; b0 < nb; b0 += 8) {
+        int t[8];
+#pragma unroll
+        for (int bb = 0; bb < 8; bb++) {
+          const int v0 = blk_hist[(long)min(b0 + bb, nb - 1) * E + e];
+          t[bb] = b0 + bb < nb ? v0 : 0;
+        }
+#pragma unroll
+        for (int bb = 0; bb < 8; bb++) cnt += t[bb];
+      }
     }
   }
-  int total;
-  const int start = block_exscan_1024(e < E ? cnt : 0, sh, &total);
+  // the values to scan over experts: the row count and the row-tile counts (the K-grouped chunk table
+  // gives an empty group one empty chunk, which writes its zeros)
+  int v[NV], x[NV];
+  v[0] = e < E ? cnt : 0;
+#pragma unroll
+  for (int i = 0; i < kNumTileSizes; i++) {
+    const int bm = kTileSizes[i];
+    v[1 + i] = e < E ? (i == kGkChunkTable ? max(1, (cnt + bm - 1) / bm) : (cnt + bm - 1) / bm) : 0;
+  }
+  // one block-wide exclusive scan of all NV values: wave scans, then the wave totals through LDS
+#pragma unroll
+  for (int j = 0; j < NV; j++) {
+    x[j] = v[j];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x[j], o, 64);
+      if (lane >= o) x[j] += y;
+    }
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int j = 0; j < NV; j++) wsum[wv][j] = x[j];
+  }
+  __syncthreads();
+  int base[NV], tot[NV];
+#pragma unroll
+  for (int j = 0; j < NV; j++) base[j] = tot[j] = 0;
+#pragma unroll 2
+  for (int w = 0; w < 16; w++) {
+#pragma unroll
+    for (int j = 0; j < NV; j++) {
+      const int t = wsum[w][j];
+      if (w < wv) base[j] += t;
+      tot[j] += t;
+    }
+  }
+  // offsets and per-block bases
   if (e < E) {
+    const int start = base[0] + x[0] - v[0];
     off[e] = start;
     int run = start;
-    for (int b0 = 0; b0 < nb; b0 += 8) {  // per-block counts loaded 8 at a time
-      int h[8];
+    if (keep) {
 #pragma unroll
-      for (int bb = 0; bb < 8; bb++) h[bb] = (b0 + bb < nb) ? blk_hist[(long)(b0 + bb) * E + e] : 0;
+      for (int b = 0; b < kKeep; b++) {
+        if (b < nb) blk_base[(long)b * E + e] = run;
+        run += h[b];
+      }
+    } else {
+      for (int b0 = 0; b0 < nb; b0 += 8) {
+        int t[8];
 #pragma unroll
-      for (int bb = 0; bb < 8; bb++) {
-        if (b0 + bb < nb) {
-          blk_base[(long)(b0 + bb) * E + e] = run;
-          run += h[bb];
+        for (int bb = 0; bb < 8; bb++) {
+          const int v0 = blk_hist[(long)min(b0 + bb, nb - 1) * E + e];
+          t[bb] = b0 + bb < nb ? v0 : 0;
+        }
+#pragma unroll
+        for (int bb = 0; bb < 8; bb++) {
+          if (b0 + bb < nb) {
+            blk_base[(long)(b0 + bb) * E + e] = run;
+            run += t[bb];
+          }
         }
       }
     }
   }
-  if (e == 0) off[E] = total;
+  if (e == 0) off[E] = tot[0];
+  // row-tile prefix sums of every table, and their row tile -> group maps
+#pragma unroll
   for (int i = 0; i < kNumTileSizes; i++) {
-    const int bm = kTileSizes[i];
-    // (the K-grouped chunk table gives an empty group one empty chunk, which writes its zeros)
-    const int tiles = e < E ? (i == kGkChunkTable ? max(1, (cnt + bm - 1) / bm) : (cnt + bm - 1) / bm) : 0;
-    int ttot;
-    const int ts = block_exscan_1024(tiles, sh, &ttot);
+    const int ts = base[1 + i] + x[1 + i] - v[1 + i];
     if (e < E) tile_tables[i * (E + 1) + e] = ts;
-    if (e == 0) tile_tables[i * (E + 1) + E] = ttot;
-    // row tile -> group map: tile t belongs to the last group whose first tile is <= t
-    if (e <= E) tsh[e] = e < E ? ts : ttot;
-    __syncthreads();
+    if (e == 0) tile_tables[i * (E + 1) + E] = tot[1 + i];
+    if (e <= E) tsh[i][e] = e < E ? ts : tot[1 + i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kNumTileSizes; i++) {
+    // tile t belongs to the last group whose first tile is <= t
     int* map = tile_maps + tile_map_offset(i, P, E);
-    for (int t = e; t < ttot; t += 1024) {
+    for (int t = e; t < tot[1 + i]; t += 1024) {
       int lo = 0, hi = E - 1;
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (tsh[mid] <= t) lo = mid; else hi = mid - 1;
+        if (tsh[i][mid] <= t) lo = mid; else hi = mid - 1;
       }
       map[t] = lo;
     }
-    __syncthreads();
   }
 }
 
@@ -299,13 +337,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ o, c
   for (int c = threadIdx.x; c * V < m; c += blockDim.x) {
     float acc[V] = {};
     for (int j0 = 0; j0 < k; j0 += kRowGroup) {
+      // unconditional loads (a slot past the token's last reads the last one, with weight 0) so that
+      // the group's rows are all in flight together
       float f[kRowGroup][V], wj[kRowGroup];
 #pragma unroll
       for (int jj = 0; jj < kRowGroup; jj++) {
-        if (j0 + jj < k) {
-          wj[jj] = w[t * k + j0 + jj];
-          Vec8<T>::load(o + (long)inv[t * k + j0 + jj] * m + c * V, f[jj]);
-        }
+        const int j = min(j0 + jj, k - 1);
+        const float wv = w[t * k + j];
+        wj[jj] = j0 + jj < k ? wv : 0.0f;
+        Vec8<T>::load(o + (long)inv[t * k + j] * m + c * V, f[jj]);
       }
 #pragma unroll
       for (int jj = 0; jj < kRowGroup; jj++) {
@@ -385,10 +425,11 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const T* __restrict__ dX
   for (int c = threadIdx.x; c * V < m; c += blockDim.x) {
     float acc[V] = {};
     for (int j0 = 0; j0 < k; j0 += kRowGroup) {
+      // unconditional loads (a slot past the token's last reads the last one and is dropped)
       float f[kRowGroup][V];
 #pragma unroll
       for (int jj = 0; jj < kRowGroup; jj++)
-        if (j0 + jj < k) Vec8<T>::load(dXp + (long)inv[t * k + j0 + jj] * m + c * V, f[jj]);
+        Vec8<T>::load(dXp + (long)inv[t * k + min(j0 + jj, k - 1)] * m + c * V, f[jj]);
 #pragma unroll
       for (int jj = 0; jj < kRowGroup; jj++) {
         if (j0 + jj < k) {
@@ -400,10 +441,9 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const T* __restrict__ dX
         float g[kRowGroup];
 #pragma unroll
         for (int jj = 0; jj < kRowGroup; jj++) {
-          if (j0 + jj < k) {
-            g[jj] = dz[t * k + j0 + jj];
-            Vec8<T>::load(WrT + (long)idx[t * k + j0 + jj] * m + c * V, f[jj]);
-          }
+          const int j = min(j0 + jj, k - 1);
+          g[jj] = dz[t * k + j];
+          Vec8<T>::load(WrT + (long)idx[t * k + j] * m + c * V, f[jj]);
         }
 #pragma unroll
         for (int jj = 0; jj < kRowGroup; jj++) {
