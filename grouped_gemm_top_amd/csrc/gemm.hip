@@ -703,16 +703,25 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
     const i32x4_t zero = {0, 0, 0, 0};
     const bf16_t* T0 = (const bf16_t*)a.TB0 + (long)e * a.tbstride;
     const bf16_t* T1 = a.TB1 ? (const bf16_t*)a.TB1 + (long)e * a.tbstride : T0;
+    // Every chunk of a stage is loaded unconditionally, all loads in flight together: a chunk past
+    // the tail's length (or outside its half's block) reads a valid address of the same operand, and
+    // the zero is selected when it is copied to LDS.
     for (int ts = 0; ts < tsteps; ts++) {
       bf16_t* sA = smem + ts * STAGE;
       bf16_t* sB = sA + A_ELEMS;
-      for (int P = tid; P < A_ELEMS / 8; P += NT) {
+      i32x4_t va[A_CPT], vb[B_CPT];
+      bool oka[A_CPT], okb[B_CPT];
+#pragma unroll
+      for (int u = 0; u < A_CPT; u++) {
+        const int P = tid + u * NT;
         const int x = P / CPR_A, q = ((P % CPR_A) ^ swz_xk<CPR_A>(x)) + ts * CPR_A;
         const int row = min(row0 + x, row_end - 1);
-        *reinterpret_cast<i32x4_t*>(lds(sA + P * 8, 16)) =
-            (q * 8 < K2) ? ld16(GCHK((const bf16_t*)a.TA + (long)row * a.lda2 + q * 8, 16)) : zero;
+        oka[u] = q * 8 < K2;
+        va[u] = ld16(GCHK((const bf16_t*)a.TA + (long)row * a.lda2 + (oka[u] ? q * 8 : 0), 16));
       }
-      for (int P = tid; P < BN * BKT / 8; P += NT) {
+#pragma unroll
+      for (int u = 0; u < B_CPT; u++) {
+        const int P = tid + u * NT;
         const bf16_t* src = nullptr;
         if constexpr (BL == LAYOUT_KX) {
           const int k = P / CPR_B, x = ((P % CPR_B) ^ swz_kx<CPR_B>(k)) * 8;
@@ -747,8 +756,15 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
             else if (k8 < 2 * r2) src = T1 + (long)jj * a.ldtb + (k8 - r2);
           }
         }
-        *reinterpret_cast<i32x4_t*>(lds(sB + P * 8, 16)) = src ? ld16(GCHK(src, 16)) : zero;
+        okb[u] = src != nullptr;
+        vb[u] = ld16(GCHK(okb[u] ? src : T0, 16));  // T0: the first chunk of this expert's factor
       }
+#pragma unroll
+      for (int u = 0; u < A_CPT; u++)
+        *reinterpret_cast<i32x4_t*>(lds(sA + (tid + u * NT) * 8, 16)) = oka[u] ? va[u] : zero;
+#pragma unroll
+      for (int u = 0; u < B_CPT; u++)
+        *reinterpret_cast<i32x4_t*>(lds(sB + (tid + u * NT) * 8, 16)) = okb[u] ? vb[u] : zero;
     }
     __syncthreads();
     compute(s0, no_side);
