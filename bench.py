@@ -270,6 +270,18 @@ def main():
     ms = start.elapsed_time(end) / args.steps
     log(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step")
 
+    # per-step distribution: each step bracketed by its own events (reported beside the mean above)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in evs:
+        e0.record()
+        step()
+        e1.record()
+    torch.cuda.synchronize()
+    per = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+    dist = {"p10": round(float(np.percentile(per, 10)), 4), "p50": round(float(np.percentile(per, 50)), 4),
+            "p90": round(float(np.percentile(per, 90)), 4)}
+    log(f"[bench] per-step ms: p10 {dist['p10']} p50 {dist['p50']} p90 {dist['p90']}")
+
     # second pass: per-stage HIP events on the launch stream
     g.moe_timing_enable(True)
     g.moe_timing_read()
@@ -321,6 +333,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_dist": dist,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
