@@ -382,7 +382,25 @@ __global__ __launch_bounds__(WM * WN * 64) void gm_mfma(GemmArgs a, int tidx, co
 
   // ---- epilogue (compile-time accumulator indices; one 32-row MFMA tile row at a time)
   OutT* C = (OutT*)a.C + (a.kchunk ? (long)blockIdx.y * a.csplit : 0L);
-  const float* bias = blockIdx.y == 0 ? a.bias : nullptr;
+  // plain store: scale and bias (of the lane's columns, loaded once at clamped columns) are applied
+  // to the accumulators here, in straight-line code, so that the store loop issues no loads: a load
+  // inside it would make every store wait for the ones before it
+  if constexpr (EPI == EPI_STORE) {
+    float bcol[TN] = {};
+    if (a.bias && (!a.kchunk || blockIdx.y == 0)) {
+#pragma unroll
+      for (int tn = 0; tn < TN; tn++) bcol[tn] = a.bias[min(j0 + wn * TN * 32 + tn * 32 + (lane & 31), a.N - 1)];
+      // wait for them here (s_waitcnt vmcnt(0), other counters untouched): the compiler moves their
+      // use into the store loop's branches, where its own waits would include the stores before
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+#pragma unroll
+    for (int tm = 0; tm < TM; tm++)
+#pragma unroll
+      for (int tn = 0; tn < TN; tn++)
+#pragma unroll
+        for (int v = 0; v < 16; v++) acc[tm][tn][v] = a.scale * acc[tm][tn][v] + bcol[tn];
+  }
   static_for<TM>([&](auto tmc) {
     constexpr int tm = decltype(tmc)::value;
     __builtin_amdgcn_sched_barrier(0);
@@ -411,10 +429,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gm_mfma(GemmArgs a, int tidx, co
             constexpr int tn = decltype(tc)::value;
             const int jj = j0 + wn * TN * 32 + tn * 32 + (lane & 31);
             if (jj < a.N) {
-              const float val = a.scale * acc[tm][tn][v];
               if constexpr (EPI == EPI_STORE) {
-                C[(long)row * a.ldc + jj] = from_f<OutT>(val + (bias ? bias[jj] : 0.0f));
+                C[(long)row * a.ldc + jj] = from_f<OutT>(acc[tm][tn][v]);  // scaled, with bias
               } else {  // EPI_SWIGLU_BWD
+                const float val = a.scale * acc[tm][tn][v];
                 const OutT* GU = (const OutT*)a.GU;
                 const float g = to_f(GU[(long)row * a.ldgu + jj]);
                 const float uu = to_f(GU[(long)row * a.ldgu + a.guup + jj]);
@@ -693,7 +711,6 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
       uch[i] = ld16(GCHK(GU + (long)grow * a.ldgu + a.guup + gcol, 16));
     }
   }
-
   // ---- Split-LoRA tail: [TA | 0] . [TB ; 0] over K2 <= 128 more reduction rows
   if (a.tail != TAIL_NONE) {
     lds_barrier();  // every wave is done with both stages
@@ -771,6 +788,42 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
     if (tsteps > 1) compute(s1, no_side);
   }
 
+  // The per-chunk side inputs (the previous output under accum; the routing weight of a row, for a
+  // row-weighted copy or the SwiGLU backward's dh; the pair id of a row, for the ds partials) are
+  // loaded before the staging, all in flight together at clamped rows, so that the store loop issues
+  // no loads: a load there would make every store wait for the ones before it.
+  i32x4_t prev[EPI == EPI_STORE ? PER : 1] = {};
+  float cw[EPI == EPI_STORE || EPI == EPI_SWIGLU_BWD ? PER : 1] = {};
+  int prow[EPI == EPI_SWIGLU_BWD ? PER : 1] = {};
+  if constexpr (EPI == EPI_SWIGLU_BWD) {
+    if (a.arow && (a.wscale || a.dspart)) {
+#pragma unroll
+      for (int i = 0; i < PER; i++) prow[i] = a.arow[min(wrow0 + (lane + 64 * i) / CH, row_end - 1)];
+      if (a.wscale) {
+#pragma unroll
+        for (int i = 0; i < PER; i++) cw[i] = a.wval[prow[i]];
+      }
+    }
+  }
+  if constexpr (EPI == EPI_STORE) {
+    if (a.accum) {
+#pragma unroll
+      for (int i = 0; i < PER; i++) {
+        const int q = lane + 64 * i;
+        const int grow = min(wrow0 + q / CH, row_end - 1);
+        const int gcol = min(j0 + wn * WC + 8 * (q % CH), a.N - 8);
+        prev[i] = ld16(GCHK(C + (long)grow * a.ldc + gcol, 16));
+      }
+    }
+    if (a.C2) {
+      int pr[PER];
+#pragma unroll
+      for (int i = 0; i < PER; i++) pr[i] = a.arow[min(wrow0 + (lane + 64 * i) / CH, row_end - 1)];
+#pragma unroll
+      for (int i = 0; i < PER; i++) cw[i] = a.wval[pr[i]];
+    }
+  }
+
   lds_barrier();  // every wave is done reading the K-tile stages
   float* stg = reinterpret_cast<float*>(smem) + wave * WR * WC;
   static_for<TM>([&](auto tmc) {
@@ -832,22 +885,21 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
         float f[8];
         rd8(r, c8, f);
         if constexpr (EPI == EPI_STORE) {
-          float prev[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-          if (a.accum) unpack8(ld16(GCHK(C + (long)grow * a.ldc + gcol, 16)), prev);
+          float pv[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+          if (a.accum) unpack8(prev[i], pv);
 #pragma unroll
-          for (int j = 0; j < 8; j++) f[j] = a.scale * f[j] + (a.bias ? a.bias[gcol + j] : 0.0f) + prev[j];
+          for (int j = 0; j < 8; j++) f[j] = a.scale * f[j] + pv[j];
           *reinterpret_cast<i32x4_t*>(GCHK(C + (long)grow * a.ldc + gcol, 16)) = pack8(f);
           if (a.C2) {  // the row-weighted copy
-            const float wr = a.wval[a.arow[grow]];
 #pragma unroll
-            for (int j = 0; j < 8; j++) f[j] *= wr;
+            for (int j = 0; j < 8; j++) f[j] *= cw[i];
             *reinterpret_cast<i32x4_t*>(GCHK((bf16_t*)a.C2 + (long)grow * a.ldc + gcol, 16)) = pack8(f);
           }
         } else {  // EPI_SWIGLU_BWD: f = dh; dg = dh u s (1 + g (1 - s)), du = dh silu(g)
           float g[8], uu[8], dg[8], du[8];
           unpack8(gch[i], g);
           unpack8(uch[i], uu);
-          const float sc = a.wscale ? a.scale * a.wval[a.arow[grow]] : a.scale;
+          const float sc = a.wscale ? a.scale * cw[i] : a.scale;
 #pragma unroll
           for (int j = 0; j < 8; j++) {
             const float dh = sc * f[j];
@@ -867,7 +919,7 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
           hdot += __shfl_xor(hdot, 4, 64);
           const int col0 = j0 + wn * WC;
           if (c8 == 0 && grow < row_end && col0 < a.N)
-            a.dspart[(long)(col0 / 64) * a.dsstride + a.arow[grow]] = hdot;
+            a.dspart[(long)(col0 / 64) * a.dsstride + prow[i]] = hdot;
         }
       }
     }
@@ -1286,7 +1338,8 @@ template <int WM, int WN, int TM, int TN, int BL, int EPI>
 hipError_t launch_gm_ring(const GemmArgs& a, int rows_bound, hipStream_t stream) {
   constexpr bool DUAL = (EPI == EPI_DUAL || EPI == EPI_SWIGLU);
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32, BNH = DUAL ? BN / 2 : BN;
-  if (!a.goff || !a.toff_all || !a.tmap_all || a.K % 64 || a.kchunk) return hipErrorInvalidValue;
+  if (!a.goff || !a.toff_all || !a.tmap_all || a.K % 64 || a.kchunk || a.bias) return hipErrorInvalidValue;
+  if (a.C2 && (!a.arow || !a.wval)) return hipErrorInvalidValue;
   if (a.tail != TAIL_NONE) {
     const int K2 = (a.tail == TAIL_SINGLE || a.tail == TAIL_SHARED) ? a.r2a : 2 * a.r2a;
     if (K2 <= 0 || K2 > 128 || K2 % 8) return hipErrorInvalidValue;

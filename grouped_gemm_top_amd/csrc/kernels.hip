@@ -18,7 +18,9 @@ namespace {
 constexpr int kMaxPerLane = 16;  // E <= 1024
 
 // z holds nsplit partial logit arrays (split_stride floats apart), summed here in split order;
-// with nsplit > 1 the sums are also written to zout.
+// with nsplit > 1 the sums are also written to zout. One wave per token; lane L holds experts
+// L + 64 q for q < NPL (NPL >= ceil(E / 64)).
+template <int NPL>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ z, int nsplit,
                                                    long split_stride, float* __restrict__ zout, int s,
                                                    int E, int k, int score, int renorm,
@@ -28,38 +30,50 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ z, 
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= s) return;
   const float* zt = z + (long)t * E;
-  float v[kMaxPerLane];
-  unsigned taken = 0;
-  const int npl = (E + 63) >> 6;
+  // Every load of the first eight partials is issued before any of them is used, at clamped
+  // expert and split indices (the surplus values are dropped), and the sums are stored only after
+  // the last load: a load issued after a store would make its wait include the store.
+  constexpr int NP = 8;
+  float part[NPL][NP];
 #pragma unroll
-  for (int q = 0; q < kMaxPerLane; q++) {
-    const int e = lane + 64 * q;
-    const bool in = q < npl && e < E;
-    float acc = -INFINITY;
-    if (in) {
-      // partials added in split order; loaded 8 at a time so that their loads overlap
-      acc = zt[e];
-      for (int p0 = 1; p0 < nsplit; p0 += 8) {
-        // loads are unconditional (a split index past the last one reads the last split) so that
-        // they issue back to back; the surplus values are dropped
-        float part[8];
+  for (int q = 0; q < NPL; q++) {
+    const int e = min(lane + 64 * q, E - 1);
 #pragma unroll
-        for (int pp = 0; pp < 8; pp++) part[pp] = zt[(long)min(p0 + pp, nsplit - 1) * split_stride + e];
-#pragma unroll
-        for (int pp = 0; pp < 8; pp++)
-          if (p0 + pp < nsplit) acc += part[pp];
-      }
-      if (nsplit > 1 && zout) zout[(long)t * E + e] = acc;
-    }
-    v[q] = acc;
-    if (!in) taken |= 1u << q;
+    for (int pp = 0; pp < NP; pp++) part[q][pp] = zt[(long)min(pp, nsplit - 1) * split_stride + e];
   }
-  float selv[kMaxPerLane];  // lane L keeps the values of slots j with j % 64 == L
+  float v[NPL];
+  unsigned taken = 0;
+#pragma unroll
+  for (int q = 0; q < NPL; q++) {
+    float acc = part[q][0];  // partials added in split order
+#pragma unroll
+    for (int pp = 1; pp < NP; pp++)
+      if (pp < nsplit) acc += part[q][pp];
+    v[q] = acc;
+  }
+  for (int p0 = NP; p0 < nsplit; p0++) {  // splits past the eighth, if any, one at a time
+#pragma unroll
+    for (int q = 0; q < NPL; q++) v[q] += zt[(long)p0 * split_stride + min(lane + 64 * q, E - 1)];
+  }
+#pragma unroll
+  for (int q = 0; q < NPL; q++) {
+    const int e = lane + 64 * q;
+    if (e < E) {
+      if (nsplit > 1 && zout) zout[(long)t * E + e] = v[q];
+    } else {
+      v[q] = -INFINITY;
+      taken |= 1u << q;
+    }
+  }
+  // k selection rounds; lane L keeps the values of the slots j with j % 64 == L
+  float selv[NPL];
+#pragma unroll
+  for (int q = 0; q < NPL; q++) selv[q] = 0.0f;
   for (int j = 0; j < k; j++) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
 #pragma unroll
-    for (int q = 0; q < kMaxPerLane; q++) {
+    for (int q = 0; q < NPL; q++) {
       if (taken & (1u << q)) continue;
       const int e = lane + 64 * q;
       if (v[q] > bv || (v[q] == bv && e < bi)) { bv = v[q]; bi = e; }
@@ -73,44 +87,40 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ z, 
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
     if ((j & 63) == lane) {
       idx[(long)t * k + j] = bi;
-      selv[j >> 6] = bv;
+#pragma unroll
+      for (int q = 0; q < NPL; q++)
+        if (q == (j >> 6)) selv[q] = bv;
     }
   }
   // scores of the selected experts
-  float denom = 1.0f;
+  float p[NPL];
+  float ps = 0.0f;
   if (score == 0) {  // softmax over all E, max-subtracted (the max is the first selection)
     const float zmax = __shfl(selv[0], 0, 64);
-    float part = 0.0f;
+    float part_sum = 0.0f;
 #pragma unroll
-    for (int q = 0; q < kMaxPerLane; q++) {
-      const int e = lane + 64 * q;
-      if (q < npl && e < E) part += expf(v[q] - zmax);
-    }
-    denom = wave_sum(part);
-    float p[kMaxPerLane];
-    float ps = 0.0f;
-    for (int jj = 0; (jj << 6) + lane < k; jj++) {
-      p[jj] = expf(selv[jj] - zmax) / denom;
-      ps += p[jj];
-    }
-    ps = wave_sum(ps);
-    for (int jj = 0; (jj << 6) + lane < k; jj++) {
-      const long o = (long)t * k + (jj << 6) + lane;
-      psel[o] = p[jj];
-      w[o] = renorm ? p[jj] / ps : p[jj];
+    for (int q = 0; q < NPL; q++)
+      if (lane + 64 * q < E) part_sum += expf(v[q] - zmax);
+    const float denom = wave_sum(part_sum);
+#pragma unroll
+    for (int q = 0; q < NPL; q++) {
+      p[q] = (q << 6) + lane < k ? expf(selv[q] - zmax) / denom : 0.0f;
+      ps += p[q];
     }
   } else {  // sigmoid
-    float p[kMaxPerLane];
-    float ps = 0.0f;
-    for (int jj = 0; (jj << 6) + lane < k; jj++) {
-      p[jj] = 1.0f / (1.0f + expf(-selv[jj]));
-      ps += p[jj];
+#pragma unroll
+    for (int q = 0; q < NPL; q++) {
+      p[q] = (q << 6) + lane < k ? 1.0f / (1.0f + expf(-selv[q])) : 0.0f;
+      ps += p[q];
     }
-    ps = wave_sum(ps);
-    for (int jj = 0; (jj << 6) + lane < k; jj++) {
-      const long o = (long)t * k + (jj << 6) + lane;
-      psel[o] = p[jj];
-      w[o] = renorm ? p[jj] / ps : p[jj];
+  }
+  ps = wave_sum(ps);
+#pragma unroll
+  for (int q = 0; q < NPL; q++) {
+    if ((q << 6) + lane < k) {
+      const long o = (long)t * k + (q << 6) + lane;
+      psel[o] = p[q];
+      w[o] = renorm ? p[q] / ps : p[q];
     }
   }
 }
@@ -155,7 +165,6 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ blk_
   constexpr int NV = 1 + kNumTileSizes;  // expert row count, then its row-tile count in every table
   constexpr int kKeep = 64;              // per-block counts kept in registers up to this many blocks
   __shared__ int wsum[16][NV];
-  __shared__ int tsh[kNumTileSizes][1025];
   const int e = threadIdx.x, lane = e & 63, wv = e >> 6;
   const bool keep = nb <= kKeep;
   // per-block counts of expert e (one pass; all loads in flight together)
@@ -249,26 +258,16 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ blk_
     }
   }
   if (e == 0) off[E] = tot[0];
-  // row-tile prefix sums of every table, and their row tile -> group maps
+  // row-tile prefix sums of every table, and their row tile -> group maps: the thread of group e
+  // writes the entries of e's own tiles (no search, no second barrier)
 #pragma unroll
   for (int i = 0; i < kNumTileSizes; i++) {
     const int ts = base[1 + i] + x[1 + i] - v[1 + i];
     if (e < E) tile_tables[i * (E + 1) + e] = ts;
     if (e == 0) tile_tables[i * (E + 1) + E] = tot[1 + i];
-    if (e <= E) tsh[i][e] = e < E ? ts : tot[1 + i];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < kNumTileSizes; i++) {
-    // tile t belongs to the last group whose first tile is <= t
-    int* map = tile_maps + tile_map_offset(i, P, E);
-    for (int t = e; t < tot[1 + i]; t += 1024) {
-      int lo = 0, hi = E - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (tsh[i][mid] <= t) lo = mid; else hi = mid - 1;
-      }
-      map[t] = lo;
+    if (e < E) {
+      int* map = tile_maps + tile_map_offset(i, P, E) + ts;
+      for (int t = 0; t < v[1 + i]; t++) map[t] = e;
     }
   }
 }
@@ -548,8 +547,25 @@ __global__ void zero_kernel(int* p, size_t n) {
 hipError_t launch_topk(const float* z, int nsplit, long split_stride, float* zout, int s, int E,
                        int k, int score, int renorm, int* idx, float* w, float* psel, hipStream_t st) {
   if (s <= 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3((s + 3) / 4), dim3(256), 0, st, z, nsplit, split_stride, zout,
-                     s, E, k, score, renorm, idx, w, psel);
+  const dim3 grid((s + 3) / 4);
+  const int npl = (E + 63) / 64;
+  if (npl <= 1)
+    hipLaunchKernelGGL(topk_kernel<1>, grid, dim3(256), 0, st, z, nsplit, split_stride, zout, s, E, k, score,
+                       renorm, idx, w, psel);
+  else if (npl <= 2)
+    hipLaunchKernelGGL(topk_kernel<2>, grid, dim3(256), 0, st, z, nsplit, split_stride, zout, s, E, k, score,
+                       renorm, idx, w, psel);
+  else if (npl <= 4)
+    hipLaunchKernelGGL(topk_kernel<4>, grid, dim3(256), 0, st, z, nsplit, split_stride, zout, s, E, k, score,
+                       renorm, idx, w, psel);
+  else if (npl <= 8)
+    hipLaunchKernelGGL(topk_kernel<8>, grid, dim3(256), 0, st, z, nsplit, split_stride, zout, s, E, k, score,
+                       renorm, idx, w, psel);
+  else if (npl <= kMaxPerLane)
+    hipLaunchKernelGGL(topk_kernel<kMaxPerLane>, grid, dim3(256), 0, st, z, nsplit, split_stride, zout, s, E, k,
+                       score, renorm, idx, w, psel);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

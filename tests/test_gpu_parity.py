@@ -247,14 +247,18 @@ def test_merged_weights_fused_gate_up(out_in, cuda):
 
 
 # Degenerate and extreme shapes of the routing: every expert chosen by every token, one expert per
-# token, a single token, the largest expert count (most experts empty), and sigmoid scores without
-# renormalisation (the router gradient then has no coupling between a token's slots).
+# token, a single token, the largest expert count (most experts empty), sigmoid scores without
+# renormalisation (the router gradient then has no coupling between a token's slots), and expert
+# counts that are not a multiple of the wave width.
 EDGE = {
     "k_equals_E": config("qwen3_30b_a3b", s=64, m=128, n=64, E=8, k=8),
     "k_one": config("qwen3_30b_a3b", s=200, m=128, n=64, E=16, k=1),
     "one_token": config("qwen3_30b_a3b", s=1, m=128, n=64, E=8, k=2),
     "max_experts": config("qwen3_30b_a3b", s=300, m=128, n=64, E=1024, k=4),
     "sigmoid_no_renorm": config("deepseek_v3", s=256, m=128, n=64, E=16, k=4, renormalize=False),
+    # expert counts that fill 4 and 8 slots per lane of the top-k wave, the last slot partly
+    "experts_200_sigmoid_bias": config("deepseek_v3", s=160, m=128, n=64, E=200, k=8, zipf=0.8),
+    "experts_320": config("qwen3_30b_a3b", s=160, m=128, n=64, E=320, k=6),
 }
 
 
