@@ -248,8 +248,8 @@ def test_merged_weights_fused_gate_up(out_in, cuda):
 
 # Degenerate and extreme shapes of the routing: every expert chosen by every token, one expert per
 # token, a single token, the largest expert count (most experts empty), sigmoid scores without
-# renormalisation (the router gradient then has no coupling between a token's slots), and expert
-# counts that are not a multiple of the wave width.
+# renormalisation (the router gradient then has no coupling between a token's slots), expert
+# counts that are not a multiple of the wave width, and more slots per token than a wave has lanes.
 EDGE = {
     "k_equals_E": config("qwen3_30b_a3b", s=64, m=128, n=64, E=8, k=8),
     "k_one": config("qwen3_30b_a3b", s=200, m=128, n=64, E=16, k=1),
@@ -259,6 +259,8 @@ EDGE = {
     # expert counts that fill 4 and 8 slots per lane of the top-k wave, the last slot partly
     "experts_200_sigmoid_bias": config("deepseek_v3", s=160, m=128, n=64, E=200, k=8, zipf=0.8),
     "experts_320": config("qwen3_30b_a3b", s=160, m=128, n=64, E=320, k=6),
+    # more than 64 slots per token: a token's slots span two waves' worth of lanes
+    "k_over_64": config("qwen3_30b_a3b", s=40, m=128, n=64, E=96, k=72),
 }
 
 
