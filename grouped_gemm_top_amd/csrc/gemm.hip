@@ -945,7 +945,8 @@ __device__ inline void gk_store(const GemmArgs& a, int e, int row, int col, floa
 // one chunk stores its result directly; the chunks of a longer group store fp32 partials, which
 // gk_reduce adds up in chunk order after the launch.
 template <int WM, int WN, int TM, int TN>
-__global__ __launch_bounds__(WM * WN * 64) void gk_mfma(GemmArgs a, const int* toffc, const int* tmapc) {
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void gk_mfma(GemmArgs a, const int* toffc, const int* tmapc) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32, NT = WM * WN * 64;
   // both operands have the output axis contiguous: unpadded rows of BM (BN) elements, 16-byte chunks
   // XOR-swizzled by row (swz_kx) so that the transposing fragment reads are free of bank conflicts
