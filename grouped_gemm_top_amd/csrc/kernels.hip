@@ -157,13 +157,14 @@ __global__ __launch_bounds__(256) void hist_rank_kernel(const int* __restrict__ 
   }
 }
 
+// kKeep: per-block counts kept in registers up to this many blocks (past it they are read twice)
+template <int kKeep>
 __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ blk_hist, int nb, int E,
                                                     int P, int* __restrict__ blk_base,
                                                     int* __restrict__ off,
                                                     int* __restrict__ tile_tables,
                                                     int* __restrict__ tile_maps) {
   constexpr int NV = 1 + kNumTileSizes;  // expert row count, then its row-tile count in every table
-  constexpr int kKeep = 64;              // per-block counts kept in registers up to this many blocks
   __shared__ int wsum[16][NV];
   const int e = threadIdx.x, lane = e & 63, wv = e >> 6;
   const bool keep = nb <= kKeep;
@@ -357,41 +358,60 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ o, c
     Vec8<T>::store(Y + t * m + c * V, acc);
   }
 }
-// One block per group of whole tokens (256 / k of them): the block first adds up the ds partials of its
-// pairs (ds[p] = sum over q < nparts of part[q * P + p], in order of q; coalesced over p), then one
-// thread per token forms dz.
+// One block per group of whole tokens (256 / k of them), in three steps through LDS:
+// 1. each pair adds up its ds partials (ds[p] = sum over q < nparts of part[q * P + p], in order of q;
+//    coalesced over p, sixteen partials in flight at a time) and loads its w and psel;
+// 2. one thread per token forms wds = sum_j w_j ds_j and S = sum_j psel_j (slots in order);
+// 3. each pair forms its dz.
+// Every load of a step is issued before its values are used and no load follows a store.
 constexpr int kRouterMaxK = 1024;
 __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict__ part, int nparts,
                                                          const float* __restrict__ w,
                                                          const float* __restrict__ psel, int s, int k,
                                                          int score, int renorm, float* __restrict__ dz) {
-  __shared__ float dsh[kRouterMaxK > 256 ? kRouterMaxK : 256];
+  constexpr int NB = kRouterMaxK > 256 ? kRouterMaxK : 256;
+  __shared__ float dsh[NB], wsh[NB], psh[NB];
+  __shared__ float twds[256], tS[256];
   const int TB = max(1, 256 / k);
   const long t0 = (long)blockIdx.x * TB;
   const int ntok = (int)min((long)TB, (long)s - t0);
   const long P = (long)s * k, p0 = t0 * k;
+  constexpr int NQ = 16;
   for (int i = threadIdx.x; i < ntok * k; i += blockDim.x) {
+    const float* pp = part + p0 + i;
+    const float wv = w[p0 + i], pv = psel[p0 + i];
     float v = 0.0f;
-    for (int q = 0; q < nparts; q++) v += part[q * P + p0 + i];
+    for (int q0 = 0; q0 < nparts; q0 += NQ) {
+      float f[NQ];
+#pragma unroll
+      for (int q = 0; q < NQ; q++) f[q] = pp[(long)min(q0 + q, nparts - 1) * P];
+#pragma unroll
+      for (int q = 0; q < NQ; q++)
+        if (q0 + q < nparts) v += f[q];
+    }
     dsh[i] = v;
+    wsh[i] = wv;
+    psh[i] = pv;
   }
   __syncthreads();
-  if ((int)threadIdx.x >= ntok) return;
-  const long t = t0 + threadIdx.x;
-  const float* dst = dsh + threadIdx.x * k;
-  const float* wt = w + t * k;
-  const float* pt = psel + t * k;
-  float wds = 0.0f, S = 0.0f;
-  for (int j = 0; j < k; j++) {
-    wds += wt[j] * dst[j];
-    S += pt[j];
+  for (int tt = threadIdx.x; tt < ntok; tt += blockDim.x) {
+    float wds = 0.0f, S = 0.0f;
+    for (int j = 0; j < k; j++) {
+      wds += wsh[tt * k + j] * dsh[tt * k + j];
+      S += psh[tt * k + j];
+    }
+    twds[tt] = wds;
+    tS[tt] = S;
   }
-  for (int j = 0; j < k; j++) {
+  __syncthreads();
+  for (int i = threadIdx.x; i < ntok * k; i += blockDim.x) {
+    const int tt = i / k;
+    const float d = dsh[i], wj = wsh[i], pj = psh[i], wds = twds[tt];
     float g;
-    if (score == 0) g = wt[j] * (dst[j] - wds);  // softmax + renormalise
-    else if (renorm) g = pt[j] * (1.0f - pt[j]) / S * (dst[j] - wds);
-    else g = pt[j] * (1.0f - pt[j]) * dst[j];
-    dz[t * k + j] = g;
+    if (score == 0) g = wj * (d - wds);  // softmax + renormalise
+    else if (renorm) g = pj * (1.0f - pj) / tS[tt] * (d - wds);
+    else g = pj * (1.0f - pj) * d;
+    dz[p0 + i] = g;
   }
 }
 
@@ -580,8 +600,12 @@ hipError_t launch_hist_rank(const int* idx, int s, int k, int E, int* blk_hist, 
 
 hipError_t launch_scan(const int* blk_hist, int nb, int E, int P, int* blk_base, int* off,
                        int* tile_tables, int* tile_maps, hipStream_t st) {
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, blk_hist, nb, E, P, blk_base, off,
-                     tile_tables, tile_maps);
+  if (nb <= 16)
+    hipLaunchKernelGGL(scan_kernel<16>, dim3(1), dim3(1024), 0, st, blk_hist, nb, E, P, blk_base, off,
+                       tile_tables, tile_maps);
+  else
+    hipLaunchKernelGGL(scan_kernel<64>, dim3(1), dim3(1024), 0, st, blk_hist, nb, E, P, blk_base, off,
+                       tile_tables, tile_maps);
   return hipGetLastError();
 }
 
