@@ -41,10 +41,12 @@ struct RouteState {
 };
 
 // K splits of the router-logit GEMM: enough workgroups to fill the chip, chunks of >= 256.
+// K splits of the router-logit GEMM (64 x 128 tiles): enough workgroups for the chip (about 256), each
+// split at least 256 long; every split adds s x E fp32 partials that top-k reads back.
 inline int route_ksplit(const moe_shape& s) {
-  const long tiles = ((long)s.s + 127) / 128 * (((long)s.E + 127) / 128);
+  const long tiles = ((long)s.s + 63) / 64 * (((long)s.E + 127) / 128);
   int n = 1;
-  while (n < 8 && tiles * n < 512 && (s.m % (2 * n * 256)) == 0) n *= 2;
+  while (n < 8 && tiles * n < 256 && (s.m % (2 * n * 256)) == 0) n *= 2;
   return n;
 }
 

@@ -1287,6 +1287,7 @@ hipError_t launch_gm_mfma(const GemmArgs& a, int rows_bound, hipStream_t stream)
 using CfgSkinny = TileCfg<4, 1, 1, 1, 64, 2>;      // 128 x 32
 using CfgSkinnyDual = TileCfg<4, 1, 1, 2, 64, 2>;  // 128 x (32 + 32)
 using CfgMid = TileCfg<2, 2, 2, 2, 64, 2>;         // 128 x 128
+using CfgRouter = TileCfg<2, 2, 1, 2, 64, 2>;      // 64 x 128: the router logits (fp32 out, split over K)
 
 template <int WM, int WN, int TM, int TN, int BL, int EPI>
 hipError_t launch_gm_ring(const GemmArgs& a, int rows_bound, hipStream_t stream);
@@ -1312,6 +1313,9 @@ hipError_t dispatch_gm_mfma(const GemmArgs& a, int rows_bound, hipStream_t strea
     return launch_gm_mfma<CfgMid, BL, EPI, OutT>(a, rows_bound, stream);
   } else {
     if (a.N <= 32) return launch_gm_mfma<CfgSkinny, BL, EPI, OutT>(a, rows_bound, stream);
+    if constexpr (std::is_same<OutT, float>::value && EPI == EPI_STORE) {
+      if (!a.goff) return launch_gm_mfma<CfgRouter, BL, EPI, OutT>(a, rows_bound, stream);
+    }
     return launch_gm_mfma<CfgMid, BL, EPI, OutT>(a, rows_bound, stream);
   }
 }
