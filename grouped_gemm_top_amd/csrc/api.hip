@@ -397,6 +397,7 @@ struct RowWeights {
   int k;
   const float* w;
   float* ds;  // when set: ds partials of every pair, [ds_parts(s)][P] (see moe_lora_backward)
+  bool tdw_ready;  // w * Tc_d rows are already in the workspace's Tdw
 };
 
 // Row grouping of the expert GEMMs: G groups of rows (off[G + 1]); grouped row i reads activation
@@ -669,15 +670,17 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
   // dY rows and apply s_{t,j}. The combine's gradient in the routing weights, ds_{t,j} = dY_t . o_{t,j},
   // equals h . (dY_t W_d^T + Uc A_d^T) for the row's h (o = h W_d + c (h A_d) B_d), so the down
   // projection's backward leaves it as partials over 64-column blocks (with the router gradient).
-  const RowWeights rw{perm, s.k, topk_w, s.router_grad ? b.ds : nullptr};
+  // Two small independent jobs in one launch: w * Tc_d rows for dB_d, and the W_r^T rows the unpermute
+  // reads for the router's term of dX.
+  STAGE(ST_BWD_ROUTER, launch_bwd_prep(s.dtype, f.Td, perm, topk_w, b.Tdw, P, s.r, s.router_grad ? W_r : nullptr,
+                                       b.WrT, s.m, s.E, hs));
+  const RowWeights rw{perm, s.k, topk_w, s.router_grad ? b.ds : nullptr, true};
   HIP_TRY_STATUS(backward_experts(s, gr, X, dY, &rw, W_gu, W_d, A_g, B_g, A_u, B_u, A_d, B_d, f, b, b.dXp, 0,
                                   dA_g, dB_g, dA_u, dB_u, dA_d, dB_d, hs));
-  // router backward: dz on the selected logits; W_r^T rows for the unpermute
-  if (s.router_grad) {
+  // router backward: dz on the selected logits
+  if (s.router_grad)
     STAGE(ST_BWD_ROUTER, launch_router_bwd(b.ds, ds_parts(s), topk_w, rs.psel, s.s, s.k, s.score, s.renormalize,
                                            b.dz, hs));
-    STAGE(ST_BWD_ROUTER, launch_transpose(s.dtype, W_r, b.WrT, s.m, s.E, 1, hs));
-  }
   // unpermute: dX[t] = sum_j dXp[inv[t k + j]] (+ sum_j dz[t,j] W_r[:, idx[t,j]])
   STAGE(ST_BWD_UNPERMUTE, launch_unpermute(s.dtype, b.dXp, inv_perm, s.router_grad ? b.dz : nullptr, topk_idx,
                            b.WrT, dX, s.s, s.k, s.m, hs));
@@ -773,7 +776,7 @@ static moe_status backward_experts(const moe_shape& s, const Grouping& gr, const
     a.A = dO; a.lda = s.m;
     a.B = f.Td; a.ldb = s.r;
     if (rw) {
-      STAGE(ST_BWD_GRAD_D, launch_row_weight(s.dtype, f.Td, rw->pair, rw->w, b.Tdw, P, s.r, hs));
+      if (!rw->tdw_ready) STAGE(ST_BWD_GRAD_D, launch_row_weight(s.dtype, f.Td, rw->pair, rw->w, b.Tdw, P, s.r, hs));
       a.arow = rw->pair; a.arow_div = rw->k;
       a.B = b.Tdw;
     }

@@ -44,6 +44,10 @@ hipError_t launch_zero(void* p, size_t words, hipStream_t st);
 // out[i, :] = w[pair[i]] * in[i, :] (rows x cols, rounded to dtype)
 hipError_t launch_row_weight(int dtype, const void* in, const int* pair, const float* w, void* out, long rows,
                              int cols, hipStream_t st);
+// row_weight (in -> out over rows x cols) and, when W is given, the transpose of W [trows, tcols] into WT,
+// in one launch.
+hipError_t launch_bwd_prep(int dtype, const void* in, const int* pair, const float* w, void* out, long rows,
+                           int cols, const void* W, void* WT, int trows, int tcols, hipStream_t st);
 
 // Wo = W + c A B over one projection block of every expert (see merge_kernel): kx selects the
 // x.W orientation (off = i * ld + j + col0) over the output-major one ((j + col0) * ld + i).

@@ -557,6 +557,37 @@ __global__ void row_weight_kernel(const T* __restrict__ in, const int* __restric
   }
 }
 
+// Two independent jobs of the routed backward in one launch: blocks [0, rw_blocks) form
+// out[i, :] = w[pair[i]] * in[i, :] (as row_weight_kernel); the blocks after them transpose W [trows,
+// tcols] into WT [tcols, trows] in 32 x 32 tiles (as transpose_kernel), when W is given.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ in, const int* __restrict__ pair,
+                                                       const float* __restrict__ w, T* __restrict__ out,
+                                                       long rows, int cols, int rw_blocks,
+                                                       const T* __restrict__ W, T* __restrict__ WT, int trows,
+                                                       int tcols) {
+  if ((int)blockIdx.x < rw_blocks) {
+    const long n = rows * cols;
+    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)rw_blocks * blockDim.x)
+      out[i] = from_f<T>(w[pair[i / cols]] * to_f(in[i]));
+    return;
+  }
+  __shared__ T tile[32][33];
+  const int gx = (tcols + 31) / 32;
+  const int tb = (int)blockIdx.x - rw_blocks;
+  const int bx = (tb % gx) * 32, by = (tb / gx) * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+  for (int yy = ty; yy < 32; yy += 8) {
+    const int r = by + yy, c = bx + tx;
+    if (r < trows && c < tcols) tile[yy][tx] = W[(long)r * tcols + c];
+  }
+  __syncthreads();
+  for (int yy = ty; yy < 32; yy += 8) {
+    const int r = bx + yy, c = by + tx;  // output row = input column
+    if (r < tcols && c < trows) WT[(long)r * trows + c] = tile[tx][yy];
+  }
+}
+
 __global__ void zero_kernel(int* p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
     p[i] = 0;
@@ -686,6 +717,23 @@ hipError_t launch_row_weight(int dtype, const void* in, const int* pair, const f
   else
     hipLaunchKernelGGL(row_weight_kernel<float>, dim3(blocks), dim3(256), 0, st, (const float*)in, pair, w,
                        (float*)out, rows, cols);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_prep(int dtype, const void* in, const int* pair, const float* w, void* out, long rows,
+                           int cols, const void* W, void* WT, int trows, int tcols, hipStream_t st) {
+  const long n = rows * cols;
+  const int rw_blocks = (int)std::min<long>((n + 255) / 256, 2048);
+  const int tr_blocks = W ? ((tcols + 31) / 32) * ((trows + 31) / 32) : 0;
+  if (rw_blocks + tr_blocks <= 0) return hipSuccess;
+  if (dtype)
+    hipLaunchKernelGGL(bwd_prep_kernel<bf16_t>, dim3((unsigned)(rw_blocks + tr_blocks)), dim3(256), 0, st,
+                       (const bf16_t*)in, pair, w, (bf16_t*)out, rows, cols, rw_blocks, (const bf16_t*)W,
+                       (bf16_t*)WT, trows, tcols);
+  else
+    hipLaunchKernelGGL(bwd_prep_kernel<float>, dim3((unsigned)(rw_blocks + tr_blocks)), dim3(256), 0, st,
+                       (const float*)in, pair, w, (float*)out, rows, cols, rw_blocks, (const float*)W,
+                       (float*)WT, trows, tcols);
   return hipGetLastError();
 }
 
