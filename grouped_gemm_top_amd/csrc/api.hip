@@ -397,7 +397,6 @@ struct RowWeights {
   int k;
   const float* w;
   float* ds;  // when set: ds partials of every pair, [ds_parts(s)][P] (see moe_lora_backward)
-  bool tdw_ready;  // w * Tc_d rows are already in the workspace's Tdw
 };
 
 // Row grouping of the expert GEMMs: G groups of rows (off[G + 1]); grouped row i reads activation
@@ -674,7 +673,7 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
   // reads for the router's term of dX.
   STAGE(ST_BWD_ROUTER, launch_bwd_prep(s.dtype, f.Td, perm, topk_w, b.Tdw, P, s.r, s.router_grad ? W_r : nullptr,
                                        b.WrT, s.m, s.E, hs));
-  const RowWeights rw{perm, s.k, topk_w, s.router_grad ? b.ds : nullptr, true};
+  const RowWeights rw{perm, s.k, topk_w, s.router_grad ? b.ds : nullptr};
   HIP_TRY_STATUS(backward_experts(s, gr, X, dY, &rw, W_gu, W_d, A_g, B_g, A_u, B_u, A_d, B_d, f, b, b.dXp, 0,
                                   dA_g, dB_g, dA_u, dB_u, dA_d, dB_d, hs));
   // router backward: dz on the selected logits
@@ -775,8 +774,7 @@ static moe_status backward_experts(const moe_shape& s, const Grouping& gr, const
     a.M = s.m; a.N = s.r;
     a.A = dO; a.lda = s.m;
     a.B = f.Td; a.ldb = s.r;
-    if (rw) {
-      if (!rw->tdw_ready) STAGE(ST_BWD_GRAD_D, launch_row_weight(s.dtype, f.Td, rw->pair, rw->w, b.Tdw, P, s.r, hs));
+    if (rw) {  // w * Tc_d rows: formed by the caller (launch_bwd_prep) before the expert backward
       a.arow = rw->pair; a.arow_div = rw->k;
       a.B = b.Tdw;
     }

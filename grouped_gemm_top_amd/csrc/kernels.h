@@ -41,11 +41,8 @@ hipError_t launch_unpermute(int dtype, const void* dXp, const int* inv, const fl
                             hipStream_t st);
 // zero-fill n 32-bit words
 hipError_t launch_zero(void* p, size_t words, hipStream_t st);
-// out[i, :] = w[pair[i]] * in[i, :] (rows x cols, rounded to dtype)
-hipError_t launch_row_weight(int dtype, const void* in, const int* pair, const float* w, void* out, long rows,
-                             int cols, hipStream_t st);
-// row_weight (in -> out over rows x cols) and, when W is given, the transpose of W [trows, tcols] into WT,
-// in one launch.
+// The row-weighted rows out[i, :] = w[pair[i]] * in[i, :] (rows x cols, rounded to dtype) and, when W is
+// given, the transpose of W [trows, tcols] into WT, in one launch.
 hipError_t launch_bwd_prep(int dtype, const void* in, const int* pair, const float* w, void* out, long rows,
                            int cols, const void* W, void* WT, int trows, int tcols, hipStream_t st);
 

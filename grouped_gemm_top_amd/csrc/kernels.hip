@@ -546,20 +546,9 @@ __global__ void one_group_tables_kernel(int rows, int* off, int* tiles, int* map
   for (long i = (long)blockIdx.x * blockDim.x + t; i < nmaps; i += (long)gridDim.x * blockDim.x) maps[i] = 0;
 }
 
-// out[i, :] = w[pair[i]] * in[i, :] for rows of `cols` elements
-template <typename T>
-__global__ void row_weight_kernel(const T* __restrict__ in, const int* __restrict__ pair,
-                                  const float* __restrict__ w, T* __restrict__ out, long rows, int cols) {
-  const long n = rows * cols;
-  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
-    const long row = i / cols;
-    out[i] = from_f<T>(w[pair[row]] * to_f(in[i]));
-  }
-}
-
-// Two independent jobs of the routed backward in one launch: blocks [0, rw_blocks) form
-// out[i, :] = w[pair[i]] * in[i, :] (as row_weight_kernel); the blocks after them transpose W [trows,
-// tcols] into WT [tcols, trows] in 32 x 32 tiles (as transpose_kernel), when W is given.
+// Two independent jobs of the routed backward in one launch: blocks [0, rw_blocks) form the row-weighted
+// rows out[i, :] = w[pair[i]] * in[i, :]; the blocks after them transpose W [trows, tcols] into
+// WT [tcols, trows] in 32 x 32 tiles (as transpose_kernel), when W is given.
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ in, const int* __restrict__ pair,
                                                        const float* __restrict__ w, T* __restrict__ out,
@@ -703,20 +692,6 @@ hipError_t launch_one_group_tables(int rows, int* off, int* tile_tables, int* ti
   const long blocks = std::min<long>((nmaps + 255) / 256, 1024);
   hipLaunchKernelGGL(one_group_tables_kernel, dim3((unsigned)std::max<long>(blocks, 1)), dim3(256), 0, st, rows,
                      off, tile_tables, tile_maps, nmaps);
-  return hipGetLastError();
-}
-
-hipError_t launch_row_weight(int dtype, const void* in, const int* pair, const float* w, void* out, long rows,
-                             int cols, hipStream_t st) {
-  const long n = rows * cols;
-  if (n <= 0) return hipSuccess;
-  const unsigned blocks = (unsigned)std::min<long>((n + 255) / 256, 2048);
-  if (dtype)
-    hipLaunchKernelGGL(row_weight_kernel<bf16_t>, dim3(blocks), dim3(256), 0, st, (const bf16_t*)in, pair, w,
-                       (bf16_t*)out, rows, cols);
-  else
-    hipLaunchKernelGGL(row_weight_kernel<float>, dim3(blocks), dim3(256), 0, st, (const float*)in, pair, w,
-                       (float*)out, rows, cols);
   return hipGetLastError();
 }
 
