@@ -397,6 +397,15 @@ struct RowWeights {
   int k;
   const float* w;
   float* ds;  // when set: ds partials of every pair, [ds_parts(s)][P] (see moe_lora_backward)
+  // The routed layer's last steps, run inside the expert backward as soon as their inputs exist: the
+  // router backward (dz, when ds is set) after the down projection's backward, and the unpermute into dX
+  // right after the dXp GEMM (while dXp is still cache-resident).
+  float* dz;
+  const float* psel;
+  const int32_t* inv;
+  const int32_t* idx;
+  const void* WrT;
+  void* dX;
 };
 
 // Row grouping of the expert GEMMs: G groups of rows (off[G + 1]); grouped row i reads activation
@@ -673,16 +682,11 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
   // reads for the router's term of dX.
   STAGE(ST_BWD_ROUTER, launch_bwd_prep(s.dtype, f.Td, perm, topk_w, b.Tdw, P, s.r, s.router_grad ? W_r : nullptr,
                                        b.WrT, s.m, s.E, hs));
-  const RowWeights rw{perm, s.k, topk_w, s.router_grad ? b.ds : nullptr};
+  // (the router backward and the unpermute run inside, as soon as their inputs exist)
+  const RowWeights rw{perm, s.k, topk_w, s.router_grad ? b.ds : nullptr, b.dz, rs.psel, inv_perm, topk_idx, b.WrT,
+                      dX};
   HIP_TRY_STATUS(backward_experts(s, gr, X, dY, &rw, W_gu, W_d, A_g, B_g, A_u, B_u, A_d, B_d, f, b, b.dXp, 0,
                                   dA_g, dB_g, dA_u, dB_u, dA_d, dB_d, hs));
-  // router backward: dz on the selected logits
-  if (s.router_grad)
-    STAGE(ST_BWD_ROUTER, launch_router_bwd(b.ds, ds_parts(s), topk_w, rs.psel, s.s, s.k, s.score, s.renormalize,
-                                           b.dz, hs));
-  // unpermute: dX[t] = sum_j dXp[inv[t k + j]] (+ sum_j dz[t,j] W_r[:, idx[t,j]])
-  STAGE(ST_BWD_UNPERMUTE, launch_unpermute(s.dtype, b.dXp, inv_perm, s.router_grad ? b.dz : nullptr, topk_idx,
-                           b.WrT, dX, s.s, s.k, s.m, hs));
   return MOE_OK;
 }
 
@@ -761,6 +765,10 @@ static moe_status backward_experts(const moe_shape& s, const Grouping& gr, const
     STAGE(ST_BWD_DOWN, gemm_gm_launch(a, out_in(s) ? LAYOUT_KX : LAYOUT_XK, EPI_SWIGLU_BWD, 0, s.dtype, Pi,
                                       ref, hs));
   }
+  // router backward (its ds partials are complete): dz on the selected logits
+  if (rw && rw->ds)
+    STAGE(ST_BWD_ROUTER, launch_router_bwd(rw->ds, ds_parts(s), rw->w, rw->psel, s.s, s.k, s.score,
+                                           s.renormalize, rw->dz, hs));
   // dA_d = h^T Uc_d ;  dB_d = Tc_d^T dO  (computed as (dO^T Tc_d)^T; routed rows: as
   // (dY_rows^T (w Tc_d))^T)
   {
@@ -823,6 +831,10 @@ static moe_status backward_experts(const moe_shape& s, const Grouping& gr, const
     STAGE(ST_BWD_GATE_UP, gemm_gm_launch(a, out_in(s) ? LAYOUT_KX : LAYOUT_XK, EPI_STORE, 0, s.dtype, Pi, ref,
                                          hs));
   }
+  // unpermute: dX[t] = sum_j dXp[inv[t k + j]] (+ sum_j dz[t,j] W_r[:, idx[t,j]])
+  if (rw && rw->dX)
+    STAGE(ST_BWD_UNPERMUTE, launch_unpermute(s.dtype, dXp_dst, rw->inv, rw->ds ? rw->dz : nullptr, rw->idx, rw->WrT,
+                                             rw->dX, s.s, s.k, s.m, hs));
   // dA_g | dA_u = Xp^T [Uc_g | Uc_u] ;  dB_g = Tc_g^T dg, dB_u = Tc_u^T du
   if (fz) {  // dA = Xp^T Uc ;  dB = Tc^T [dg | du]
     GemmArgs a = base;
