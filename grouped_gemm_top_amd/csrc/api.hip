@@ -769,27 +769,6 @@ static moe_status backward_experts(const moe_shape& s, const Grouping& gr, const
   if (rw && rw->ds)
     STAGE(ST_BWD_ROUTER, launch_router_bwd(rw->ds, ds_parts(s), rw->w, rw->psel, s.s, s.k, s.score,
                                            s.renormalize, rw->dz, hs));
-  // dA_d = h^T Uc_d ;  dB_d = Tc_d^T dO  (computed as (dO^T Tc_d)^T; routed rows: as
-  // (dY_rows^T (w Tc_d))^T)
-  {
-    GemmArgs a = base;
-    a.M = s.n; a.N = s.r;
-    a.A = f.h; a.lda = s.n;
-    a.B = rw ? b.Udw : b.Ud; a.ldb = s.r;
-    a.C = dA_d; a.ldc = s.r; a.cstride = (long)n * r;
-    gk_prep(a);
-    STAGE(ST_BWD_GRAD_D, gemm_gk_launch(a, s.dtype, ref, Pi, hs));
-    a.M = s.m; a.N = s.r;
-    a.A = dO; a.lda = s.m;
-    a.B = f.Td; a.ldb = s.r;
-    if (rw) {  // w * Tc_d rows: formed by the caller (launch_bwd_prep) before the expert backward
-      a.arow = rw->pair; a.arow_div = rw->k;
-      a.B = b.Tdw;
-    }
-    a.C = dB_d; a.ldc = s.m; a.cstride = (long)r * m; a.ctrans = 1;
-    gk_prep(a);
-    STAGE(ST_BWD_GRAD_D, gemm_gk_launch(a, s.dtype, ref, Pi, hs));
-  }
   const bool fz = fused_gu(s);
   // Uc_gu = c * [dg B_g^T | du B_u^T]  (fused pair: Uc = c * [dg | du] B^T, one product over 2n)
   if (fz) {
@@ -835,6 +814,29 @@ static moe_status backward_experts(const moe_shape& s, const Grouping& gr, const
   if (rw && rw->dX)
     STAGE(ST_BWD_UNPERMUTE, launch_unpermute(s.dtype, dXp_dst, rw->inv, rw->ds ? rw->dz : nullptr, rw->idx, rw->WrT,
                                              rw->dX, s.s, s.k, s.m, hs));
+  // (the LoRA-factor gradients run last: the dgu rows are read by the two GEMMs above while they are
+  // still cache-resident)
+  // dA_d = h^T Uc_d ;  dB_d = Tc_d^T dO  (computed as (dO^T Tc_d)^T; routed rows: as
+  // (dY_rows^T (w Tc_d))^T)
+  {
+    GemmArgs a = base;
+    a.M = s.n; a.N = s.r;
+    a.A = f.h; a.lda = s.n;
+    a.B = rw ? b.Udw : b.Ud; a.ldb = s.r;
+    a.C = dA_d; a.ldc = s.r; a.cstride = (long)n * r;
+    gk_prep(a);
+    STAGE(ST_BWD_GRAD_D, gemm_gk_launch(a, s.dtype, ref, Pi, hs));
+    a.M = s.m; a.N = s.r;
+    a.A = dO; a.lda = s.m;
+    a.B = f.Td; a.ldb = s.r;
+    if (rw) {  // w * Tc_d rows: formed by the caller (launch_bwd_prep) before the expert backward
+      a.arow = rw->pair; a.arow_div = rw->k;
+      a.B = b.Tdw;
+    }
+    a.C = dB_d; a.ldc = s.m; a.cstride = (long)r * m; a.ctrans = 1;
+    gk_prep(a);
+    STAGE(ST_BWD_GRAD_D, gemm_gk_launch(a, s.dtype, ref, Pi, hs));
+  }
   // dA_g | dA_u = Xp^T [Uc_g | Uc_u] ;  dB_g = Tc_g^T dg, dB_u = Tc_u^T du
   if (fz) {  // dA = Xp^T Uc ;  dB = Tc^T [dg | du]
     GemmArgs a = base;
