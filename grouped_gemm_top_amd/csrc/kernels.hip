@@ -20,6 +20,16 @@ constexpr int kMaxPerLane = 16;  // E <= 1024
 // z holds nsplit partial logit arrays (split_stride floats apart), summed here in split order;
 // with nsplit > 1 the sums are also written to zout. One wave per token; lane L holds experts
 // L + 64 q for q < NPL (NPL >= ceil(E / 64)).
+// A DPP move of a 32-bit value within rows of 16 lanes (CTRL: a gfx9 DPP control, all rows and banks).
+template <int CTRL>
+__device__ inline int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ inline float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
 template <int NPL>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ z, int nsplit,
                                                    long split_stride, float* __restrict__ zout, int s,
@@ -78,11 +88,28 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ z, 
       const int e = lane + 64 * q;
       if (v[q] > bv || (v[q] == bv && e < bi)) { bv = v[q]; bi = e; }
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
+    // wave argmax (larger value, then lower index): quads and rows of 16 lanes through DPP moves
+    // (quad xor 1 and 2, then rotations by 4 and 8 lanes within each row), the four row winners
+    // through readlane
+    auto take = [&](float ov, int oi) {
       if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    };
+    take(dpp_f<0xB1>(bv), dpp_i<0xB1>(bi));    // quad_perm [1, 0, 3, 2]
+    take(dpp_f<0x4E>(bv), dpp_i<0x4E>(bi));    // quad_perm [2, 3, 0, 1]
+    take(dpp_f<0x124>(bv), dpp_i<0x124>(bi));  // row_ror 4
+    take(dpp_f<0x128>(bv), dpp_i<0x128>(bi));  // row_ror 8
+    {
+      const float v16 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 16));
+      const int i16 = __builtin_amdgcn_readlane(bi, 16);
+      const float v32 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 32));
+      const int i32 = __builtin_amdgcn_readlane(bi, 32);
+      const float v48 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 48));
+      const int i48 = __builtin_amdgcn_readlane(bi, 48);
+      bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
+      bi = __builtin_amdgcn_readlane(bi, 0);
+      take(v16, i16);
+      take(v32, i32);
+      take(v48, i48);
     }
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
     if ((j & 63) == lane) {
