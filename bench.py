@@ -193,8 +193,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the layer is benchmarked on a single MI355X and multi-GPU runs are not part of "
-              "this build.", file=sys.stderr)
+              "the layer is benchmarked on a single MI355X; sharding it over several GPUs is not "
+              "implemented.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
