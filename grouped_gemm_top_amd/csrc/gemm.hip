@@ -46,35 +46,6 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 __device__ inline i32x4_t ld16(const bf16_t* p) { return *reinterpret_cast<const i32x4_t*>(p); }
 
-#ifdef MOE_GEMM_BOUNDS_CHECK
-// Checking builds (test harnesses only): every global address of the streaming kernel must lie in
-// one of the registered allocations and every LDS address inside the kernel's LDS; a stray address
-// is replaced by a valid one and flagged in *err (bit 0 global, bit 1 LDS).
-struct GemmBounds {
-  const char* lo[32];
-  const char* hi[32];
-  int n;
-  unsigned* err;
-};
-__device__ GemmBounds g_gemm_bounds;
-__device__ inline const void* gchk(const void* p, int bytes) {
-  const char* c = (const char*)p;
-  for (int i = 0; i < g_gemm_bounds.n; i++)
-    if (c >= g_gemm_bounds.lo[i] && c + bytes <= g_gemm_bounds.hi[i]) return p;
-  atomicOr(g_gemm_bounds.err, 1u);
-  return g_gemm_bounds.lo[0];
-}
-__device__ inline int lchk(int byte_off, int bytes, int limit) {
-  if (byte_off < 0 || byte_off + bytes > limit) {
-    atomicOr(g_gemm_bounds.err, 2u);
-    return 0;
-  }
-  return byte_off;
-}
-#define GCHK(p, bytes) ((std::remove_reference_t<decltype(p)>)gchk((p), (bytes)))
-#else
-#define GCHK(p, bytes) (p)
-#endif
 
 __device__ inline float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
@@ -134,25 +105,14 @@ __device__ inline bf16x8_t frag_kx_s(const bf16_t* tile, int x0, int k0, int lan
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-typedef __attribute__((address_space(1))) void gbl_void_t;
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// One 16-byte chunk per lane straight into LDS at lds_wave_base + 16 * lane.
-__device__ inline void dma16(const bf16_t* src, bf16_t* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)(lds_bf16_t*)lds_wave_base, 16, 0, 0);
-}
-
-// Wait until at most N of this wave's vector-memory operations are outstanding.
-template <int N>
-__device__ inline void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
-
-// Row-grouped MFMA GEMM.
+// Row-grouped MFMA GEMM (the router logits and the shapes no other kernel takes).
 //
-// K tiles of BKT stream through two LDS stages with gfx950's direct-to-LDS loads
-// (global_load_lds_dwordx4: lane L of a wave instruction writes the L-th 16-byte chunk of a
-// contiguous 1 KB LDS span, so each lane fetches whichever global chunk belongs at that position):
-// the loads of tile kt+1 run while tile kt is multiplied. LDS tiles are unpadded and XOR-swizzled at
-// 16-byte chunk granularity against bank conflicts of the fragment reads.
+// K tiles of BKT stream through two LDS stages: the 16-byte-per-lane register loads of tile kt+1
+// are in flight while tile kt is multiplied, then go to the other stage, and one barrier per tile
+// hands the stages over. Lane L of wave instruction i moves the L-th 16-byte chunk of a contiguous
+// 1 KB LDS span, so each lane fetches whichever global chunk belongs at that position. LDS tiles are
+// unpadded and XOR-swizzled at 16-byte chunk granularity against bank conflicts of the fragment
+// reads.
 template <int WM, int WN, int TM, int TN, int BKT, int S, int BL, int EPI, typename OutT, bool TAIL>
 __global__ __launch_bounds__(WM * WN * 64) void gm_mfma(GemmArgs a, int tidx, const int* tmap) {
   constexpr bool DUAL = (EPI == EPI_DUAL || EPI == EPI_SWIGLU);
@@ -161,9 +121,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gm_mfma(GemmArgs a, int tidx, co
   constexpr int CPR_A = BKT / 8;                                 // chunks per XK row
   constexpr int CPR_B = BN / 8;                                  // chunks per KX B row
   constexpr int A_ELEMS = BM * BKT, B_ELEMS = BN * BKT, STAGE = A_ELEMS + B_ELEMS;
-  constexpr int A_IPW = BM * BKT / 8 / 64 / NW;                  // DMA instructions per wave
+  constexpr int A_IPW = BM * BKT / 8 / 64 / NW;                  // load instructions per wave
   constexpr int B_IPW = BN * BKT / 8 / 64 / NW;
-  constexpr int IPW = A_IPW + B_IPW;
   constexpr int TAIL_STEPS = 64 / BKT;                           // LoRA tail: up to 64 reduction rows
   static_assert(A_IPW * 64 * NW * 8 == BM * BKT && B_IPW * 64 * NW * 8 == BN * BKT, "tile/wave mismatch");
   static_assert(!DUAL || (TN % 2 == 0), "dual epilogue needs an even TN");
@@ -243,16 +202,22 @@ __global__ __launch_bounds__(WM * WN * 64) void gm_mfma(GemmArgs a, int tidx, co
   // K split of this workgroup (ungrouped launches only): reduction rows [kbase, kbase + Keff)
   const int kbase = a.kchunk ? (int)blockIdx.y * a.kchunk : 0;
   const int Keff = a.kchunk ? a.kchunk : a.K;
-  // DMA of one K tile into the stage at sA (A tile) / sA + A_ELEMS (B tile)
-  auto issue = [&](bf16_t* sA, int k0) {
+  // Register loads of one K tile, and their copy into the stage at sA (A tile) / sA + A_ELEMS (B tile)
+  i32x4_t ra[A_IPW], rb[B_IPW];
+  auto gload = [&](int k0) {
     k0 += kbase;
-    bf16_t* sB = sA + A_ELEMS;
 #pragma unroll
-    for (int i = 0; i < A_IPW; i++) dma16(Ab + aoff[i] + k0, sA + (wave * A_IPW + i) * 512);
+    for (int i = 0; i < A_IPW; i++) ra[i] = ld16(Ab + aoff[i] + k0);
     const int kb = (BL == LAYOUT_KX) ? k0 * (int)a.ldb : k0;
 #pragma unroll
-    for (int i = 0; i < B_IPW; i++)
-      dma16((bup[i] ? Bug : Bg) + boff[i] + kb, sB + (wave * B_IPW + i) * 512);
+    for (int i = 0; i < B_IPW; i++) rb[i] = ld16((bup[i] ? Bug : Bg) + boff[i] + kb);
+  };
+  auto sstore = [&](bf16_t* sA) {
+    bf16_t* sB = sA + A_ELEMS;
+#pragma unroll
+    for (int i = 0; i < A_IPW; i++) *reinterpret_cast<i32x4_t*>(sA + (wave * A_IPW + i) * 512 + lane * 8) = ra[i];
+#pragma unroll
+    for (int i = 0; i < B_IPW; i++) *reinterpret_cast<i32x4_t*>(sB + (wave * B_IPW + i) * 512 + lane * 8) = rb[i];
   };
   auto wcol = [&](int tn) {
     if constexpr (DUAL) {
@@ -292,30 +257,20 @@ __global__ __launch_bounds__(WM * WN * 64) void gm_mfma(GemmArgs a, int tidx, co
       mma(fa1, fb1);
     });
   };
-  // One pipeline step: DMA of the next tile into `next` while the tile in `cur` is multiplied. The
-  // two stages are distinct, and saying so (__restrict__) lets the compiler keep the DMA in flight
-  // across the LDS fragment reads instead of draining it first.
-  auto step = [&](bf16_t* __restrict__ next, const bf16_t* __restrict__ cur, int k0_next) {
-    if (k0_next >= 0) issue(next, k0_next);
-    compute(cur);
-  };
-
-  // ---- main K loop: loads of tile kt+1 in flight while tile kt is multiplied
+  // ---- main K loop: the loads of tile kt+1 are in flight while tile kt is multiplied; they are
+  //      copied into the other stage afterwards (its readers finished before the last barrier)
   const int nk = Keff / BKT;
   bf16_t* const stage0 = smem;
   bf16_t* const stage1 = smem + STAGE;
-  issue(stage0, 0);
-  wait_vm<0>();
+  gload(0);
+  sstore(stage0);
   __syncthreads();
-  for (int kt = 0; kt < nk; kt += 2) {
-    step(stage1, stage0, kt + 1 < nk ? (kt + 1) * BKT : -1);
-    wait_vm<0>();
+  for (int kt = 0; kt < nk; kt++) {
+    const bool more = kt + 1 < nk;
+    if (more) gload((kt + 1) * BKT);
+    compute((kt & 1) ? stage1 : stage0);
+    if (more) sstore((kt & 1) ? stage0 : stage1);
     __syncthreads();
-    if (kt + 1 < nk) {
-      step(stage0, stage1, kt + 2 < nk ? (kt + 2) * BKT : -1);
-      wait_vm<0>();
-      __syncthreads();
-    }
   }
 
   // ---- Split-LoRA tail: TAIL_STEPS more K tiles [TA | 0] . [TB ; 0], zero-filled via registers
@@ -487,13 +442,6 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
   static_assert(!DUAL || TN % 2 == 0, "dual epilogue needs an even TN");
   static_assert(BL == LAYOUT_XK || CPR_B >= 4, "KX tiles need >= 4 chunks per row");
   __shared__ __attribute__((aligned(16))) bf16_t smem[SMEM_ELEMS];
-#ifdef MOE_GEMM_BOUNDS_CHECK
-  auto lds = [&](bf16_t* p, int bytes) -> bf16_t* {
-    return smem + lchk((int)((char*)p - (char*)smem), bytes, LDS_BYTES) / 2;
-  };
-#else
-  auto lds = [](bf16_t* p, int) { return p; };
-#endif
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -559,17 +507,17 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
   i32x4_t ra[4][A_CPT], rb[4][B_CPT];  // register ring: slot = tile % 4
   auto load = [&](i32x4_t(&da)[A_CPT], i32x4_t(&db)[B_CPT], int t) {
 #pragma unroll
-    for (int u = 0; u < A_CPT; u++) da[u] = ld16(GCHK(asrc[u] + t * BKT, 16));
+    for (int u = 0; u < A_CPT; u++) da[u] = ld16(asrc[u] + t * BKT);
     const long adv = t * bstep;
 #pragma unroll
-    for (int u = 0; u < B_CPT; u++) db[u] = ld16(GCHK(bsrc[u] + adv, 16));
+    for (int u = 0; u < B_CPT; u++) db[u] = ld16(bsrc[u] + adv);
   };
   auto store = [&](bf16_t* st, const i32x4_t(&da)[A_CPT], const i32x4_t(&db)[B_CPT]) {
 #pragma unroll
-    for (int u = 0; u < A_CPT; u++) *reinterpret_cast<i32x4_t*>(lds(st + (tid + u * NT) * 8, 16)) = da[u];
+    for (int u = 0; u < A_CPT; u++) *reinterpret_cast<i32x4_t*>(st + (tid + u * NT) * 8) = da[u];
 #pragma unroll
     for (int u = 0; u < B_CPT; u++)
-      *reinterpret_cast<i32x4_t*>(lds(st + A_ELEMS + (tid + u * NT) * 8, 16)) = db[u];
+      *reinterpret_cast<i32x4_t*>(st + A_ELEMS + (tid + u * NT) * 8) = db[u];
   };
   auto wcol = [&](int tn) {
     if constexpr (DUAL) {
@@ -619,15 +567,15 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
   // one 16-byte chunk c of a ring slot (c < A_CPT: A chunk c, else B chunk c - A_CPT)
   auto load1 = [&](auto cc, i32x4_t(&da)[A_CPT], i32x4_t(&db)[B_CPT], int t) {
     constexpr int c = decltype(cc)::value;
-    if constexpr (c < A_CPT) da[c] = ld16(GCHK(asrc[c] + t * BKT, 16));
-    else db[c - A_CPT] = ld16(GCHK(bsrc[c - A_CPT] + t * bstep, 16));
+    if constexpr (c < A_CPT) da[c] = ld16(asrc[c] + t * BKT);
+    else db[c - A_CPT] = ld16(bsrc[c - A_CPT] + t * bstep);
   };
   auto store1 = [&](auto cc, bf16_t* st, const i32x4_t(&da)[A_CPT], const i32x4_t(&db)[B_CPT]) {
     constexpr int c = decltype(cc)::value;
     if constexpr (c < A_CPT)
-      *reinterpret_cast<i32x4_t*>(lds(st + (tid + c * NT) * 8, 16)) = da[c];
+      *reinterpret_cast<i32x4_t*>(st + (tid + c * NT) * 8) = da[c];
     else
-      *reinterpret_cast<i32x4_t*>(lds(st + A_ELEMS + (tid + (c - A_CPT) * NT) * 8, 16)) = db[c - A_CPT];
+      *reinterpret_cast<i32x4_t*>(st + A_ELEMS + (tid + (c - A_CPT) * NT) * 8) = db[c - A_CPT];
   };
   constexpr int CPT = A_CPT + B_CPT, NSIDE = BKT / 16, CPJ = (CPT + NSIDE - 1) / NSIDE;
 
@@ -707,8 +655,8 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
       const int q = lane + 64 * i, r = q / CH, c8 = q % CH;
       const int grow = min(wrow0 + r, row_end - 1);
       const int gcol = min(j0 + wn * WC + 8 * c8, a.N - 8);
-      gch[i] = ld16(GCHK(GU + (long)grow * a.ldgu + gcol, 16));
-      uch[i] = ld16(GCHK(GU + (long)grow * a.ldgu + a.guup + gcol, 16));
+      gch[i] = ld16(GU + (long)grow * a.ldgu + gcol);
+      uch[i] = ld16(GU + (long)grow * a.ldgu + a.guup + gcol);
     }
   }
   // ---- Split-LoRA tail: [TA | 0] . [TB ; 0] over K2 <= 128 more reduction rows
@@ -734,7 +682,7 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
         const int x = P / CPR_A, q = ((P % CPR_A) ^ swz_xk<CPR_A>(x)) + ts * CPR_A;
         const int row = min(row0 + x, row_end - 1);
         oka[u] = q * 8 < K2;
-        va[u] = ld16(GCHK((const bf16_t*)a.TA + (long)row * a.lda2 + (oka[u] ? q * 8 : 0), 16));
+        va[u] = ld16((const bf16_t*)a.TA + (long)row * a.lda2 + (oka[u] ? q * 8 : 0));
       }
 #pragma unroll
       for (int u = 0; u < B_CPT; u++) {
@@ -774,14 +722,14 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
           }
         }
         okb[u] = src != nullptr;
-        vb[u] = ld16(GCHK(okb[u] ? src : T0, 16));  // T0: the first chunk of this expert's factor
+        vb[u] = ld16(okb[u] ? src : T0);  // T0: the first chunk of this expert's factor
       }
 #pragma unroll
       for (int u = 0; u < A_CPT; u++)
-        *reinterpret_cast<i32x4_t*>(lds(sA + (tid + u * NT) * 8, 16)) = oka[u] ? va[u] : zero;
+        *reinterpret_cast<i32x4_t*>(sA + (tid + u * NT) * 8) = oka[u] ? va[u] : zero;
 #pragma unroll
       for (int u = 0; u < B_CPT; u++)
-        *reinterpret_cast<i32x4_t*>(lds(sB + (tid + u * NT) * 8, 16)) = okb[u] ? vb[u] : zero;
+        *reinterpret_cast<i32x4_t*>(sB + (tid + u * NT) * 8) = okb[u] ? vb[u] : zero;
     }
     __syncthreads();
     compute(s0, no_side);
@@ -812,7 +760,7 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
         const int q = lane + 64 * i;
         const int grow = min(wrow0 + q / CH, row_end - 1);
         const int gcol = min(j0 + wn * WC + 8 * (q % CH), a.N - 8);
-        prev[i] = ld16(GCHK(C + (long)grow * a.ldc + gcol, 16));
+        prev[i] = ld16(C + (long)grow * a.ldc + gcol);
       }
     }
     if (a.C2) {
@@ -868,10 +816,10 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
           float hh[8];
 #pragma unroll
           for (int j = 0; j < 8; j++) hh[j] = silu_f(g[j]) * uu[j];
-          *reinterpret_cast<i32x4_t*>(GCHK((bf16_t*)a.H + (long)grow * a.ldh + gcol, 16)) = pack8(hh);
+          *reinterpret_cast<i32x4_t*>((bf16_t*)a.H + (long)grow * a.ldh + gcol) = pack8(hh);
         }
-        *reinterpret_cast<i32x4_t*>(GCHK(C + (long)grow * a.ldc + gcol, 16)) = pack8(g);
-        *reinterpret_cast<i32x4_t*>(GCHK(C + (long)grow * a.ldc + a.cup + gcol, 16)) = pack8(uu);
+        *reinterpret_cast<i32x4_t*>(C + (long)grow * a.ldc + gcol) = pack8(g);
+        *reinterpret_cast<i32x4_t*>(C + (long)grow * a.ldc + a.cup + gcol) = pack8(uu);
       }
     }
   } else {
@@ -889,11 +837,11 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
           if (a.accum) unpack8(prev[i], pv);
 #pragma unroll
           for (int j = 0; j < 8; j++) f[j] = a.scale * f[j] + pv[j];
-          *reinterpret_cast<i32x4_t*>(GCHK(C + (long)grow * a.ldc + gcol, 16)) = pack8(f);
+          *reinterpret_cast<i32x4_t*>(C + (long)grow * a.ldc + gcol) = pack8(f);
           if (a.C2) {  // the row-weighted copy
 #pragma unroll
             for (int j = 0; j < 8; j++) f[j] *= cw[i];
-            *reinterpret_cast<i32x4_t*>(GCHK((bf16_t*)a.C2 + (long)grow * a.ldc + gcol, 16)) = pack8(f);
+            *reinterpret_cast<i32x4_t*>((bf16_t*)a.C2 + (long)grow * a.ldc + gcol) = pack8(f);
           }
         } else {  // EPI_SWIGLU_BWD: f = dh; dg = dh u s (1 + g (1 - s)), du = dh silu(g)
           float g[8], uu[8], dg[8], du[8];
@@ -908,8 +856,8 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
             du[j] = dh * g[j] * sg;
             hdot += a.scale * f[j] * (g[j] * sg * uu[j]);
           }
-          *reinterpret_cast<i32x4_t*>(GCHK(C + (long)grow * a.ldc + gcol, 16)) = pack8(dg);
-          *reinterpret_cast<i32x4_t*>(GCHK(C + (long)grow * a.ldc + a.cup + gcol, 16)) = pack8(du);
+          *reinterpret_cast<i32x4_t*>(C + (long)grow * a.ldc + gcol) = pack8(dg);
+          *reinterpret_cast<i32x4_t*>(C + (long)grow * a.ldc + a.cup + gcol) = pack8(du);
         }
       }
       if constexpr (EPI == EPI_SWIGLU_BWD && CH == 8) {
@@ -1253,13 +1201,9 @@ hipError_t launch_gm_mfma_t(const GemmArgs& a, int rows_bound, hipStream_t strea
   constexpr bool DUAL = (EPI == EPI_DUAL || EPI == EPI_SWIGLU);
   constexpr int BNH = DUAL ? Cfg::BN / 2 : Cfg::BN;
   auto kern = gm_mfma<Cfg::WM, Cfg::WN, Cfg::TM, Cfg::TN, Cfg::BKT, Cfg::S, BL, EPI, OutT, TAIL>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)Cfg::lds_bytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // every configuration stays within the 64 KB of dynamic LDS a launch gets without raising the
+  // kernel's limit, so no per-process attribute call (and no host state) is needed
+  static_assert(Cfg::lds_bytes <= 65536, "dynamic LDS above the default launch limit");
   const int tilesN = (a.N + BNH - 1) / BNH;
   const long mtiles = a.goff ? (long)rows_bound / Cfg::BM + a.G : ((long)a.M + Cfg::BM - 1) / Cfg::BM;
   const long units = mtiles * tilesN;

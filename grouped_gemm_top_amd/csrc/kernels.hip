@@ -70,6 +70,9 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ z, 
     const int e = lane + 64 * q;
     if (e < E) {
       if (nsplit > 1 && zout) zout[(long)t * E + e] = v[q];
+      // a NaN logit ranks as -inf: never selected before a number, score 0 (and every selection
+      // round then finds a valid expert id, since (value, id) is a total order)
+      if (v[q] != v[q]) v[q] = -INFINITY;
     } else {
       v[q] = -INFINITY;
       taken |= 1u << q;

@@ -120,7 +120,8 @@ size_t moe_bwd_ws_bytes(const moe_shape* shape);
  * moe_route -- router logits, top-k selection, routing weights and grouping of the P pairs into
  * contiguous per-expert runs.
  *   logits z = X W_r (+ router_bias), fp32 accumulate. Per token the k largest logits are selected
- *   (equal logits: lower expert id first); slot j is the j-th selection. Scores: softmax over all E
+ *   (equal logits: lower expert id first; a NaN logit counts as -inf, so it is never selected
+ *   before a number, scores 0, and every id written lies in [0, E)); slot j is the j-th selection. Scores: softmax over all E
  *   (MOE_SCORE_SOFTMAX) or sigmoid; weights s_{t,j} renormalised over the k selected when
  *   shape->renormalize. Grouping: expert_off[e] = number of pairs routed to experts < e
  *   (expert_off[E] = P); perm[row] = pair id, ordered by expert then token; inv_perm[pair] = row.

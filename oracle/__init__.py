@@ -13,7 +13,7 @@ Readings taken where the pages are silent (each is listed with its reason in the
   * Router: softmax over all E logits, keep the top k, renormalise the k kept weights; the
     sigmoid variant scores each logit with 1/(1+exp(-z)) and renormalises the same way.
   * Top-k selection compares logits, larger first; equal logits go to the lower expert id.
-    The slot order j of a token is its selection order.
+    The slot order j of a token is its selection order. A NaN logit counts as -inf.
   * LoRA update of an expert projection W (x.W orientation, W in R^{m x n}) is
     (alpha/r) * (x A) B with A in R^{m x r}, B in R^{r x n}.
   * Gate/up: gate_up = [gate | up] along the output axis, h = silu(gate) * up.
@@ -31,9 +31,9 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "router_logits", "topk_experts", "routing_weights", "group_by_expert", "route",
+    "router_logits", "nan_as_neg_inf", "topk_experts", "routing_weights", "group_by_expert", "route",
     "silu", "expert_rows_forward", "expert_rows_backward", "forward", "router_backward",
-    "backward", "forward_tokens", "backward_tokens", "backward_expert", "fused_gate_up_pair",
+    "backward", "forward_tokens", "backward_tokens", "token_outputs", "backward_expert", "fused_gate_up_pair",
     "fused_gate_up_grads", "shared_expert_forward", "shared_expert_backward",
 ]
 
@@ -56,26 +56,31 @@ def router_logits(X, W_r, bias=None) -> np.ndarray:
     return z
 
 
+def nan_as_neg_inf(z) -> np.ndarray:
+    """Logits with every NaN replaced by -inf.
+
+    The pages say nothing of non-numbers. Reading taken: a NaN logit (say from a NaN in x_t or
+    in a column of W_r) counts as -inf, so it is never selected before a number and its score is
+    0 under softmax and under sigmoid. Infinite logits keep their value.
+    """
+    z = np.array(z, dtype=np.float64, copy=True)
+    z[np.isnan(z)] = -np.inf
+    return z
+
+
 def topk_experts(z, k: int) -> np.ndarray:
     """Indices of the k largest logits per token, in selection order.
 
     [ALK] routing equation, Top-k(.) over the router scores. Softmax and sigmoid are both
     increasing, so ranking the logits ranks the scores; ties go to the lower expert id
-    (np.argmax returns the first maximum).
+    (a stable sort keeps equal keys in index order). A NaN logit ranks as -inf (nan_as_neg_inf).
     """
-    z = np.array(z, dtype=np.float64, copy=True)
-    if not np.all(np.isfinite(z)):
-        raise ValueError("router logits must be finite")
+    z = nan_as_neg_inf(z)
     s, E = z.shape
     if not 1 <= k <= E:
         raise ValueError("need 1 <= k <= E")
-    idx = np.empty((s, k), dtype=np.int32)
-    rows = np.arange(s)
-    for j in range(k):
-        best = np.argmax(z, axis=1)
-        idx[:, j] = best
-        z[rows, best] = -np.inf
-    return idx
+    order = np.argsort(-z, axis=1, kind="stable")  # descending logits, equal ones by id
+    return order[:, :k].astype(np.int32)
 
 
 def routing_weights(z, idx, score: str = "softmax", renormalize: bool = True):
@@ -85,10 +90,11 @@ def routing_weights(z, idx, score: str = "softmax", renormalize: bool = True):
     softmax: p = exp(z - max z) / sum over all E; sigmoid: p = 1 / (1 + exp(-z)).
     With renormalize, s_{t,j} = p_j / sum_{j'} p_{j'} over the token's k selected experts.
     """
-    z = _f64(z)
+    z = nan_as_neg_inf(z)
     if score == "softmax":
         zmax = z.max(axis=1, keepdims=True)
-        ex = np.exp(z - zmax)
+        with np.errstate(invalid="ignore"):  # a token whose logits are all -inf: NaN weights
+            ex = np.exp(z - zmax)
         p = ex / ex.sum(axis=1, keepdims=True)
         p_sel = np.take_along_axis(p, idx.astype(np.int64), axis=1)
     elif score == "sigmoid":
@@ -413,6 +419,45 @@ def backward_tokens(tokens, dY, X, W_r, W: dict, rt: dict, alpha: float, r: int,
             dX_r, _ = router_backward(ds[None, :], sub, Wr, score, renormalize)
             out[q] += dX_r[0]
     return out
+
+
+def token_outputs(tokens, X, W: dict, rt: dict, alpha: float, r: int, dY=None, W_r=None,
+                  score: str = "softmax", renormalize: bool = True, router_grad: bool = True):
+    """y_t (and, with dY, dX_t) for the listed tokens, visiting each expert the tokens use once.
+
+    The same sums as forward_tokens / backward_tokens, ordered by expert instead of by token, so
+    that a layer with large experts needs only one expert's weights in memory at a time. Returns
+    (y [T, m], dX [T, m] or None).
+    """
+    tokens = np.asarray(tokens, dtype=np.int64)
+    c = alpha / r
+    k = rt["k"]
+    m = X.shape[1]
+    T = len(tokens)
+    y = np.zeros((T, m))
+    dx = np.zeros((T, m)) if dY is not None else None
+    ds = np.zeros((T, k))
+    users = {}
+    for q, t in enumerate(tokens):
+        for j in range(k):
+            users.setdefault(int(rt["idx"][t, j]), []).append((q, j))
+    for e in sorted(users):
+        q = np.array([u[0] for u in users[e]])
+        j = np.array([u[1] for u in users[e]])
+        ew = _expert(W, e)
+        xr = _f64(X[tokens[q]])
+        f = expert_rows_forward(xr, ew, c)
+        w = rt["w"][tokens[q], j][:, None]
+        y[q] += w * f["o"]              # a token uses an expert at most once: q has no repeats
+        if dY is not None:
+            dy = _f64(dY[tokens[q]])
+            ds[q, j] = np.einsum("ij,ij->i", dy, f["o"])
+            dx[q] += expert_rows_backward(xr, w * dy, ew, c, f)["dX"]
+    if dY is not None and router_grad:
+        sub = dict(w=rt["w"][tokens], p_sel=rt["p_sel"][tokens], idx=rt["idx"][tokens])
+        dX_r, _ = router_backward(ds, sub, W_r, score, renormalize)
+        dx += dX_r
+    return y, dx
 
 
 def backward_expert(e: int, dY, X, W: dict, rt: dict, alpha: float, r: int) -> dict:

@@ -45,9 +45,13 @@ def oracle_weights(inp, flags):
     return W
 
 
-def run_gpu(cfg, device, flags=0, router_grad=True):
+def run_gpu(cfg, device, flags=0, router_grad=True, mutate=None):
+    """One route + forward (+ backward) of cfg's seeded layer through the C ABI. mutate(inp), when
+    given, edits the host inputs first (tied logits, zero factors, non-numbers)."""
     from grouped_gemm_top_amd import layer
     inp = make_inputs(cfg, seed=0, device="cpu", with_grad_output=cfg.backward)
+    if mutate is not None:
+        mutate(inp)
     if flags & FLAG_FUSED_GU:
         inp = fuse_gate_up(inp)
     d = {k: (v.to(device) if v is not None else None) for k, v in inp.items()}
@@ -73,7 +77,10 @@ def check_routing(cfg, inp, rt):
     bias = np64(inp["router_bias"]) if inp["router_bias"] is not None else None
     z_ref = oracle.router_logits(X, Wr, bias)
     z_gpu = rt["logits"].cpu().numpy().astype(np.float64)
-    assert rel_err(z_gpu, z_ref) <= LOGIT_TOL
+    # NaN logits (from a NaN input) must be NaN on both sides; the numbers are compared
+    assert np.array_equal(np.isnan(z_gpu), np.isnan(z_ref))
+    num = ~np.isnan(z_ref)
+    assert rel_err(z_gpu[num], z_ref[num]) <= LOGIT_TOL
     ort = oracle_route_from(z_gpu, cfg)
     np.testing.assert_array_equal(rt["topk_idx"].cpu().numpy(), ort["idx"])
     np.testing.assert_array_equal(rt["expert_off"].cpu().numpy(), ort["off"])
@@ -110,10 +117,10 @@ def test_layer_parity_flags(name, mode, cuda):
     _parity(VARIANTS[name], name, FLAG_CASES[mode], cuda)
 
 
-def _parity(cfg, name, flags, cuda):
+def _parity(cfg, name, flags, cuda, mutate=None):
     _say(f"[parity] {name} flags={flags} s={cfg.s} m={cfg.m} n={cfg.n} E={cfg.E} k={cfg.k} "
          f"r={cfg.r} {cfg.dtype} {cfg.score} backward={cfg.backward}")
-    inp, out = run_gpu(cfg, cuda, flags=flags)
+    inp, out = run_gpu(cfg, cuda, flags=flags, mutate=mutate)
     ort = check_routing(cfg, inp, out["rt"])
     W = oracle_weights(inp, flags)
     X = np64(inp["X"])
@@ -135,6 +142,7 @@ def _parity(cfg, name, flags, cuda):
     _say("  rel errors: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, f"over tolerance {tol}: {bad}"
+    return inp, out
 
 
 def test_router_grad_off(cuda):
@@ -161,11 +169,18 @@ def test_zero_token_experts_get_zero_grads(cuda):
         assert torch.all(out[key][torch.as_tensor(empty, device=cuda)] == 0)
 
 
-def test_determinism(cuda):
-    cfg = VARIANTS["qwen3_small"]
-    _say("[parity] determinism qwen3_small")
+@pytest.mark.parametrize("name", ["qwen3_small", "chunked_expert", "big_expert"])
+def test_determinism(name, cuda):
+    """Two runs give bit-identical outputs and gradients: no float atomics anywhere, and the
+    chunked LoRA-gradient reductions (experts longer than one 1024-row chunk) add their partials
+    in chunk order."""
+    cfg = VARIANTS[name]
+    _say(f"[parity] determinism {name}")
     _, a = run_gpu(cfg, cuda)
     _, b = run_gpu(cfg, cuda)
+    if name == "chunked_expert":
+        cnt = np.diff(a["rt"]["expert_off"].cpu().numpy())
+        assert cnt.max() > 1024, "the layer should have an expert longer than one gradient chunk"
     for key in ("Y", "dX") + GRAD_KEYS:
         assert torch.equal(a[key], b[key]), key
 
@@ -286,3 +301,106 @@ def test_empty_batch(cuda):
     assert torch.all(rt["expert_off"] == 0)
     for key, v in grads.items():
         assert torch.all(v == 0), key
+
+
+# ---------------------------------------------------------------- the method's own special cases
+
+def _zero_rows(inp):
+    """Every fifth token's x_t = 0 (no router bias): all E logits of those tokens are exactly 0."""
+    inp["X"][::5] = 0
+
+
+def _dup_router_columns(inp):
+    """W_r[:, 2j+1] = W_r[:, 2j]: the two logits of each expert pair are equal for every token."""
+    inp["W_r"][:, 1::2] = inp["W_r"][:, 0::2]
+
+
+@pytest.mark.parametrize("name", ["qwen3_small", "deepseek_small"])
+def test_exact_ties_go_to_the_lower_expert(name, cuda):
+    """Exactly tied logits: all-zero logits select experts 0..k-1 with weights 1/k (softmax) or
+    equal sigmoid weights, and tied expert pairs are taken lower id first. The ids are checked bit-exact
+    against the oracle's selection on the GPU's logits, which holds the tie rule."""
+    cfg = VARIANTS[name]
+    _, out = _parity(cfg, f"{name}_zero_rows", 0, cuda, mutate=_zero_rows)
+    idx = out["rt"]["topk_idx"].cpu().numpy()
+    w = out["rt"]["topk_w"].cpu().numpy()
+    z = out["rt"]["logits"].cpu().numpy()
+    assert np.all(z[::5] == 0.0)
+    assert np.all(idx[::5] == np.arange(cfg.k))
+    np.testing.assert_allclose(w[::5], 1.0 / cfg.k, rtol=1e-6, atol=0)
+    _, out = _parity(cfg, f"{name}_dup_columns", 0, cuda, mutate=_dup_router_columns)
+    z = out["rt"]["logits"].cpu().numpy()
+    assert np.array_equal(z[:, 0::2], z[:, 1::2]), "duplicated W_r columns should give equal logits"
+    idx = out["rt"]["topk_idx"].cpu().numpy()
+    pos = np.full((cfg.s, cfg.E), cfg.k)
+    np.put_along_axis(pos, idx.astype(np.int64), np.arange(cfg.k)[None, :].repeat(cfg.s, 0), axis=1)
+    even, odd = pos[:, 0::2], pos[:, 1::2]
+    # of each tied pair, the lower id is selected whenever the higher one is, and before it
+    assert np.all(even[odd < cfg.k] < odd[odd < cfg.k])
+
+
+def test_alpha_zero_is_the_plain_moe_layer(cuda):
+    """alpha = 0: Y is the MoE layer without adapters and every LoRA gradient is exactly zero."""
+    cfg = config("qwen3_30b_a3b", s=512, m=256, n=192, E=16, k=4, alpha=0.0)
+    _, out = _parity(cfg, "alpha_zero", 0, cuda)
+    for key in GRAD_KEYS:
+        assert torch.count_nonzero(out[key]).item() == 0, key
+
+
+def _zero_B(inp):
+    for key in ("B_g", "B_u", "B_d"):
+        inp[key].zero_()
+
+
+def test_zero_B_gives_zero_dA(cuda):
+    """B = 0 (the usual LoRA initialisation): the adapters add nothing, dA is exactly zero and dB is
+    not."""
+    cfg = VARIANTS["qwen3_small"]
+    _, out = _parity(cfg, "zero_B", 0, cuda, mutate=_zero_B)
+    for key in ("dA_g", "dA_u", "dA_d"):
+        assert torch.count_nonzero(out[key]).item() == 0, key
+    for key in ("dB_g", "dB_u", "dB_d"):
+        assert torch.count_nonzero(out[key]).item() > 0, key
+
+
+def _nan_router_column(inp):
+    inp["W_r"][:, 5] = float("nan")
+
+
+def test_nan_router_column_is_never_selected(cuda):
+    """A NaN column of W_r gives that expert NaN logits, which count as -inf: the expert is never
+    selected, scores 0 in every softmax denominator, and the rest of the layer matches the oracle."""
+    cfg = VARIANTS["qwen3_small"]
+    _, out = _parity(cfg, "nan_router_column", 0, cuda, mutate=_nan_router_column)
+    idx = out["rt"]["topk_idx"].cpu().numpy()
+    assert not np.any(idx == 5)
+    assert torch.isfinite(out["Y"]).all() and torch.isfinite(out["dX"]).all()
+
+
+def test_nan_token_routes_to_valid_experts(cuda):
+    """A token whose x_t is NaN has only NaN logits: it is routed to experts 0..k-1 (ties at -inf go
+    to the lower id), every id stays in range, and every other token's output matches the oracle."""
+    from grouped_gemm_top_amd import layer
+    cfg = config("qwen3_30b_a3b", s=256, m=256, n=128, E=16, k=4, backward=False)
+    _say("[edge] NaN token row")
+    bad_t = 7
+    inp = make_inputs(cfg, seed=0, device="cpu", with_grad_output=False)
+    inp["X"][bad_t] = float("nan")
+    d = {k: (v.to(cuda) if v is not None else None) for k, v in inp.items()}
+    shape = layer.shape_of(cfg)
+    rt = layer.route(shape, d["X"], d["W_r"], d["router_bias"])
+    Y, _ = layer.forward(shape, d["X"], rt, d, training=False)
+    torch.cuda.synchronize()
+    idx = rt["topk_idx"].cpu().numpy()
+    assert idx.min() >= 0 and idx.max() < cfg.E
+    assert list(idx[bad_t]) == list(range(cfg.k))
+    z_gpu = rt["logits"].cpu().numpy().astype(np.float64)
+    assert np.all(np.isnan(z_gpu[bad_t]))
+    ort = oracle_route_from(z_gpu, cfg)
+    np.testing.assert_array_equal(idx, ort["idx"])
+    np.testing.assert_array_equal(rt["perm"].cpu().numpy(), ort["perm"])
+    good = np.arange(cfg.s) != bad_t
+    Xh = np64(inp["X"])
+    Xh[bad_t] = 0.0  # its rows' results are not compared
+    Y_ref, _ = oracle.forward(Xh, host_weights(inp), ort, cfg.alpha, cfg.r, keep=False)
+    assert rel_err(np64(Y)[good], Y_ref[good]) <= TOL[cfg.dtype]

@@ -121,6 +121,80 @@ def test_grouping_invariants():
 
 # ------------------------------------------------------------------------------- forward
 
+# ------------------------------------------------------------------------ router bias
+# The skewed-routing workload adds a fixed per-expert bias beta to the logits,
+# beta_e = -zipf * ln(rank_e), so that the bias alone gives a Zipf law on the experts. These pins
+# tie the oracle's logits to that law and to properties of softmax, so that a dropped or negated
+# bias fails.
+
+def test_router_bias_alone_gives_the_zipf_law():
+    rng = np.random.default_rng(21)
+    s, m, E, a = 7, 16, 12, 1.2
+    rank = rng.permutation(E) + 1.0
+    beta = -a * np.log(rank)
+    X = rng.normal(size=(s, m))
+    z = oracle.router_logits(X, np.zeros((m, E)), beta)
+    rt = oracle.route(z, E, E, "softmax")           # k = E: every expert, weights = softmax
+    zipf = rank ** -a / np.sum(rank ** -a)
+    for t in range(s):
+        assert list(rt["idx"][t]) == list(np.argsort(rank))  # rank 1 first
+        np.testing.assert_allclose(rt["p_sel"][t], zipf[rt["idx"][t]], rtol=1e-13, atol=0)
+
+
+def test_router_bias_shift_leaves_softmax_routing_unchanged():
+    rng = np.random.default_rng(22)
+    s, m, E, k = 40, 24, 10, 3
+    X, W_r = rng.normal(size=(s, m)), rng.normal(size=(m, E))
+    beta = rng.normal(size=E)
+    a = oracle.route(oracle.router_logits(X, W_r, beta), k, E, "softmax")
+    b = oracle.route(oracle.router_logits(X, W_r, beta + 3.25), k, E, "softmax")
+    assert np.array_equal(a["idx"], b["idx"])
+    np.testing.assert_allclose(a["w"], b["w"], rtol=1e-12, atol=0)
+    # and the bias does act: the logits move by exactly beta against the unbiased ones
+    z0 = oracle.router_logits(X, W_r)
+    np.testing.assert_allclose(oracle.router_logits(X, W_r, beta) - z0, np.tile(beta, (s, 1)),
+                               rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("score", ["softmax", "sigmoid"])
+def test_large_positive_bias_puts_its_expert_first(score):
+    rng = np.random.default_rng(23)
+    s, m, E, k, j = 50, 16, 9, 3, 6
+    X, W_r = rng.normal(size=(s, m)), rng.normal(size=(m, E))
+    beta = np.zeros(E)
+    beta[j] = 100.0
+    rt = oracle.route(oracle.router_logits(X, W_r, beta), k, E, score)
+    assert np.all(rt["idx"][:, 0] == j)
+    assert np.all(rt["w"][:, 0] > 1.0 / k)
+
+
+# ------------------------------------------------------------------------ non-numbers
+# Reading: a NaN logit counts as -inf (never selected before a number, score 0).
+
+def test_nan_logits_rank_below_numbers_and_ids_stay_valid():
+    rng = np.random.default_rng(24)
+    s, E, k = 30, 7, 3
+    z = rng.normal(size=(s, E))
+    z[:, 2] = np.nan                       # a NaN column: never selected while numbers remain
+    z[5, :] = np.nan                       # a NaN row: all ties at -inf -> experts 0..k-1
+    z[9, :5] = np.nan                      # fewer numbers than... still k of them
+    rt = oracle.route(z, k, E, "softmax")
+    idx = rt["idx"]
+    assert idx.min() >= 0 and idx.max() < E
+    assert all(len(set(r.tolist())) == k for r in idx)
+    assert list(idx[5]) == [0, 1, 2]
+    assert set(idx[9].tolist()) <= {5, 6, 0}  # the two numbers first, then the lowest NaN id
+    assert list(idx[9][:2]) == list(np.argsort(-z[9, 5:])[:2] + 5)
+    for t in range(s):
+        if t not in (5, 9):
+            assert 2 not in idx[t]
+            # unaffected tokens: the same selection and weights as with the column removed
+            keep = [e for e in range(E) if e != 2]
+            sub = oracle.route(z[t:t + 1, keep], k, E - 1, "softmax")
+            assert [keep[e] for e in sub["idx"][0]] == list(idx[t])
+            np.testing.assert_allclose(sub["w"][0], rt["w"][t], rtol=1e-14, atol=0)
+
+
 def test_gate_up_order_closed_form():
     fx = json.load(open(os.path.join(GOLDEN, "swiglu_gate_first.json")))
     m = n = 64
@@ -332,6 +406,9 @@ def test_sampled_outputs_equal_full_layer():
         np.testing.assert_allclose(
             oracle.backward_tokens(toks, dY, X, W_r, W, rt, alpha, r, score), g["dX"][toks],
             rtol=1e-12, atol=1e-14)
+        yt, dxt = oracle.token_outputs(toks, X, W, rt, alpha, r, dY, W_r, score)
+        np.testing.assert_allclose(yt, Y[toks], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(dxt, g["dX"][toks], rtol=1e-12, atol=1e-14)
         for e in range(E):
             ge = oracle.backward_expert(e, dY, X, W, rt, alpha, r)
             for key, v in ge.items():
