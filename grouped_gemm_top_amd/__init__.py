@@ -16,6 +16,7 @@ __all__ = [
     "MoeShape", "MoeError", "lib", "LIB_PATH", "make_shape", "moe_status_str", "moe_abi_version",
     "moe_check_shape", "moe_route_state_bytes", "moe_fwd_saved_bytes", "moe_fwd_ws_bytes",
     "moe_bwd_ws_bytes", "moe_route", "moe_lora_forward", "moe_lora_backward",
+    "moe_lora_forward_noalloc", "MOE_NOALLOC_SCRATCH_BYTES",
     "MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP",
     "MOE_FLAG_REFERENCE_GEMM", "MOE_FLAG_RSLORA", "MOE_FLAG_WEIGHTS_OUT_IN", "MOE_FLAG_MERGED", "MOE_FLAG_RECOMPUTE",
     "MOE_FLAG_FUSED_GU_LORA",
@@ -35,6 +36,7 @@ MOE_FLAG_WEIGHTS_OUT_IN = 4
 MOE_FLAG_MERGED = 8
 MOE_FLAG_RECOMPUTE = 16
 MOE_FLAG_FUSED_GU_LORA = 32
+MOE_NOALLOC_SCRATCH_BYTES = 128 << 20  # the fixed device scratch of moe_lora_forward_noalloc
 
 
 class MoeShape(ctypes.Structure):
@@ -67,6 +69,7 @@ _SIGNATURES = {
     "moe_bwd_ws_bytes": (_SZ, [_SHAPE]),
     "moe_route": (_I32, [_SHAPE] + [_P] * 10 + [_SZ, _P]),
     "moe_lora_forward": (_I32, [_SHAPE] + [_P] * 17 + [_SZ, _P, _SZ, _P]),
+    "moe_lora_forward_noalloc": (_I32, [_SHAPE] + [_P] * 17),
     "moe_lora_backward": (_I32, [_SHAPE] + [_P] * 18 + [_SZ] + [_P] * 8 + [_SZ, _P]),
     "moe_peft_merge": (_I32, [_SHAPE] + [_P] * 11),
     "moe_shared_saved_bytes": (_SZ, [_SHAPE]),
@@ -175,6 +178,15 @@ def moe_lora_forward(shape, X, topk_idx, topk_w, expert_off, perm, inv_perm, rou
         _ptr(B_u), _ptr(A_d), _ptr(B_d), _ptr(Y), _ptr(saved), _nbytes(saved), _ptr(ws),
         _nbytes(ws), _stream(stream))
     _check(st, "moe_lora_forward")
+
+
+def moe_lora_forward_noalloc(shape, X, topk_idx, topk_w, expert_off, perm, inv_perm, route_state, W_gu,
+                             W_d, A_g, B_g, A_u, B_u, A_d, B_d, Y, stream=None):
+    st = lib().moe_lora_forward_noalloc(
+        ctypes.byref(shape), _ptr(X), _ptr(topk_idx), _ptr(topk_w), _ptr(expert_off), _ptr(perm),
+        _ptr(inv_perm), _ptr(route_state), _ptr(W_gu), _ptr(W_d), _ptr(A_g), _ptr(B_g), _ptr(A_u),
+        _ptr(B_u), _ptr(A_d), _ptr(B_d), _ptr(Y), _stream(stream))
+    _check(st, "moe_lora_forward_noalloc")
 
 
 def moe_peft_merge(shape, W_gu, W_d, A_g, B_g, A_u, B_u, A_d, B_d, W_gu_merged, W_d_merged,

@@ -282,6 +282,32 @@ struct StageScope {
     HIP_TRY(x);                       \
   } while (0)
 
+// ------------------------------------------------------------------------------------------------
+// Device scratch of moe_lora_forward_noalloc: one fixed array per GPU, resident from the library's
+// load on that GPU until the process ends. Host code never uses the array's name as an address (on
+// the host it is only a stand-in for the symbol): its device address comes from hipGetSymbolAddress,
+// looked up once per device with that device current, and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (looked up on the first call on that device).
+moe_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 GemmArgs gemm_args() {
   GemmArgs a;
   std::memset(&a, 0, sizeof(a));
@@ -572,6 +598,24 @@ moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t
   // combine
   STAGE(ST_FWD_COMBINE, launch_combine(s.dtype, f.o, inv_perm, topk_w, Y, s.s, s.k, s.m, hs));
   return MOE_OK;
+}
+
+moe_status moe_lora_forward_noalloc(const moe_shape* shape, const void* X, const int32_t* topk_idx,
+                                    const float* topk_w, const int32_t* expert_off, const int32_t* perm,
+                                    const int32_t* inv_perm, const void* route_state, const void* W_gu,
+                                    const void* W_d, const void* A_g, const void* B_g, const void* A_u,
+                                    const void* B_u, const void* A_d, const void* B_d, void* Y,
+                                    void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const size_t need = moe_fwd_ws_bytes(shape, 0);
+  if (need > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need) HIP_TRY_STATUS(scratch_address(&ws));
+  // the inference forward of moe_lora_forward with the scratch as its workspace: every byte of it
+  // that a kernel reads is written earlier in the same call, so nothing needs clearing
+  return moe_lora_forward(shape, X, topk_idx, topk_w, expert_off, perm, inv_perm, route_state, W_gu, W_d,
+                          A_g, B_g, A_u, B_u, A_d, B_d, Y, nullptr, 0, ws, need, stream);
 }
 
 moe_status moe_peft_merge(const moe_shape* shape, const void* W_gu, const void* W_d, const void* A_g,

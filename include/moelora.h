@@ -176,6 +176,28 @@ moe_status moe_lora_backward(const moe_shape* shape, const void* dY, const void*
                              void* stream);
 
 /*
+ * moe_lora_forward_noalloc -- moe_lora_forward for inference (saved == NULL) that allocates
+ * nothing and takes no workspace argument: for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation). Same arguments,
+ * semantics and results as moe_lora_forward(shape, ..., Y, NULL, 0, ws, ws_bytes, stream); its
+ * scratch is a fixed array of MOE_NOALLOC_SCRATCH_BYTES in device memory that the library holds on
+ * every GPU it runs on until the process ends.
+ * Limit: moe_fwd_ws_bytes(shape, 0) <= MOE_NOALLOC_SCRATCH_BYTES (about 1 900 tokens of the
+ * Qwen3-30B-A3B layer, 128 experts, top-8); larger shapes return MOE_ERR_WORKSPACE and enqueue
+ * nothing.
+ * Every call on one GPU uses that GPU's one array: calls that overlap on a GPU (on different streams,
+ * or from several host threads without ordering) race and must not be made. Nothing needs clearing
+ * between calls; the array keeps the last call's intermediates.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+moe_status moe_lora_forward_noalloc(const moe_shape* shape, const void* X, const int32_t* topk_idx,
+                                    const float* topk_w, const int32_t* expert_off, const int32_t* perm,
+                                    const int32_t* inv_perm, const void* route_state, const void* W_gu,
+                                    const void* W_d, const void* A_g, const void* B_g, const void* A_u,
+                                    const void* B_u, const void* A_d, const void* B_d, void* Y,
+                                    void* stream);
+
+/*
  * moe_peft_merge -- the materialised form of the LoRA update that Split LoRA avoids
  * (ailinkdeeptech.com cookbook page, section "1. Standard PEFT Materialization Overhead"):
  *     W_gu' = W_gu + c [A_g B_g | A_u B_u],   W_d' = W_d + c A_d B_d      (per expert)

@@ -134,6 +134,16 @@ def test_forward_validation():
     assert _forward(sh, saved=FAKE + 16) == g.MOE_ERR_INVALID_ARG
 
 
+def test_noalloc_forward_refuses_layers_beyond_its_scratch():
+    """The no-allocation forward checks the shape and its fixed scratch before touching a device."""
+    lib = g.lib()
+    big = shape(s=1 << 20)
+    assert g.moe_fwd_ws_bytes(big, False) > g.MOE_NOALLOC_SCRATCH_BYTES
+    assert lib.moe_lora_forward_noalloc(ctypes.byref(big), *([FAKE] * 16), None) == g.MOE_ERR_WORKSPACE
+    bad = shape(m=100)
+    assert lib.moe_lora_forward_noalloc(ctypes.byref(bad), *([FAKE] * 16), None) == g.MOE_ERR_UNSUPPORTED
+
+
 def _backward(sh, ws_bytes=None, saved=FAKE, dX=FAKE):
     lib = g.lib()
     if ws_bytes is None:
