@@ -219,14 +219,14 @@ inline bool lora_ptrs_ok(const moe_shape& s, const void* A_g, const void* B_g, c
 enum Stage {
   ST_ROUTE_LOGITS, ST_ROUTE_TOPK, ST_ROUTE_HIST, ST_ROUTE_SCAN, ST_ROUTE_SCATTER,
   ST_FWD_T_GU, ST_FWD_GATE_UP, ST_FWD_T_D, ST_FWD_DOWN, ST_FWD_COMBINE,
-  ST_BWD_ROUTER, ST_BWD_U_D, ST_BWD_DOWN, ST_BWD_GRAD_D, ST_BWD_U_GU,
-  ST_BWD_GATE_UP, ST_BWD_GRAD_GU, ST_BWD_UNPERMUTE, ST_COUNT
+  ST_BWD_ROUTER, ST_BWD_U_D, ST_BWD_DOWN, ST_BWD_U_GU,
+  ST_BWD_GATE_UP, ST_BWD_UNPERMUTE, ST_BWD_GRADS, ST_COUNT
 };
 const char* const kStageNames[ST_COUNT] = {
   "route_logits", "route_topk", "route_hist_rank", "route_scan", "route_scatter",
   "fwd_lora_t_gate_up", "fwd_gate_up", "fwd_lora_t_down", "fwd_down", "fwd_combine",
-  "bwd_router", "bwd_lora_u_down", "bwd_down", "bwd_lora_grads_down",
-  "bwd_lora_u_gate_up", "bwd_gate_up", "bwd_lora_grads_gate_up", "bwd_unpermute"};
+  "bwd_router", "bwd_lora_u_down", "bwd_down",
+  "bwd_lora_u_gate_up", "bwd_gate_up", "bwd_unpermute", "bwd_lora_grads"};
 
 struct Timing {
   std::mutex mu;
@@ -752,18 +752,20 @@ static moe_status backward_experts(const moe_shape& s, const Grouping& gr, const
   const int Pi = (int)P;
   const size_t es = esize(s);
 
-  // LoRA-factor gradients (K-grouped launches): an expert longer than one row chunk leaves fp32
-  // partials in its launch's region of b.gkpart, and one reduce after the last of them completes all
+  // LoRA-factor gradients (K-grouped jobs over the same row grouping, run together in one launch
+  // after the dXp GEMM): an expert longer than one row chunk leaves fp32 partials in its job's region
+  // of b.gkpart, and one reduce after the launch completes all of them
   const bool chunked = s.dtype == MOE_DTYPE_BF16 && !ref;
   GemmArgs gk_jobs[kGkMaxJobs];
   int n_gk = 0;
   float* gk_next = b.gkpart;
   auto gk_prep = [&](GemmArgs& a) {
     a.gkpart = nullptr;
-    if (!chunked) return;
-    a.gkpart = gk_next;
-    a.gkchunk = gk_chunk_rows(s);
-    gk_next += gk_part_floats((long)P, s.E, a.M, a.N, a.gkchunk);
+    if (chunked) {
+      a.gkpart = gk_next;
+      a.gkchunk = gk_chunk_rows(s);
+      gk_next += gk_part_floats((long)P, s.E, a.M, a.N, a.gkchunk);
+    }
     gk_jobs[n_gk++] = a;
   };
 
@@ -858,8 +860,8 @@ static moe_status backward_experts(const moe_shape& s, const Grouping& gr, const
   if (rw && rw->dX)
     STAGE(ST_BWD_UNPERMUTE, launch_unpermute(s.dtype, dXp_dst, rw->inv, rw->ds ? rw->dz : nullptr, rw->idx, rw->WrT,
                                              rw->dX, s.s, s.k, s.m, hs));
-  // (the LoRA-factor gradients run last: the dgu rows are read by the two GEMMs above while they are
-  // still cache-resident)
+  // LoRA-factor gradients, all in one launch (last: the dgu rows are read by the two GEMMs above while
+  // they are still cache-resident)
   // dA_d = h^T Uc_d ;  dB_d = Tc_d^T dO  (computed as (dO^T Tc_d)^T; routed rows: as
   // (dY_rows^T (w Tc_d))^T)
   {
@@ -869,7 +871,6 @@ static moe_status backward_experts(const moe_shape& s, const Grouping& gr, const
     a.B = rw ? b.Udw : b.Ud; a.ldb = s.r;
     a.C = dA_d; a.ldc = s.r; a.cstride = (long)n * r;
     gk_prep(a);
-    STAGE(ST_BWD_GRAD_D, gemm_gk_launch(a, s.dtype, ref, Pi, hs));
     a.M = s.m; a.N = s.r;
     a.A = dO; a.lda = s.m;
     a.B = f.Td; a.ldb = s.r;
@@ -879,7 +880,6 @@ static moe_status backward_experts(const moe_shape& s, const Grouping& gr, const
     }
     a.C = dB_d; a.ldc = s.m; a.cstride = (long)r * m; a.ctrans = 1;
     gk_prep(a);
-    STAGE(ST_BWD_GRAD_D, gemm_gk_launch(a, s.dtype, ref, Pi, hs));
   }
   // dA_g | dA_u = Xp^T [Uc_g | Uc_u] ;  dB_g = Tc_g^T dg, dB_u = Tc_u^T du
   if (fz) {  // dA = Xp^T Uc ;  dB = Tc^T [dg | du]
@@ -889,15 +889,12 @@ static moe_status backward_experts(const moe_shape& s, const Grouping& gr, const
     a.B = b.Ugu; a.ldb = s.r;
     a.C = dA_g; a.ldc = s.r; a.cstride = (long)m * r;
     gk_prep(a);
-    STAGE(ST_BWD_GRAD_GU, gemm_gk_launch(a, s.dtype, ref, Pi, hs));
     GemmArgs bg = base;
     bg.M = 2 * s.n; bg.N = s.r;
     bg.A = b.dgu; bg.lda = 2 * s.n;
     bg.B = f.Tgu; bg.ldb = s.r;
     bg.C = dB_g; bg.ldc = 2 * s.n; bg.cstride = (long)r * 2 * n; bg.ctrans = 1;
     gk_prep(bg);
-    STAGE(ST_BWD_GRAD_GU, gemm_gk_launch(bg, s.dtype, ref, Pi, hs));
-    if (n_gk) STAGE(ST_BWD_GRAD_GU, gemm_gk_reduce(gk_jobs, n_gk, Pi, hs));
   } else {
     GemmArgs a = base;
     a.M = s.m; a.N = 2 * s.r;
@@ -905,24 +902,19 @@ static moe_status backward_experts(const moe_shape& s, const Grouping& gr, const
     a.B = b.Ugu; a.ldb = 2 * s.r;
     a.C = dA_g; a.C1 = dA_u; a.nsplit = s.r; a.ldc = s.r; a.cstride = (long)m * r;
     gk_prep(a);
-    STAGE(ST_BWD_GRAD_GU, gemm_gk_launch(a, s.dtype, ref, Pi, hs));
-    // dB_g and dB_u have the same shape: one launch runs both (each with its own partials)
     GemmArgs bg = base;
     bg.M = s.n; bg.N = s.r;
     bg.A = b.dgu; bg.lda = 2 * s.n;
     bg.B = f.Tgu; bg.ldb = 2 * s.r;
     bg.C = dB_g; bg.ldc = s.n; bg.cstride = (long)r * n; bg.ctrans = 1;
-    GemmArgs bu = bg;
-    bu.A = (const char*)b.dgu + n * es;
-    bu.B = (const char*)f.Tgu + r * es;
-    bu.C = dB_u;
     gk_prep(bg);
-    gk_prep(bu);
-    bg.nbatch = 2;
-    bg.bA = bu.A; bg.bB = bu.B; bg.bC = bu.C; bg.bgkpart = bu.gkpart;
-    STAGE(ST_BWD_GRAD_GU, gemm_gk_launch(bg, s.dtype, ref, Pi, hs));
-    if (n_gk) STAGE(ST_BWD_GRAD_GU, gemm_gk_reduce(gk_jobs, n_gk, Pi, hs));
+    bg.A = (const char*)b.dgu + n * es;  // dB_u: the up half of dgu against the up half of Tc_gu
+    bg.B = (const char*)f.Tgu + r * es;
+    bg.C = dB_u;
+    gk_prep(bg);
   }
+  STAGE(ST_BWD_GRADS, gemm_gk_launch(gk_jobs, n_gk, s.dtype, ref, Pi, hs));
+  if (chunked) STAGE(ST_BWD_GRADS, gemm_gk_reduce(gk_jobs, n_gk, Pi, hs));
   return MOE_OK;
 }
 

@@ -109,8 +109,11 @@ struct GemmArgs {
 // GM: rows_bound = upper bound on the total number of rows over all groups (sizes the grid).
 hipError_t gemm_gm_launch(const GemmArgs& a, int b_layout, int epi, int out_f32, int dtype,
                           int rows_bound, int reference, hipStream_t stream);
-// GK: rows_bound bounds the total group rows (sizes the chunk grid when a.gkpart is set).
-hipError_t gemm_gk_launch(const GemmArgs& a, int dtype, int reference, int rows_bound, hipStream_t stream);
+// GK: njobs <= kGkMaxJobs problems over the same row grouping (G, goff, chunk tables, and either all
+// or none with partials), in one launch. rows_bound bounds the total group rows (sizes the chunk
+// grid when gkpart is set).
+hipError_t gemm_gk_launch(const GemmArgs* jobs, int njobs, int dtype, int reference, int rows_bound,
+                          hipStream_t stream);
 
 // Row-tile tables for the MFMA row tile sizes used by gemm_gm_launch.
 constexpr int kNumTileSizes = 5;

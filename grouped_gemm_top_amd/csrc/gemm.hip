@@ -875,7 +875,8 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
 }
 
 // Stores element (row, col) of group e's K-grouped output.
-__device__ inline void gk_store(const GemmArgs& a, int e, int row, int col, float v) {
+template <typename Job>
+__device__ inline void gk_store(const Job& a, int e, int row, int col, float v) {
   float* C = (float*)a.C;
   if (a.C1 && col >= a.nsplit) {
     C = (float*)a.C1;
@@ -885,8 +886,52 @@ __device__ inline void gk_store(const GemmArgs& a, int e, int row, int col, floa
   C[a.ctrans ? (long)col * a.ldc + row : (long)row * a.ldc + col] = v;
 }
 
+struct GkJobs {
+  GemmArgs job[kGkMaxJobs];
+};
+// The fields of one K-grouped job that its units read, picked out of a GkJobs with constant indices:
+// indexing the kernel-argument array with a run-time job number would copy it to the stack.
+struct GkJob {
+  const void* A;
+  const void* B;
+  void* C;
+  void* C1;
+  float* gkpart;
+  const int* arow;
+  long lda, ldb, ldc, cstride;
+  int M, N, nsplit, ctrans, arow_div;
+  float scale;
+};
+__device__ inline GkJob gk_job(const GkJobs& J, int j) {
+  GkJob o;
+  switch (j) {
+#define MOE_GK_PICK(i)                                                                              \
+  case i: {                                                                                         \
+    const GemmArgs& a = J.job[i];                                                                   \
+    o = GkJob{a.A, a.B, a.C, a.C1, a.gkpart, a.arow, a.lda, a.ldb, a.ldc, a.cstride, a.M, a.N,    \
+              a.nsplit, a.ctrans, a.arow_div, a.scale};                                             \
+    break;                                                                                          \
+  }
+    MOE_GK_PICK(0) MOE_GK_PICK(1) MOE_GK_PICK(2) MOE_GK_PICK(3)
+    MOE_GK_PICK(4) MOE_GK_PICK(5) MOE_GK_PICK(6) default: MOE_GK_PICK(7)
+#undef MOE_GK_PICK
+  }
+  return o;
+}
+static_assert(kGkMaxJobs == 8, "gk_job picks one of eight jobs");
+// Several K-grouped problems over the same row grouping in one launch: each chunk (or group) of the
+// grouping has tiles_pre[njobs] work units, job j's output tiles being [tiles_pre[j], tiles_pre[j + 1]).
+struct GkLaunch {
+  GkJobs jobs;
+  int tiles_pre[kGkMaxJobs + 1];
+  int tiles_all;  // tiles_pre[njobs]
+  int njobs;
+};
+static_assert(sizeof(GkLaunch) + 2 * sizeof(void*) <= 4096, "kernel arguments within 4 KB");
+
 // K-grouped MFMA GEMM: C_e = scale * L[rows_e]^T . R[rows_e]; both operands stored with the output
-// axis contiguous, so both fragments come from transposing LDS reads.
+// axis contiguous, so both fragments come from transposing LDS reads. One launch runs every job of a
+// GkLaunch (all of them share the row grouping), so that the short reductions fill the chip together.
 // Without a.gkpart, one workgroup per output tile reduces all rows of its group. With it, work
 // units are (chunk of kGkChunk, or kGkChunkSmall, group rows, output tile), listed by the chunk table (toffc: chunk
 // prefix sums per group, tmapc: chunk -> group; an empty group has one empty chunk). A group of
@@ -894,7 +939,7 @@ __device__ inline void gk_store(const GemmArgs& a, int e, int row, int col, floa
 // gk_reduce adds up in chunk order after the launch.
 template <int WM, int WN, int TM, int TN>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
-void gk_mfma(GemmArgs a, const int* toffc, const int* tmapc) {
+void gk_mfma(const GkLaunch L, const int* toffc, const int* tmapc) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32, NT = WM * WN * 64;
   // both operands have the output axis contiguous: unpadded rows of BM (BN) elements, 16-byte chunks
   // XOR-swizzled by row (swz_kx) so that the transposing fragment reads are free of bank conflicts
@@ -906,18 +951,25 @@ void gk_mfma(GemmArgs a, const int* toffc, const int* tmapc) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
-  if (blockIdx.y) {  // the second problem of a batched launch
-    a.A = a.bA;
-    a.B = a.bB;
-    a.C = a.bC;
-    a.gkpart = a.bgkpart;
-  }
-  const int tilesM = (a.M + BM - 1) / BM, tilesN = (a.N + BN - 1) / BN;
-  const int units = a.gkpart ? toffc[a.G] : a.G;
-  const int T = xcd_unit(units * tilesM * tilesN);
+  // unit order: chunk (or group) outermost, then job, then output tile, so that each XCD takes a
+  // contiguous range of groups with all of their jobs and reuses their rows in its L2
+  const int units = L.jobs.job[0].gkpart ? toffc[L.jobs.job[0].G] : L.jobs.job[0].G;
+  const int T = xcd_unit(units * L.tiles_all);
   if (T < 0) return;
-  const int u0 = T / (tilesM * tilesN);  // group (whole-group mode) or chunk
-  const int rem = T - u0 * tilesM * tilesN;
+  const int u0 = T / L.tiles_all;  // group (whole-group mode) or chunk
+  int rem = T - u0 * L.tiles_all;
+  int j = 0, jbase = 0;
+#pragma unroll
+  for (int i = 1; i < kGkMaxJobs; i++) {  // (constant indices: see gk_job)
+    if (i < L.njobs && rem >= L.tiles_pre[i]) {
+      j = i;
+      jbase = L.tiles_pre[i];
+    }
+  }
+  rem -= jbase;
+  const GkJob a = gk_job(L.jobs, j);
+  const GemmArgs& g0 = L.jobs.job[0];  // the grouping, shared by every job
+  const int tilesM = (a.M + BM - 1) / BM;
   const int nt = rem / tilesM, mt = rem - nt * tilesM;
   int e, kb, ke, nch = 1;
   int c0 = 0;
@@ -925,13 +977,13 @@ void gk_mfma(GemmArgs a, const int* toffc, const int* tmapc) {
     e = tmapc[u0];
     c0 = toffc[e];
     nch = toffc[e + 1] - c0;
-    const int chunk = a.gkchunk == kGkChunkSmall ? kGkChunkSmall : kGkChunk;
-    kb = a.goff[e] + (u0 - c0) * chunk;
-    ke = min(kb + chunk, a.goff[e + 1]);
+    const int chunk = g0.gkchunk == kGkChunkSmall ? kGkChunkSmall : kGkChunk;
+    kb = g0.goff[e] + (u0 - c0) * chunk;
+    ke = min(kb + chunk, g0.goff[e + 1]);
   } else {
     e = u0;
-    kb = a.goff[e];
-    ke = a.goff[e + 1];
+    kb = g0.goff[e];
+    ke = g0.goff[e + 1];
   }
 
   int acol[A_PT], bcol[B_PT];
@@ -1056,17 +1108,15 @@ void gk_mfma(GemmArgs a, const int* toffc, const int* tmapc) {
 // Completion of chunked K-grouped launches: block (x, j) walks the groups of job j and, for each
 // group of several chunks, strides over its output with the gridDim.x blocks of the job (groups of
 // one chunk are already stored).
-struct GkJobs {
-  GemmArgs job[kGkMaxJobs];
-};
 __global__ __launch_bounds__(256) void gk_reduce(GkJobs jobs, const int* toffc) {
   __shared__ int off[kGkMaxGroups + 1];
-  const GemmArgs& a = jobs.job[blockIdx.y];
-  if (toffc[a.G] == a.G) return;  // every group has one chunk (none has fewer): nothing to add up
-  for (int e = threadIdx.x; e <= a.G; e += 256) off[e] = toffc[e];
+  const GkJob a = gk_job(jobs, blockIdx.y);
+  const GemmArgs& g0 = jobs.job[0];  // the grouping, shared by every job
+  if (toffc[g0.G] == g0.G) return;  // every group has one chunk (none has fewer): nothing to add up
+  for (int e = threadIdx.x; e <= g0.G; e += 256) off[e] = toffc[e];
   __syncthreads();
   const long MN = (long)a.M * a.N;
-  for (int e = 0; e < a.G; e++) {
+  for (int e = 0; e < g0.G; e++) {
     const int c0 = off[e], nch = off[e + 1] - c0;
     if (nch <= 1) continue;
     for (long idx = (long)blockIdx.x * 256 + threadIdx.x; idx < MN; idx += (long)gridDim.x * 256) {
@@ -1365,37 +1415,61 @@ hipError_t gemm_gm_launch(const GemmArgs& a, int b_layout, int epi, int out_f32,
   }
 }
 
-hipError_t gemm_gk_launch(const GemmArgs& a, int dtype, int reference, int rows_bound,
+hipError_t gemm_gk_launch(const GemmArgs* jobs, int njobs, int dtype, int reference, int rows_bound,
                           hipStream_t stream) {
-  if (a.G <= 0 || a.M <= 0 || a.N <= 0) return hipSuccess;
-  if (a.nbatch > 2 || (a.nbatch == 2 && (!a.bA || !a.bB || !a.bC || (a.gkpart && !a.bgkpart))))
-    return hipErrorInvalidValue;
-  const unsigned nb = a.nbatch == 2 ? 2 : 1;
+  if (njobs <= 0) return hipSuccess;
+  if (njobs > kGkMaxJobs) return hipErrorInvalidValue;
+  const GemmArgs& a0 = jobs[0];
+  for (int i = 0; i < njobs; i++) {
+    const GemmArgs& a = jobs[i];
+    if (a.nbatch > 1 || a.G != a0.G || a.goff != a0.goff || (a.gkpart != nullptr) != (a0.gkpart != nullptr) ||
+        a.gkchunk != a0.gkchunk || a.toff_all != a0.toff_all || a.tmap_all != a0.tmap_all)
+      return hipErrorInvalidValue;
+  }
+  if (a0.G <= 0) return hipSuccess;
   if (dtype == 0 || reference) {
-    dim3 grid((a.N + 63) / 64, a.M, a.G * nb);
-    if (dtype == 0) hipLaunchKernelGGL(gk_simt<float>, grid, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL(gk_simt<bf16_t>, grid, dim3(64), 0, stream, a);
-    return hipGetLastError();
+    for (int i = 0; i < njobs; i++) {
+      const GemmArgs& a = jobs[i];
+      if (a.M <= 0 || a.N <= 0) continue;
+      dim3 grid((a.N + 63) / 64, a.M, a.G);
+      if (dtype == 0) hipLaunchKernelGGL(gk_simt<float>, grid, dim3(64), 0, stream, a);
+      else hipLaunchKernelGGL(gk_simt<bf16_t>, grid, dim3(64), 0, stream, a);
+      const hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
   }
   // output rows = the wide dimension (m or n), output columns = the LoRA rank side
   constexpr int WM = 4, WN = 1, TM = 1, TN = 1;
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
-  const long tiles = (long)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  GkLaunch L;
+  L.njobs = njobs;
+  L.tiles_pre[0] = 0;
+  for (int i = 0; i < kGkMaxJobs; i++) {
+    L.jobs.job[i] = jobs[i < njobs ? i : 0];
+    const GemmArgs& a = jobs[i < njobs ? i : 0];
+    const int tiles = (a.M > 0 && a.N > 0) ? ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) : 0;
+    L.tiles_pre[i + 1] = L.tiles_pre[i] + (i < njobs ? tiles : 0);
+  }
   const int* toffc = nullptr;
   const int* tmapc = nullptr;
-  long units = (long)a.G * tiles;
-  if (a.gkpart) {
-    if (!a.toff_all || !a.tmap_all || rows_bound < 0) return hipErrorInvalidValue;
-    if (a.gkchunk != 0 && a.gkchunk != kGkChunk && a.gkchunk != kGkChunkSmall) return hipErrorInvalidValue;
-    const int tab = gk_chunk_table(a.gkchunk);
-    toffc = a.toff_all + tab * (a.G + 1);
-    tmapc = a.tmap_all + tile_map_offset(tab, rows_bound, a.G);
-    units = tile_map_capacity(tab, rows_bound, a.G) * tiles;
+  long cap = a0.G;  // units: groups, or (with partials) at most this many chunks
+  if (a0.gkpart) {
+    if (!a0.toff_all || !a0.tmap_all || rows_bound < 0) return hipErrorInvalidValue;
+    if (a0.gkchunk != 0 && a0.gkchunk != kGkChunk && a0.gkchunk != kGkChunkSmall) return hipErrorInvalidValue;
+    const int tab = gk_chunk_table(a0.gkchunk);
+    toffc = a0.toff_all + tab * (a0.G + 1);
+    tmapc = a0.tmap_all + tile_map_offset(tab, rows_bound, a0.G);
+    cap = tile_map_capacity(tab, rows_bound, a0.G);
+  } else {
+    for (int i = 0; i < njobs; i++)
+      if (jobs[i].gkpart) return hipErrorInvalidValue;
   }
-  const long blocks = (units + 7) / 8 * 8;
+  L.tiles_all = L.tiles_pre[njobs];
+  const long blocks = (cap * L.tiles_all + 7) / 8 * 8;
   if (blocks > 0)
-    hipLaunchKernelGGL((gk_mfma<WM, WN, TM, TN>), dim3((unsigned)blocks, nb), dim3(WM * WN * 64), 0,
-                       stream, a, toffc, tmapc);
+    hipLaunchKernelGGL((gk_mfma<WM, WN, TM, TN>), dim3((unsigned)blocks), dim3(WM * WN * 64), 0, stream, L,
+                       toffc, tmapc);
   return hipGetLastError();
 }
 
