@@ -30,24 +30,73 @@ def log(msg):
 
 
 def stage_work(stage, cfg, cnt, b):
-    """Algorithmic FLOPs and unique HBM bytes of one launch of a GEMM stage."""
-    P, m, n, r = cfg.s * cfg.k, cfg.m, cfg.n, cfg.r
-    used = int((cnt > 0).sum())   # experts whose weights are read
+    """Algorithmic FLOPs and unique HBM bytes of one step's worth of a stage (a launch, or the few
+    small launches a stage groups). Bytes count each tensor the stage must read or write once: the
+    activations (gathered rows count their source matrix once), the weights of the experts that
+    received pairs, and the stage's outputs; recomputation, padding rows and re-reads do not count."""
+    s, P, m, n, r, E, k = cfg.s, cfg.s * cfg.k, cfg.m, cfg.n, cfg.r, cfg.E, cfg.k
+    u = int((cnt > 0).sum())   # experts whose weights are read
+    nb = (s + 255) // 256
     if stage == "fwd_gate_up":
         fl = 2 * P * m * 2 * n + 2 * P * r * 2 * n
-        by = (P * m + used * m * 2 * n + P * 2 * r + 2 * used * r * n + P * 2 * n + P * n) * b
+        by = (s * m + u * m * 2 * n + P * 2 * r + 2 * u * r * n + P * 2 * n + P * n) * b
     elif stage == "fwd_down":
         fl = 2 * P * n * m + 2 * P * r * m
-        by = (P * n + used * n * m + P * r + used * r * m + P * m) * b
+        by = (P * n + u * n * m + P * r + u * r * m + P * m) * b
     elif stage == "bwd_down":
         fl = 2 * P * m * n + 2 * P * r * n
-        by = (P * m + used * n * m + P * r + used * n * r + P * 2 * n + P * 2 * n) * b
+        by = (s * m + u * n * m + P * r + u * n * r + P * 2 * n + P * 2 * n) * b
     elif stage == "bwd_gate_up":
         fl = 2 * P * 2 * n * m + 2 * P * 2 * r * m
-        by = (P * 2 * n + used * m * 2 * n + P * 2 * r + 2 * used * m * r + P * m) * b
+        by = (P * 2 * n + u * m * 2 * n + P * 2 * r + 2 * u * m * r + P * m) * b
+    elif stage == "route_logits":
+        fl = 2 * s * m * E
+        by = (s * m + m * E) * b + s * E * 4
+    elif stage == "route_topk":
+        fl, by = 0, s * E * 4 + P * 12
+    elif stage == "route_hist_rank":
+        fl, by = 0, P * 8 + nb * E * 4
+    elif stage == "route_scan":
+        fl, by = 0, nb * E * 8 + (E + 1) * 4
+    elif stage == "route_scatter":
+        fl, by = 0, P * 8 + nb * E * 4 + P * 12
+    elif stage == "fwd_lora_t_gate_up":
+        fl = 2 * P * m * 2 * r
+        by = (s * m + u * m * 2 * r + P * 2 * r) * b
+    elif stage == "fwd_lora_t_down":
+        fl = 2 * P * n * r
+        by = (P * n + u * n * r + P * r) * b
+    elif stage == "fwd_combine":
+        fl, by = 2 * P * m, P * m * b + s * m * b + 8 * P
+    elif stage == "bwd_router":   # row-weighted T_d rows, W_r^T, ds partials -> dz
+        fl = 0
+        by = 2 * P * r * b + 2 * m * E * b + (n // 64) * P * 4 + 12 * P
+    elif stage == "bwd_lora_u_down":
+        fl = 2 * P * m * r
+        by = (s * m + u * r * m + 2 * P * r) * b
+    elif stage == "bwd_lora_u_gate_up":
+        fl = 2 * P * 2 * n * r
+        by = (P * 2 * n + 2 * u * r * n + P * 2 * r) * b
+    elif stage == "bwd_unpermute":
+        fl, by = P * m * 3, P * m * b + s * m * b + 8 * P + u * m * b
+    elif stage == "bwd_lora_grads":
+        fl = 2 * P * (m * 2 * r + 2 * n * r + n * r + m * r)
+        by = (2 * s * m + P * n + P * 2 * n + P * 6 * r) * b + E * (3 * m * r + 3 * r * n) * 4
     else:
         raise KeyError(stage)
     return fl, by
+
+
+def roofline(fl, by, t_s):
+    """The binding roof of algorithmic work fl (FLOP) and by (bytes) at the MI355X peaks, and the
+    fraction of it that a measured time t_s reaches."""
+    t_mfma = fl / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = by / (PEAK_HBM_GBS * 1e9)
+    if t_hbm >= t_mfma:
+        return {"bound": "hbm", "achieved": round(by / t_s / 1e9, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(by / t_s / 1e9 / PEAK_HBM_GBS, 4)}
+    return {"bound": "mfma", "achieved": round(fl / t_s / 1e12, 1), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(fl / t_s / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
 def traffic_for(stage, workload):
@@ -67,17 +116,33 @@ def traffic_for(stage, workload):
     return None
 
 
-def cpu_baseline(cfg, inp, tokens, min_seconds=10.0, max_passes=8):
-    """The oracle, untuned, on the first `tokens` tokens of the same layer (route + fwd + bwd)."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(cfg, inp, tokens, runs=3):
+    """The oracle, untuned, on the first `tokens` tokens of the same layer (route, forward and
+    backward timed separately), median of `runs` runs. Its matrix products run on the BLAS thread
+    pool; the rest is single-threaded numpy."""
+    import statistics
+
     import numpy as np
     import torch
 
     import oracle
+    threads = None
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+        pass
+    nproc = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     S = min(tokens, cfg.s)
     f64 = lambda t: t.detach().to("cpu", torch.float32).numpy().astype(np.float64)
     X = f64(inp["X"][:S])
@@ -86,20 +151,26 @@ def cpu_baseline(cfg, inp, tokens, min_seconds=10.0, max_passes=8):
     bias = f64(inp["router_bias"]) if inp["router_bias"] is not None else None
     W = {k: inp[k].detach().to("cpu", torch.float32).numpy() for k in
          ("W_gu", "W_d", "A_g", "B_g", "A_u", "B_u", "A_d", "B_d")}
-    passes, t0 = 0, time.perf_counter()
-    while True:   # whole passes until at least min_seconds of CPU work
+    phases = {"route": [], "forward": [], "backward": []}
+    for _ in range(runs):
+        t0 = time.perf_counter()
         z = oracle.router_logits(X, Wr, bias)
         rt = oracle.route(z, cfg.k, cfg.E, cfg.score, cfg.renormalize)
+        t1 = time.perf_counter()
         _, saved = oracle.forward(X, W, rt, cfg.alpha, cfg.r)
+        t2 = time.perf_counter()
         oracle.backward(dY, X, Wr, W, rt, cfg.alpha, cfg.r, cfg.score, cfg.renormalize, True, saved)
-        passes += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds or passes >= max_passes:
-            break
-    return {"value": round(passes * S / dt, 3), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+        t3 = time.perf_counter()
+        phases["route"].append(t1 - t0)
+        phases["forward"].append(t2 - t1)
+        phases["backward"].append(t3 - t2)
+    med = {k: statistics.median(v) for k, v in phases.items()}
+    total = sum(med.values())
+    return {"value": round(S / total, 3), "unit": "tokens/s", "cores": int(threads or nproc),
+            "kind": "oracle", "nproc": nproc, "cpu_model": _cpu_model(),
+            "phase_seconds": {k: round(v, 3) for k, v in med.items()},
             "sample": f"first {S} of {cfg.s} tokens of the same layer, route + forward + backward "
-                      f"(fp64 numpy), {passes} pass(es) in {dt:.1f} s"}
+                      f"(fp64 numpy), median of {runs} runs ({total:.1f} s each)"}
 
 
 def crossover(args, g, layer, config, make_inputs, torch, dev):
@@ -303,27 +374,39 @@ def main():
     tflops = total_flops / (ms * 1e-3) / 1e12
     cnt = np.diff(rt["expert_off"].cpu().numpy())
     b = 2 if cfg.dtype == "bf16" else 4
+    # per-stage roofline: algorithmic work of one step's worth of the stage against its measured
+    # time per step; the layer against the sum of the stage roofs
+    stages_roof = {}
+    t_roof_sum = 0.0
+    for st, t_us in per_step.items():
+        try:
+            fl, by = stage_work(st, cfg, cnt, b)
+        except KeyError:
+            continue
+        t_s = t_us * 1e-3
+        rf = roofline(fl, by, t_s)
+        t_roof = max(fl / (PEAK_BF16_TFLOPS * 1e12), by / (PEAK_HBM_GBS * 1e9))
+        t_roof_sum += t_roof
+        stages_roof[st] = {"us": round(t_us * 1e3, 1), "gflop": round(fl / 1e9, 2), "mb": round(by / 1e6, 1),
+                           "bound": rf["bound"], "frac": rf["frac"],
+                           "mfma_frac": round(fl / t_s / 1e12 / PEAK_BF16_TFLOPS, 4) if fl else 0.0}
     dom = max(GEMM_STAGES, key=lambda st: per_step.get(st, 0.0))
     fl, by = stage_work(dom, cfg, cnt, b)
     t_s = avg[dom] * 1e-3
-    t_mfma = fl / (PEAK_BF16_TFLOPS * 1e12)
-    t_hbm = by / (PEAK_HBM_GBS * 1e9)
-    if t_hbm > t_mfma:
-        roof = {"bound": "hbm", "achieved": round(by / t_s / 1e9, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(by / t_s / 1e9 / PEAK_HBM_GBS, 4)}
-    else:
-        roof = {"bound": "mfma", "achieved": round(fl / t_s / 1e12, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(fl / t_s / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    roof = roofline(fl, by, t_s)
     roof["traffic"] = traffic_for(dom, cfg.name)
     roof["kernel"] = dom
     roof["avg_launch_ms"] = round(avg[dom], 4)
     roof["mfma_frac"] = round(fl / t_s / 1e12 / PEAK_BF16_TFLOPS, 4)
+    layer_roof = {"ms": round(ms, 4), "roof_ms": round(t_roof_sum * 1e3, 4),
+                  "frac": round(t_roof_sum * 1e3 / ms, 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle on {args.cpu_tokens} tokens ...")
         cpu = cpu_baseline(cfg, inp, args.cpu_tokens)
-        log(f"[bench] CPU oracle: {cpu['value']} tokens/s on {cpu['cores']} threads")
+        log(f"[bench] CPU oracle: {cpu['value']} tokens/s on {cpu['cores']} threads "
+            f"({cpu['nproc']} host cores, {cpu['cpu_model']}); phases {cpu['phase_seconds']}")
 
     out = {
         "metric": METRIC,
@@ -348,6 +431,8 @@ def main():
         "tflops": round(tflops, 2),
         "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": roof,
+        "stage_roofline": stages_roof,
+        "layer_roofline": layer_roof,
         "cpu_baseline": cpu,
         "stage_us_per_step": {k: round(v * 1e3, 1) for k, v in per_step.items()},
     }
