@@ -180,8 +180,8 @@ moe_status check_shape(const moe_shape* sp) {
   if (s.m % 64 || s.n % 64) return MOE_ERR_UNSUPPORTED;
   if (s.E > 1024 || s.r > 64) return MOE_ERR_UNSUPPORTED;
   if (s.dtype == MOE_DTYPE_BF16 && (s.r % 8 || s.E % 8)) return MOE_ERR_UNSUPPORTED;
-  const long wide = s.m > 2L * s.n ? s.m : 2L * s.n;
-  if ((long)s.s * s.k * wide >= (1L << 31)) return MOE_ERR_UNSUPPORTED;
+  // pair and row indices are 32-bit (element offsets are 64-bit everywhere)
+  if ((long)s.s * s.k >= (1L << 31)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

@@ -160,18 +160,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gm_mfma(GemmArgs a, int tidx, co
   // ---- per-lane source offsets of the chunks this lane moves (32-bit; the shape limits keep them
   //      below 2^31)
   const bf16_t* Ab = (const bf16_t*)a.A;
-  int aoff[A_IPW];
+  long aoff[A_IPW];  // element offsets: an activation matrix may hold more than 2^31 elements
 #pragma unroll
   for (int i = 0; i < A_IPW; i++) {
     const int P = (wave * A_IPW + i) * 64 + lane;
     const int x = P / CPR_A, q = (P % CPR_A) ^ swz_xk<CPR_A>(x);
     const int row = min(row0 + x, row_end - 1);
     const int src = a.arow ? a.arow[row] / a.arow_div : row;
-    aoff[i] = src * (int)a.lda + q * 8;
+    aoff[i] = (long)src * a.lda + q * 8;
   }
   const bf16_t* Bg = (const bf16_t*)a.B + (long)e * a.bstride;
   const bf16_t* Bug = DUAL ? (const bf16_t*)a.Bu + (long)e * a.bstride : nullptr;
-  int boff[B_IPW];
+  long boff[B_IPW];
   bool bup[B_IPW];
 #pragma unroll
   for (int i = 0; i < B_IPW; i++) {
@@ -181,13 +181,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gm_mfma(GemmArgs a, int tidx, co
       const int half = DUAL ? (x >= BNH) : 0;
       const int jj = min(j0 + x - half * BNH, a.N - 8);
       bup[i] = half;
-      boff[i] = k * (int)a.ldb + jj;
+      boff[i] = (long)k * a.ldb + jj;
     } else {
       const int x = P / CPR_A, q = (P % CPR_A) ^ swz_xk<CPR_A>(x);
       const int half = DUAL ? (x >= BNH) : 0;
       const int jj = min(j0 + x - half * BNH, a.N - 1);
       bup[i] = half;
-      boff[i] = jj * (int)a.ldb + q * 8;
+      boff[i] = (long)jj * a.ldb + q * 8;
     }
   }
 
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gm_mfma(GemmArgs a, int tidx, co
     k0 += kbase;
 #pragma unroll
     for (int i = 0; i < A_IPW; i++) ra[i] = ld16(Ab + aoff[i] + k0);
-    const int kb = (BL == LAYOUT_KX) ? k0 * (int)a.ldb : k0;
+    const long kb = (BL == LAYOUT_KX) ? (long)k0 * a.ldb : (long)k0;
 #pragma unroll
     for (int i = 0; i < B_IPW; i++) rb[i] = ld16((bup[i] ? Bug : Bg) + boff[i] + kb);
   };

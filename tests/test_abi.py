@@ -70,7 +70,9 @@ def shape(**kw):
     (dict(r=12), g.MOE_ERR_UNSUPPORTED),
     (dict(r=128), g.MOE_ERR_UNSUPPORTED),
     (dict(E=12), g.MOE_ERR_UNSUPPORTED),
-    (dict(s=1 << 20, m=4096), g.MOE_ERR_UNSUPPORTED),
+    (dict(s=1 << 29, k=4), g.MOE_ERR_UNSUPPORTED),   # 2^31 pairs: pair ids are int32
+    (dict(s=1 << 20, m=4096), g.MOE_OK),             # 2^32 activation elements: 64-bit offsets
+    (dict(s=65536, m=7168, n=2048, E=256, k=8), g.MOE_OK),  # the DeepSeek-V3 layer at 64K tokens
     (dict(), g.MOE_OK),
     (dict(dtype="f32", r=4, E=12), g.MOE_OK),
     (dict(s=0), g.MOE_OK),

@@ -174,3 +174,53 @@ def test_fullsize_parity(name, ntok, nexp, cuda):
         ge = oracle.backward_expert(e, dYr, Xr, W, ort, cfg.alpha, cfg.r)
         errs = _check_expert_grads(e, cnt, grads, ge, tol)
         _say(f"  expert {e} ({cnt[e]} rows): " + ", ".join(f"{k}={v:.1e}" for k, v in errs.items()))
+
+
+@pytest.mark.timeout(900)
+def test_long_context_deepseek_layer(cuda):
+    """The DeepSeek-V3 layer at 65 536 tokens (8x the benchmark's batch): 524 288 routed pairs, so the
+    grouped activations o, dXp and gu hold up to 3.8e9 elements and their row offsets pass 2^31.
+    Routing is checked in full; Y and dX on tokens whose pairs sit in the highest grouped rows (the
+    last experts), and the gradients of the last expert and one more, against the oracle in fp64."""
+    from grouped_gemm_top_amd import layer
+    cfg = config("deepseek_v3", s=65536)
+    _say(f"[long context] deepseek_v3 s={cfg.s}: P={cfg.s * cfg.k}")
+    inp = make_inputs(cfg, seed=0, device=cuda, with_grad_output=True)
+    shape = layer.shape_of(cfg)
+    rt = layer.route(shape, inp["X"], inp["W_r"], inp["router_bias"])
+    Y, saved = layer.forward(shape, inp["X"], rt, inp, training=True)
+    dX, grads = layer.backward(shape, inp["dY"], inp["X"], inp["W_r"], rt, inp, saved)
+    torch.cuda.synchronize()
+    _say("  GPU pass done")
+    del saved
+    z_gpu = rt["logits"].cpu().numpy().astype(np.float64)
+    ort = oracle.route(z_gpu, cfg.k, cfg.E, cfg.score, cfg.renormalize)
+    assert np.array_equal(rt["topk_idx"].cpu().numpy(), ort["idx"])
+    assert np.array_equal(rt["expert_off"].cpu().numpy(), ort["off"])
+    assert np.array_equal(rt["perm"].cpu().numpy(), ort["perm"])
+    assert np.array_equal(rt["inv_perm"].cpu().numpy(), ort["inv"])
+    assert rel_err(rt["topk_w"].cpu().numpy(), ort["w"]) <= WEIGHT_TOL
+    P = cfg.s * cfg.k
+    assert (P - 1) * cfg.m >= 1 << 31
+    # tokens holding the last grouped rows (each row's offset in o and dXp is row * m elements)
+    top_rows = np.arange(P - 1, P - 6000, -1)
+    tok = np.unique(ort["perm"][top_rows] // cfg.k)[-6:]
+    tok = np.concatenate([tok, [cfg.s - 1, 0]])
+    hi = max(int(ort["inv"][t * cfg.k + j]) for t in tok for j in range(cfg.k))
+    _say(f"  tokens {tok.tolist()}, highest grouped row {hi} (offset {hi * cfg.m:.3e} elements)")
+    assert hi * cfg.m >= 1 << 31
+    W = {key: NoCache(inp[key]) for key in ("W_gu", "W_d", "A_g", "B_g", "A_u", "B_u", "A_d", "B_d")}
+    Xr, dYr = Rows(inp["X"]), Rows(inp["dY"])
+    Wr = f64(inp["W_r"])
+    y_ref, dx_ref = oracle.token_outputs(tok, Xr, W, ort, cfg.alpha, cfg.r, dYr, Wr, cfg.score,
+                                         cfg.renormalize, True)
+    tt = torch.as_tensor(tok, device=cuda)
+    e_y, e_dx = rel_err(f64(Y[tt]), y_ref), rel_err(f64(dX[tt]), dx_ref)
+    _say(f"  tokens: Y {e_y:.2e}, dX {e_dx:.2e}")
+    tol = TOL[cfg.dtype]
+    assert e_y <= tol and e_dx <= tol
+    cnt = ort["cnt"]
+    for e in (cfg.E - 1, int(np.argmax(cnt))):
+        ge = oracle.backward_expert(e, dYr, Xr, W, ort, cfg.alpha, cfg.r)
+        errs = _check_expert_grads(e, cnt, grads, ge, tol)
+        _say(f"  expert {e} ({cnt[e]} rows): " + ", ".join(f"{k}={v:.1e}" for k, v in errs.items()))
