@@ -38,11 +38,16 @@ struct RouteState {
   int* tiles;
   int* tmaps;
   float* zpart;  // K-split partial router logits
+  void* wr_pad;  // bf16 with E % 8 != 0: W_r with rows padded to E8 columns (zeros past E)
 };
 
 // K splits of the router-logit GEMM: enough workgroups to fill the chip, chunks of >= 256.
 // K splits of the router-logit GEMM (64 x 128 tiles): enough workgroups for the chip (about 256), each
 // split at least 256 long; every split adds s x E fp32 partials that top-k reads back.
+// W_r's rows padded to a multiple of 8 columns (16 bytes of bf16) for the router GEMM's chunk loads
+inline int router_cols(const moe_shape& s) { return (s.E + 7) & ~7; }
+inline bool router_padded(const moe_shape& s) { return s.dtype == MOE_DTYPE_BF16 && s.E % 8 != 0; }
+
 inline int route_ksplit(const moe_shape& s) {
   const long tiles = ((long)s.s + 63) / 64 * (((long)s.E + 127) / 128);
   int n = 1;
@@ -97,6 +102,7 @@ size_t route_layout(const moe_shape& s, void* base, RouteState* rs) {
   r.tiles = c.take<int>((size_t)kNumTileSizes * (s.E + 1));
   r.tmaps = c.take<int>((size_t)tile_map_offset(kNumTileSizes, P, s.E));
   r.zpart = c.take<float>((size_t)route_ksplit(s) * s.s * s.E);
+  r.wr_pad = c.bytes(router_padded(s) ? (size_t)s.m * router_cols(s) * 2 : 0);
   if (rs) *rs = r;
   return align_up(c.off, 256);
 }
@@ -179,7 +185,7 @@ moe_status check_shape(const moe_shape* sp) {
   if (!std::isfinite(s.alpha)) return MOE_ERR_INVALID_ARG;
   if (s.m % 64 || s.n % 64) return MOE_ERR_UNSUPPORTED;
   if (s.E > 1024 || s.r > 64) return MOE_ERR_UNSUPPORTED;
-  if (s.dtype == MOE_DTYPE_BF16 && (s.r % 8 || s.E % 8)) return MOE_ERR_UNSUPPORTED;
+  if (s.dtype == MOE_DTYPE_BF16 && s.r % 8) return MOE_ERR_UNSUPPORTED;
   // pair and row indices are 32-bit (element offsets are 64-bit everywhere)
   if ((long)s.s * s.k >= (1L << 31)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
@@ -396,6 +402,11 @@ moe_status moe_route(const moe_shape* shape, const void* X, const void* W_r,
   a.lda = s.m;
   a.B = W_r;
   a.ldb = s.E;
+  if (router_padded(s)) {  // bf16 rows of E columns are not 16-byte aligned: a padded copy
+    STAGE(ST_ROUTE_LOGITS, launch_pad_cols(W_r, rs.wr_pad, s.m, s.E, router_cols(s), hs));
+    a.B = rs.wr_pad;
+    a.ldb = router_cols(s);
+  }
   a.C = nsplit > 1 ? rs.zpart : z;
   a.ldc = s.E;
   a.bias = router_bias;

@@ -179,7 +179,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gm_mfma(GemmArgs a, int tidx, co
     if (BL == LAYOUT_KX) {
       const int k = P / CPR_B, x = ((P % CPR_B) ^ swz_kx<CPR_B>(k)) * 8;
       const int half = DUAL ? (x >= BNH) : 0;
-      const int jj = min(j0 + x - half * BNH, a.N - 8);
+      // (a chunk past the last column re-reads the last whole chunk of the row: the operand rows
+      // are padded to a multiple of 8 columns, so that chunk stays aligned)
+      const int jj = min(j0 + x - half * BNH, ((a.N + 7) & ~7) - 8);
       bup[i] = half;
       boff[i] = (long)k * a.ldb + jj;
     } else {

@@ -39,6 +39,8 @@ hipError_t launch_transpose(int dtype, const void* W, void* WT, int rows, int co
 hipError_t launch_unpermute(int dtype, const void* dXp, const int* inv, const float* dz,
                             const int* idx, const void* WrT, void* dX, int s, int k, int m,
                             hipStream_t st);
+// bf16 [rows, cols] -> [rows, ld] (ld >= cols), zeros in columns [cols, ld)
+hipError_t launch_pad_cols(const void* W, void* Wp, int rows, int cols, int ld, hipStream_t st);
 // zero-fill n 32-bit words
 hipError_t launch_zero(void* p, size_t words, hipStream_t st);
 // The row-weighted rows out[i, :] = w[pair[i]] * in[i, :] (rows x cols, rounded to dtype) and, when W is

@@ -607,6 +607,16 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ in,
   }
 }
 
+__global__ void pad_cols_kernel(const bf16_t* __restrict__ W, bf16_t* __restrict__ Wp, int rows, int cols,
+                                int ld) {
+  const long n = (long)rows * ld;
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
+    const long r = i / ld;
+    const int c = (int)(i - r * ld);
+    Wp[i] = c < cols ? W[r * cols + c] : (bf16_t)0;
+  }
+}
+
 __global__ void zero_kernel(int* p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
     p[i] = 0;
@@ -739,6 +749,15 @@ hipError_t launch_bwd_prep(int dtype, const void* in, const int* pair, const flo
     hipLaunchKernelGGL(bwd_prep_kernel<float>, dim3((unsigned)(rw_blocks + tr_blocks)), dim3(256), 0, st,
                        (const float*)in, pair, w, (float*)out, rows, cols, rw_blocks, (const float*)W,
                        (float*)WT, trows, tcols);
+  return hipGetLastError();
+}
+
+hipError_t launch_pad_cols(const void* W, void* Wp, int rows, int cols, int ld, hipStream_t st) {
+  const long n = (long)rows * ld;
+  if (n <= 0) return hipSuccess;
+  const long blocks = std::min<long>((n + 255) / 256, 2048);
+  hipLaunchKernelGGL(pad_cols_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (const bf16_t*)W, (bf16_t*)Wp, rows,
+                     cols, ld);
   return hipGetLastError();
 }
 

@@ -32,7 +32,7 @@
  *  - Pair id p = t*k + j (token t, slot j of its selection order); P = s*k pairs.
  *
  * Supported shapes: s >= 0; m and n multiples of 64; 1 <= k <= E <= 1024; 1 <= r <= 64, and for
- * bf16 r a multiple of 8 and E a multiple of 8; s*k < 2^31 (pair and row indices are int32; element
+ * bf16 r a multiple of 8; s*k < 2^31 (pair and row indices are int32; element
  * offsets are 64-bit, so activations and intermediates may exceed 2^31 elements). Anything else
  * returns MOE_ERR_UNSUPPORTED (there is no fallback path).
  */

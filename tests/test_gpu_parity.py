@@ -276,6 +276,10 @@ EDGE = {
     "experts_320": config("qwen3_30b_a3b", s=160, m=128, n=64, E=320, k=6),
     # more than 64 slots per token: a token's slots span two waves' worth of lanes
     "k_over_64": config("qwen3_30b_a3b", s=40, m=128, n=64, E=96, k=72),
+    # bf16 expert counts that are not a multiple of 8 (rows of W_r not 16-byte aligned): 60 experts
+    # as in Qwen1.5-MoE, and 12
+    "experts_60": config("qwen3_30b_a3b", s=300, m=192, n=128, E=60, k=4),
+    "experts_12": config("qwen3_30b_a3b", s=200, m=128, n=64, E=12, k=2),
 }
 
 
