@@ -425,10 +425,12 @@ __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_b
 template <int N_>
 using IC = std::integral_constant<int, N_>;
 
-template <int WM, int WN, int TM, int TN, int BL, int EPI>
-__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int WM, int WN, int TM, int TN, int BL, int EPI, int RS>
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(RS == 4 ? 2 : 3, RS == 4 ? 2 : 3)))
 void gm_ring(GemmArgs a, int tidx, const int* tmap) {
   constexpr int BKT = 64, NW = WM * WN, NT = NW * 64;
+  // RS register-ring slots: each tile is loaded RS - 1 tiles ahead of its copy into LDS
+  static_assert(RS == 2 || RS == 4, "ring of two or four slots");
   constexpr bool DUAL = (EPI == EPI_DUAL || EPI == EPI_SWIGLU);
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   constexpr int BNH = DUAL ? BN / 2 : BN;
@@ -506,7 +508,7 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
 #pragma unroll
       for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
 
-  i32x4_t ra[4][A_CPT], rb[4][B_CPT];  // register ring: slot = tile % 4
+  i32x4_t ra[RS][A_CPT], rb[RS][B_CPT];  // register ring: slot = tile % RS
   auto load = [&](i32x4_t(&da)[A_CPT], i32x4_t(&db)[B_CPT], int t) {
 #pragma unroll
     for (int u = 0; u < A_CPT; u++) da[u] = ld16(asrc[u] + t * BKT);
@@ -582,23 +584,23 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
   constexpr int CPT = A_CPT + B_CPT, NSIDE = BKT / 16, CPJ = (CPT + NSIDE - 1) / NSIDE;
 
   // ---- main loop. Step kt: (barrier) multiply tile kt from stage kt&1; spread over its MFMAs, copy
-  //      tile kt+1 from registers into LDS stage (kt+1)&1 and load tile kt+4 into the ring slot tile
+  //      tile kt+1 from registers into LDS stage (kt+1)&1 and load tile kt+RS into the ring slot tile
   //      kt left.
   const int nk = a.K / BKT;
   const int last = nk - 1;
   bf16_t* const s0 = smem;
   bf16_t* const s1 = smem + STAGE;
-  load(ra[0], rb[0], 0);
-  load(ra[1], rb[1], min(1, last));
-  load(ra[2], rb[2], min(2, last));
-  load(ra[3], rb[3], min(3, last));
+  static_for<RS>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    load(ra[i], rb[i], min(i, last));
+  });
   store(s0, ra[0], rb[0]);
   auto step = [&](auto slot_c, int kt) {
-    constexpr int sl = decltype(slot_c)::value;       // kt % 4
-    constexpr int nx = (sl + 1) & 3;                  // (kt + 1) % 4
+    constexpr int sl = decltype(slot_c)::value;       // kt % RS
+    constexpr int nx = (sl + 1) % RS;                 // (kt + 1) % RS
     lds_barrier();
     bf16_t* const st = (sl & 1) ? s0 : s1;
-    const int tl = min(kt + 4, last);
+    const int tl = min(kt + RS, last);
     compute((sl & 1) ? s1 : s0, [&](auto jc) {
       constexpr int j = decltype(jc)::value;
       static_for<CPJ>([&](auto qc) {
@@ -610,18 +612,15 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
       });
     });
   };
-  // whole groups of four steps run unguarded (the same loads in flight on every path into the loop
-  // head), the last nk % 4 steps after the loop
+  // whole groups of RS steps run unguarded (the same loads in flight on every path into the loop
+  // head), the last nk % RS steps after the loop
   int kt = 0;
-  for (; kt + 4 <= nk; kt += 4) {
-    step(IC<0>{}, kt);
-    step(IC<1>{}, kt + 1);
-    step(IC<2>{}, kt + 2);
-    step(IC<3>{}, kt + 3);
+  for (; kt + RS <= nk; kt += RS) {
+    static_for<RS>([&](auto ic) { step(ic, kt + decltype(ic)::value); });
   }
-  if (kt < nk) step(IC<0>{}, kt);
-  if (kt + 1 < nk) step(IC<1>{}, kt + 1);
-  if (kt + 2 < nk) step(IC<2>{}, kt + 2);
+  static_for<RS - 1>([&](auto ic) {
+    if (kt + decltype(ic)::value < nk) step(ic, kt + decltype(ic)::value);
+  });
 
   // ---- epilogue (after the tail): each wave stages its fp32 accumulators in its own LDS region, then writes whole
   //      16-byte row chunks (8 columns). Staged row r keeps its 4-float groups XOR-permuted by one
@@ -1285,7 +1284,7 @@ using CfgSkinnyDual = TileCfg<4, 1, 1, 2, 64, 2>;  // 128 x (32 + 32)
 using CfgMid = TileCfg<2, 2, 2, 2, 64, 2>;         // 128 x 128
 using CfgRouter = TileCfg<2, 2, 1, 2, 64, 2>;      // 64 x 128: the router logits (fp32 out, split over K)
 
-template <int WM, int WN, int TM, int TN, int BL, int EPI>
+template <int WM, int WN, int TM, int TN, int BL, int EPI, int RS = 4>
 hipError_t launch_gm_ring(const GemmArgs& a, int rows_bound, hipStream_t stream);
 
 template <int BL, int EPI, typename OutT>
@@ -1295,8 +1294,10 @@ hipError_t dispatch_gm_mfma(const GemmArgs& a, int rows_bound, hipStream_t strea
   // workgroups (the 128-row skinny tiles leave most of the chip idle on these short launches)
   if constexpr (std::is_same<OutT, bf16_t>::value && EPI != EPI_SWIGLU && EPI != EPI_SWIGLU_BWD) {
     if (a.goff && a.N <= 32 && a.tail == TAIL_NONE) {
-      if constexpr (DUAL) return launch_gm_ring<2, 1, 1, 2, BL, EPI>(a, rows_bound, stream);
-      else return launch_gm_ring<1, 1, 1, 1, BL, EPI>(a, rows_bound, stream);
+      // (a two-slot ring: fewer registers, three waves per SIMD instead of two; these short launches
+      // are latency-bound, and the extra waves took 1.5 us off each of the four)
+      if constexpr (DUAL) return launch_gm_ring<2, 1, 1, 2, BL, EPI, 2>(a, rows_bound, stream);
+      else return launch_gm_ring<1, 1, 1, 1, BL, EPI, 2>(a, rows_bound, stream);
     }
   }
   // grouped products without a LoRA tail and with wide outputs (merged-weight expert projections)
@@ -1335,7 +1336,7 @@ hipError_t launch_expert_projection(const GemmArgs& a, int b_layout, int epi, in
 }
 
 // Deep-prefetch kernel (grouped launches).
-template <int WM, int WN, int TM, int TN, int BL, int EPI>
+template <int WM, int WN, int TM, int TN, int BL, int EPI, int RS>
 hipError_t launch_gm_ring(const GemmArgs& a, int rows_bound, hipStream_t stream) {
   constexpr bool DUAL = (EPI == EPI_DUAL || EPI == EPI_SWIGLU);
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32, BNH = DUAL ? BN / 2 : BN;
@@ -1353,7 +1354,7 @@ hipError_t launch_gm_ring(const GemmArgs& a, int rows_bound, hipStream_t stream)
   const long blocks = (units + 7) / 8 * 8;
   const int* tmap = a.tmap_all + tile_map_offset(tidx, rows_bound, a.G);
   if (a.nbatch > 2 || (a.nbatch == 2 && (!a.bA || !a.bB || !a.bC))) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gm_ring<WM, WN, TM, TN, BL, EPI>), dim3((unsigned)blocks, a.nbatch == 2 ? 2u : 1u),
+  hipLaunchKernelGGL((gm_ring<WM, WN, TM, TN, BL, EPI, RS>), dim3((unsigned)blocks, a.nbatch == 2 ? 2u : 1u),
                      dim3(WM * WN * 64), 0, stream, a, tidx, tmap);
   return hipGetLastError();
 }
