@@ -1290,14 +1290,15 @@ hipError_t launch_gm_ring(const GemmArgs& a, int rows_bound, hipStream_t stream)
 template <int BL, int EPI, typename OutT>
 hipError_t dispatch_gm_mfma(const GemmArgs& a, int rows_bound, hipStream_t stream) {
   constexpr bool DUAL = (EPI == EPI_DUAL || EPI == EPI_SWIGLU);
-  // grouped low-rank products (N <= 32, bf16 out): 32- and 64-row tiles give ~P/32 and ~P/64
-  // workgroups (the 128-row skinny tiles leave most of the chip idle on these short launches)
+  // grouped low-rank products (N <= 32, bf16 out): 64-row tiles of two waves, ~P/64 workgroups (the
+  // 128-row skinny tiles leave most of the chip idle on these short launches; 32-row tiles of one wave
+  // were 1-2 us slower on each launch)
   if constexpr (std::is_same<OutT, bf16_t>::value && EPI != EPI_SWIGLU && EPI != EPI_SWIGLU_BWD) {
     if (a.goff && a.N <= 32 && a.tail == TAIL_NONE) {
       // (a two-slot ring: fewer registers, three waves per SIMD instead of two; these short launches
       // are latency-bound, and the extra waves took 1.5 us off each of the four)
       if constexpr (DUAL) return launch_gm_ring<2, 1, 1, 2, BL, EPI, 2>(a, rows_bound, stream);
-      else return launch_gm_ring<1, 1, 1, 1, BL, EPI, 2>(a, rows_bound, stream);
+      else return launch_gm_ring<2, 1, 1, 1, BL, EPI, 2>(a, rows_bound, stream);
     }
   }
   // grouped products without a LoRA tail and with wide outputs (merged-weight expert projections)
