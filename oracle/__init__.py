@@ -33,7 +33,8 @@ import numpy as np
 __all__ = [
     "router_logits", "nan_as_neg_inf", "topk_experts", "routing_weights", "group_by_expert", "route",
     "silu", "expert_rows_forward", "expert_rows_backward", "forward", "router_backward",
-    "backward", "forward_tokens", "backward_tokens", "token_outputs", "backward_expert", "fused_gate_up_pair",
+    "backward", "forward_tokens", "backward_tokens", "token_outputs", "backward_expert", "merged_weights",
+    "fused_gate_up_pair",
     "fused_gate_up_grads", "shared_expert_forward", "shared_expert_backward",
 ]
 
@@ -254,6 +255,21 @@ def forward(X, W: dict, rt: dict, alpha: float, r: int, keep: bool = True, rslor
         Y += w[:, j:j + 1] * o[inv[tok * k + j]]
     saved["o"] = o
     return Y, saved
+
+
+def merged_weights(W: dict, alpha: float, r: int, rslora: bool = False) -> dict:
+    """The materialised PEFT weights W + c A B of every expert: the dense form against which the pages
+    set the Split-LoRA evaluation order ([ALK] section "2. Split LoRA Associative Transformation";
+    the scale c is lora_scale's). Gate columns first, as in W_gu. With one fused gate/up pair
+    (A_u and B_u absent) the update is c A_g B_g over all 2n columns ([UNS] section "Faster LoRA MoE
+    training"). Returns fp64 {"W_gu": [E, m, 2n], "W_d": [E, n, m]}.
+    """
+    c = lora_scale(alpha, r, rslora)
+    if W.get("A_u") is None:
+        d_gu = _f64(W["A_g"]) @ _f64(W["B_g"])
+    else:
+        d_gu = np.concatenate([_f64(W["A_g"]) @ _f64(W["B_g"]), _f64(W["A_u"]) @ _f64(W["B_u"])], axis=-1)
+    return {"W_gu": _f64(W["W_gu"]) + c * d_gu, "W_d": _f64(W["W_d"]) + c * (_f64(W["A_d"]) @ _f64(W["B_d"]))}
 
 
 def fused_gate_up_pair(A, B) -> dict:

@@ -205,10 +205,9 @@ def test_merged_weights_forward(name, out_in, cuda):
                    d["B_d"], Wm_gu, Wm_d)
     torch.cuda.synchronize()
     W = host_weights(inp)
-    c = cfg.alpha / cfg.r
     n = cfg.n
-    ref_gu = W["W_gu"] + c * np.concatenate([W["A_g"] @ W["B_g"], W["A_u"] @ W["B_u"]], axis=2)
-    ref_d = W["W_d"] + c * W["A_d"] @ W["B_d"]
+    ref = oracle.merged_weights(W, cfg.alpha, cfg.r)
+    ref_gu, ref_d = ref["W_gu"], ref["W_d"]
     got_gu, got_d = np64(Wm_gu), np64(Wm_d)
     if out_in:
         got_gu, got_d = got_gu.transpose(0, 2, 1), got_d.transpose(0, 2, 1)
@@ -244,8 +243,8 @@ def test_merged_weights_fused_gate_up(out_in, cuda):
                    Wm_gu, Wm_d)
     torch.cuda.synchronize()
     W = oracle_weights(inp, flags)
-    c = cfg.alpha / cfg.r
-    ref_gu = np64(inp["W_gu"]) + c * np64(inp["A_g"]) @ np64(inp["B_g"])
+    ref_gu = oracle.merged_weights({key: (np64(v) if v is not None else None) for key, v in inp.items()},
+                                   cfg.alpha, cfg.r)["W_gu"]
     got_gu = np64(Wm_gu)
     if out_in:
         got_gu = got_gu.transpose(0, 2, 1)

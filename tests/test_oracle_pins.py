@@ -232,6 +232,28 @@ def test_split_lora_equals_dense_merge_and_per_token_loop(score):
     np.testing.assert_allclose(Y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
 
 
+@pytest.mark.parametrize("rslora", [False, True], ids=["alpha_over_r", "rslora"])
+def test_merged_weights_give_the_split_lora_forward(rslora):
+    """merged_weights (the materialised W + c A B) against the Split-LoRA forward: the layer on the
+    merged weights with zero low-rank factors equals the layer on the split weights (associativity of
+    X W + c (X A) B), for the per-projection pairs and for one fused gate/up pair."""
+    rng = np.random.default_rng(12)
+    s, m, n, E, k, r, alpha = 31, 16, 8, 5, 2, 3, 6.0
+    X, W_r, W, _ = _rand_layer(rng, s, m, n, E, k, r)
+    rt = oracle.route(oracle.router_logits(X, W_r), k, E)
+    for Wsplit in (W, dict(W, **oracle.fused_gate_up_pair(W["A_g"], np.concatenate([W["B_g"], W["B_u"]], axis=-1)))):
+        Y, _ = oracle.forward(X, Wsplit, rt, alpha, r, keep=False, rslora=rslora)
+        if Wsplit is W:
+            Wm = oracle.merged_weights(W, alpha, r, rslora)
+        else:  # the fused pair given as one [m, r] x [r, 2n] product
+            Wm = oracle.merged_weights(dict(W, A_u=None, B_u=None,
+                                            B_g=np.concatenate([W["B_g"], W["B_u"]], axis=-1)), alpha, r, rslora)
+        zero = {key: np.zeros_like(W[key]) for key in ("A_g", "B_g", "A_u", "B_u", "A_d", "B_d")}
+        Ym, _ = oracle.forward(X, dict(zero, W_gu=Wm["W_gu"], W_d=Wm["W_d"]), rt, alpha, r, keep=False,
+                               rslora=rslora)
+        np.testing.assert_allclose(Ym, Y, rtol=1e-12, atol=1e-12 * np.abs(Y).max())
+
+
 def test_rslora_scale_is_alpha_over_sqrt_r():
     """Rank-stabilised LoRA (bluecore.net/archives/629, LoRA section, rsLoRA item) scales the
     low-rank update by alpha/sqrt(r): the forward equals the dense merge with that scale, and the
