@@ -1043,6 +1043,10 @@ void gk_mfma(const GkLaunch L, const int* toffc, const int* tmapc) {
           k0 + row < ke ? rb[u] : zero;
     }
   };
+  // A job whose output is stored transposed (ctrans) multiplies with the operands swapped, so that
+  // its accumulators hold the transposed tile: lane l then holds output column l of the stored
+  // layout, and each store instruction writes whole rows of it.
+  const bool ct = a.ctrans != 0;
   auto compute = [&](const bf16_t* sA) {
     const bf16_t* sB = sA + A_ELEMS;
 #pragma unroll
@@ -1056,7 +1060,8 @@ void gk_mfma(const GkLaunch L, const int* toffc, const int* tmapc) {
       for (int tm = 0; tm < TM; tm++)
 #pragma unroll
         for (int tn = 0; tn < TN; tn++)
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[tm], fb[tn], acc[tm][tn], 0, 0, 0);
+          acc[tm][tn] = ct ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[tn], fa[tm], acc[tm][tn], 0, 0, 0)
+                           : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[tm], fb[tn], acc[tm][tn], 0, 0, 0);
     }
   };
 
@@ -1097,11 +1102,14 @@ void gk_mfma(const GkLaunch L, const int* toffc, const int* tmapc) {
     for (int tn = 0; tn < TN; tn++)
 #pragma unroll
       for (int v = 0; v < 16; v++) {
-        const int row = mt * BM + wm * TM * 32 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        const int col = nt * BN + wn * TN * 32 + tn * 32 + (lane & 31);
+        // accumulator element v of this lane: (row, col) of C, or (col, row) with the swapped operands
+        const int vr = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), vl = lane & 31;
+        const int row = mt * BM + wm * TM * 32 + tm * 32 + (ct ? vl : vr);
+        const int col = nt * BN + wn * TN * 32 + tn * 32 + (ct ? vr : vl);
         if (row >= a.M || col >= a.N) continue;
         if (nch == 1) gk_store(a, e, row, col, a.scale * acc[tm][tn][v]);
-        else a.gkpart[((long)u0 * a.M + row) * a.N + col] = acc[tm][tn][v];
+        else if (ct) a.gkpart[(long)u0 * a.M * a.N + (long)col * a.M + row] = acc[tm][tn][v];  // [N][M]
+        else a.gkpart[((long)u0 * a.M + row) * a.N + col] = acc[tm][tn][v];                     // [M][N]
       }
 }
 
@@ -1123,7 +1131,10 @@ __global__ __launch_bounds__(256) void gk_reduce(GkJobs jobs, const int* toffc) 
     for (long idx = (long)blockIdx.x * 256 + threadIdx.x; idx < MN; idx += (long)gridDim.x * 256) {
       float v = 0.0f;
       for (int c = 0; c < nch; c++) v += a.gkpart[(long)(c0 + c) * MN + idx];
-      gk_store(a, e, (int)(idx / a.N), (int)(idx % a.N), a.scale * v);
+      // partials of a transposed-store job are laid out [N][M], so consecutive threads store
+      // consecutive addresses in either case
+      if (a.ctrans) gk_store(a, e, (int)(idx % a.M), (int)(idx / a.M), a.scale * v);
+      else gk_store(a, e, (int)(idx / a.N), (int)(idx % a.N), a.scale * v);
     }
   }
 }
