@@ -425,6 +425,12 @@ __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_b
 template <int N_>
 using IC = std::integral_constant<int, N_>;
 
+// Whether a gm_ring configuration runs persistent workgroups (one per CU, each taking units in turn):
+// the 8-wave tiles on the two-slot ring, except the SwiGLU backward, whose epilogue inputs leave no
+// registers for the unit loop.
+template <int NW, int RS, int EPI>
+constexpr bool ring_persist() { return RS == 2 && NW == 8 && EPI != EPI_SWIGLU_BWD; }
+
 template <int WM, int WN, int TM, int TN, int BL, int EPI, int RS>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(RS == 4 || WM * WN >= 8 ? 2 : 3, RS == 4 || WM * WN >= 8 ? 2 : 3)))
 void gm_ring(GemmArgs a, int tidx, const int* tmap) {
@@ -456,58 +462,79 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
     a.C = a.bC;
   }
 
-  // ---- which (group, row tile, column tile)
+  // ---- work units (group, row tile, column tile). Unit p of XCD x's contiguous range of units goes to
+  //      the workgroups of that XCD (blockIdx % 8 == x), so the units in flight on an XCD are
+  //      consecutive: an expert's row and column tiles share its L2. Persistent configurations run a
+  //      grid of one workgroup per CU, each taking its XCD's units in turn; the others run one unit
+  //      per workgroup.
+  constexpr bool PERSIST = ring_persist<NW, RS, EPI>();
   const int tilesN = (a.N + BNH - 1) / BNH;
   const int* toff = a.toff_all + tidx * (a.G + 1);
-  const int T = xcd_unit(toff[a.G] * tilesN);
-  if (T < 0) return;
-  const int e = tmap[T / tilesN];  // row tiles of group e are [toff[e], toff[e+1])
-  const int nte = toff[e + 1] - toff[e];
-  const int local = T - toff[e] * tilesN;
-  const int nt = local / nte;
-  const int row0 = a.goff[e] + (local - nt * nte) * BM;
-  const int row_end = a.goff[e + 1];
-  const int j0 = nt * BNH;
+  const int total = toff[a.G] * tilesN;
+  const int per = (total + 7) >> 3;    // units of each XCD
+  const int xbase = (blockIdx.x & 7) * per;
+  const int wstride = gridDim.x >> 3;  // workgroups of each XCD (the grid is a multiple of 8)
+  int pos = blockIdx.x >> 3;
+  auto unit_at = [&](int p) { return (p < per && xbase + p < total) ? xbase + p : -1; };
+  const int T0 = unit_at(pos);
+  if (T0 < 0) return;
 
+  // a unit: its group, rows and column tile, and the source row of each A chunk this thread moves
+  struct Unit {
+    int e, row0, row_end, j0;
+    int asrow[A_CPT];
+  };
+  auto meta = [&](int t, Unit& U) {
+    const int e = tmap[t / tilesN];  // row tiles of group e are [toff[e], toff[e+1])
+    const int nte = toff[e + 1] - toff[e];
+    const int local = t - toff[e] * tilesN;
+    const int nt = local / nte;
+    U.e = e;
+    U.row0 = a.goff[e] + (local - nt * nte) * BM;
+    U.row_end = a.goff[e + 1];
+    U.j0 = nt * BNH;
+#pragma unroll
+    for (int u = 0; u < A_CPT; u++) {
+      const int row = min(U.row0 + (tid + u * NT) / CPR_A, U.row_end - 1);
+      U.asrow[u] = a.arow ? a.arow[row] : row;  // (divided by arow_div where used)
+    }
+  };
   // ---- source of every 16-byte chunk this thread moves; LDS chunk position P of a tile holds
   //      global chunk (P mod CPR) ^ swizzle(row)
   const bf16_t* asrc[A_CPT];
-#pragma unroll
-  for (int u = 0; u < A_CPT; u++) {
-    const int P = tid + u * NT;
-    const int x = P / CPR_A, q = (P % CPR_A) ^ swz_xk<CPR_A>(x);
-    const int row = min(row0 + x, row_end - 1);
-    const int src = a.arow ? a.arow[row] / a.arow_div : row;
-    asrc[u] = (const bf16_t*)a.A + (long)src * a.lda + q * 8;
-  }
-  const bf16_t* Bg = (const bf16_t*)a.B + (long)e * a.bstride;
-  const bf16_t* Bug = DUAL ? (const bf16_t*)a.Bu + (long)e * a.bstride : Bg;
   const bf16_t* bsrc[B_CPT];
+  auto point = [&](const Unit& U) {
 #pragma unroll
-  for (int u = 0; u < B_CPT; u++) {
-    const int P = tid + u * NT;
-    if constexpr (BL == LAYOUT_KX) {
-      const int k = P / CPR_B, x = ((P % CPR_B) ^ swz_kx<CPR_B>(k)) * 8;
-      const int half = DUAL ? (x >= BNH) : 0;
-      const int jj = min(j0 + x - half * BNH, a.N - 8);
-      bsrc[u] = (half ? Bug : Bg) + (long)k * a.ldb + jj;
-    } else {
-      const int x = P / CPR_B, q = (P % CPR_B) ^ swz_xk<CPR_B>(x);
-      const int half = DUAL ? (x >= BNH) : 0;
-      const int jj = min(j0 + x - half * BNH, a.N - 1);
-      bsrc[u] = (half ? Bug : Bg) + (long)jj * a.ldb + q * 8;
+    for (int u = 0; u < A_CPT; u++) {
+      const int P = tid + u * NT;
+      const int x = P / CPR_A, q = (P % CPR_A) ^ swz_xk<CPR_A>(x);
+      const int src = a.arow ? U.asrow[u] / a.arow_div : U.asrow[u];
+      asrc[u] = (const bf16_t*)a.A + (long)src * a.lda + q * 8;
     }
-  }
+    const bf16_t* Bg = (const bf16_t*)a.B + (long)U.e * a.bstride;
+    const bf16_t* Bug = DUAL ? (const bf16_t*)a.Bu + (long)U.e * a.bstride : Bg;
+#pragma unroll
+    for (int u = 0; u < B_CPT; u++) {
+      const int P = tid + u * NT;
+      if constexpr (BL == LAYOUT_KX) {
+        const int k = P / CPR_B, x = ((P % CPR_B) ^ swz_kx<CPR_B>(k)) * 8;
+        const int half = DUAL ? (x >= BNH) : 0;
+        const int jj = min(U.j0 + x - half * BNH, a.N - 8);
+        bsrc[u] = (half ? Bug : Bg) + (long)k * a.ldb + jj;
+      } else {
+        const int x = P / CPR_B, q = (P % CPR_B) ^ swz_xk<CPR_B>(x);
+        const int half = DUAL ? (x >= BNH) : 0;
+        const int jj = min(U.j0 + x - half * BNH, a.N - 1);
+        bsrc[u] = (half ? Bug : Bg) + (long)jj * a.ldb + q * 8;
+      }
+    }
+  };
   const long bstep = (BL == LAYOUT_KX) ? (long)BKT * a.ldb : (long)BKT;  // source advance per tile
+  Unit cur;
+  meta(T0, cur);
+  point(cur);
 
   f32x16_t acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; i++)
-#pragma unroll
-    for (int j = 0; j < TN; j++)
-#pragma unroll
-      for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
-
   i32x4_t ra[RS][A_CPT], rb[RS][B_CPT];  // register ring: slot = tile % RS
   auto load = [&](i32x4_t(&da)[A_CPT], i32x4_t(&db)[B_CPT], int t) {
 #pragma unroll
@@ -594,7 +621,6 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
     constexpr int i = decltype(ic)::value;
     load(ra[i], rb[i], min(i, last));
   });
-  store(s0, ra[0], rb[0]);
   auto step = [&](auto slot_c, int kt) {
     constexpr int sl = decltype(slot_c)::value;       // kt % RS
     constexpr int nx = (sl + 1) % RS;                 // (kt + 1) % RS
@@ -612,6 +638,15 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
       });
     });
   };
+  for (;;) {  // the units of this workgroup
+#pragma unroll
+  for (int i = 0; i < TM; i++)
+#pragma unroll
+    for (int j = 0; j < TN; j++)
+#pragma unroll
+      for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
+  const int e = cur.e, row0 = cur.row0, row_end = cur.row_end, j0 = cur.j0;
+  store(s0, ra[0], rb[0]);
   // whole groups of RS steps run unguarded (the same loads in flight on every path into the loop
   // head), the last nk % RS steps after the loop
   int kt = 0;
@@ -621,6 +656,16 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
   static_for<RS - 1>([&](auto ic) {
     if (kt + decltype(ic)::value < nk) step(ic, kt + decltype(ic)::value);
   });
+  // the workgroup's next unit: its group offsets and gathered row indices load while this unit's tail
+  // is fetched (or right away, without a tail); its first RS tiles after this unit's stores (loading
+  // them before the stores, with the ring live through the epilogue, made these kernels spill)
+  int Tn = -1;
+  Unit nxt;
+  if constexpr (PERSIST) {
+    pos += wstride;
+    Tn = unit_at(pos);
+    if (a.tail == TAIL_NONE && Tn >= 0) meta(Tn, nxt);
+  }
 
   // ---- epilogue (after the tail): each wave stages its fp32 accumulators in its own LDS region, then writes whole
   //      16-byte row chunks (8 columns). Staged row r keeps its 4-float groups XOR-permuted by one
@@ -724,6 +769,9 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
         }
         okb[u] = src != nullptr;
         vb[u] = ld16(okb[u] ? src : T0);  // T0: the first chunk of this expert's factor
+      }
+      if constexpr (PERSIST) {
+        if (ts == 0 && Tn >= 0) meta(Tn, nxt);
       }
 #pragma unroll
       for (int u = 0; u < A_CPT; u++)
@@ -873,6 +921,16 @@ void gm_ring(GemmArgs a, int tidx, const int* tmap) {
       }
     }
   }
+  if constexpr (!PERSIST) break;
+  if (Tn < 0) break;
+  point(nxt);
+  static_for<RS>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    load(ra[i], rb[i], min(i, last));
+  });
+  lds_barrier();  // every wave has read its staged results back before stage 0 is refilled
+  cur = nxt;
+  }  // units of this workgroup
 }
 
 // Stores element (row, col) of group e's K-grouped output.
@@ -1368,7 +1426,14 @@ hipError_t launch_gm_ring(const GemmArgs& a, int rows_bound, hipStream_t stream)
   const long tilesN = (a.N + BNH - 1) / BNH;
   const long units = ((long)rows_bound / BM + a.G) * tilesN;
   if (units <= 0) return hipSuccess;
-  const long blocks = (units + 7) / 8 * 8;
+  long blocks = (units + 7) / 8 * 8;
+  if (ring_persist<WM * WN, RS, EPI>()) {  // workgroups that take their units in turn: one per CU
+    int dev = 0, cus = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess) return err;
+    blocks = std::min(blocks, std::max(8L, (long)cus / 8 * 8));
+  }
   const int* tmap = a.tmap_all + tile_map_offset(tidx, rows_bound, a.G);
   if (a.nbatch > 2 || (a.nbatch == 2 && (!a.bA || !a.bB || !a.bC))) return hipErrorInvalidValue;
   hipLaunchKernelGGL((gm_ring<WM, WN, TM, TN, BL, EPI, RS>), dim3((unsigned)blocks, a.nbatch == 2 ? 2u : 1u),
