@@ -41,18 +41,20 @@ struct RouteState {
   void* wr_pad;  // bf16 with E % 8 != 0: W_r with rows padded to E8 columns (zeros past E)
 };
 
-// K splits of the router-logit GEMM: enough workgroups to fill the chip, chunks of >= 256.
-// K splits of the router-logit GEMM (64 x 128 tiles): enough workgroups for the chip (about 256), each
-// split at least 256 long; every split adds s x E fp32 partials that top-k reads back.
+// K splits of the router-logit GEMM (64 x 128 tiles): the most splits that divide its K tiles into
+// chunks of at least 256 with at most 512 workgroups (two per CU), so that each workgroup's chain of
+// K tiles is short; every split adds s x E fp32 partials that top-k reads back.
 // W_r's rows padded to a multiple of 8 columns (16 bytes of bf16) for the router GEMM's chunk loads
 inline int router_cols(const moe_shape& s) { return (s.E + 7) & ~7; }
 inline bool router_padded(const moe_shape& s) { return s.dtype == MOE_DTYPE_BF16 && s.E % 8 != 0; }
 
 inline int route_ksplit(const moe_shape& s) {
   const long tiles = ((long)s.s + 63) / 64 * (((long)s.E + 127) / 128);
-  int n = 1;
-  while (n < 8 && tiles * n < 256 && (s.m % (2 * n * 256)) == 0) n *= 2;
-  return n;
+  const int kt = s.m / 64;  // K tiles (m is a multiple of 64)
+  int best = 1;
+  for (int n = 2; n <= 16; n++)
+    if (kt % n == 0 && s.m / n >= 256 && tiles * n <= 512) best = n;
+  return best;
 }
 
 struct FwdBufs {
