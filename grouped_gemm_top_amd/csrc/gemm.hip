@@ -426,8 +426,8 @@ template <int N_>
 using IC = std::integral_constant<int, N_>;
 
 // Whether a gm_ring configuration runs persistent workgroups (one per CU, each taking units in turn):
-// the 8-wave tiles on the two-slot ring, except the SwiGLU backward, whose epilogue inputs leave no
-// registers for the unit loop.
+// the 8-wave tiles on the two-slot ring, except the SwiGLU backward, whose saved gate/up inputs leave
+// too few registers for the unit loop (made to fit, it was no faster).
 template <int NW, int RS, int EPI>
 constexpr bool ring_persist() { return RS == 2 && NW == 8 && EPI != EPI_SWIGLU_BWD; }
 
