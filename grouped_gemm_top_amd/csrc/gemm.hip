@@ -63,12 +63,12 @@ __device__ inline int xcd_unit(int total) {
 // ------------------------------------------------------------------------------------------------
 // Row-grouped MFMA GEMM.
 //
-// LDS tiles are unpadded and XOR-swizzled at 16-byte-chunk granularity so that global->LDS copies
-// can use gfx950's direct-to-LDS loads (global_load_lds_dwordx4: lane L of a wave instruction
-// writes the L-th 16-byte chunk of a contiguous 1 KB LDS span, so each lane fetches whichever global
-// chunk belongs at that position). Tiles whose reduction axis is contiguous hold 8 chunks per row
-// (BK = 64) with chunk q of row x at q ^ swz_xk(x); tiles whose output axis is contiguous hold
-// BN/8 chunks per row with chunk q of row k at q ^ swz_kx(k).
+// LDS tiles are unpadded and XOR-swizzled at 16-byte-chunk granularity: lane L of a copy instruction
+// writes the L-th 16-byte chunk of a contiguous 1 KB LDS span and fetches whichever global chunk
+// belongs at that position (the layout gfx950's direct-to-LDS loads would write; every kernel here
+// copies through registers with plain loads and ds_write). Tiles whose reduction axis is contiguous
+// hold 8 chunks per row (BK = 64) with chunk q of row x at q ^ swz_xk(x); tiles whose output axis
+// is contiguous hold BN/8 chunks per row with chunk q of row k at q ^ swz_kx(k).
 // XOR swizzles (measured conflict-free on gfx950, whose LDS serves 256 bytes per clock: 16 lanes per
 // cycle for ds_read_b128, 32 lanes per cycle for ds_read_b64_tr_b16).
 // XK tiles (CPR chunks per row): the 16 rows read together by one MFMA fragment must land on
