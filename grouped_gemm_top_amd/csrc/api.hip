@@ -565,23 +565,36 @@ static moe_status forward_experts(const moe_shape& s, const void* X, const Group
   return MOE_OK;
 }
 
-moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t* topk_idx,
-                            const float* topk_w, const int32_t* expert_off, const int32_t* perm,
-                            const int32_t* inv_perm, const void* route_state, const void* W_gu,
-                            const void* W_d, const void* A_g, const void* B_g, const void* A_u,
-                            const void* B_u, const void* A_d, const void* B_d, void* Y, void* saved,
-                            size_t saved_bytes, void* ws, size_t ws_bytes, void* stream) {
+// The routed forward's shape and every buffer but its workspaces (shared by both forward entry points).
+static moe_status forward_args(const moe_shape* shape, const void* X, const int32_t* topk_idx,
+                               const float* topk_w, const int32_t* expert_off, const int32_t* perm,
+                               const int32_t* inv_perm, const void* route_state, const void* W_gu,
+                               const void* W_d, const void* A_g, const void* B_g, const void* A_u,
+                               const void* B_u, const void* A_d, const void* B_d, const void* Y) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
   const moe_shape& s = *shape;
   const long P = pairs(s);
-  const size_t E = s.E, m = s.m, n = s.n, r = s.r;
+  const size_t E = s.E, m = s.m, n = s.n;
   if (!ptr_ok(X, (size_t)s.s * m) || !ptr_ok(topk_idx, P) || !ptr_ok(topk_w, P) ||
       !ptr_ok(expert_off, E + 1) || !ptr_ok(perm, P) || !ptr_ok(inv_perm, P) ||
       !ptr_ok(W_gu, E * m * 2 * n) || !ptr_ok(W_d, E * n * m) || !ptr_ok(Y, (size_t)s.s * m))
     return MOE_ERR_INVALID_ARG;
   if (!merged(s) && !lora_ptrs_ok(s, A_g, B_g, A_u, B_u, A_d, B_d)) return MOE_ERR_INVALID_ARG;
   if (!route_state || ((uintptr_t)route_state & 255u)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+moe_status moe_lora_forward(const moe_shape* shape, const void* X, const int32_t* topk_idx,
+                            const float* topk_w, const int32_t* expert_off, const int32_t* perm,
+                            const int32_t* inv_perm, const void* route_state, const void* W_gu,
+                            const void* W_d, const void* A_g, const void* B_g, const void* A_u,
+                            const void* B_u, const void* A_d, const void* B_d, void* Y, void* saved,
+                            size_t saved_bytes, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = forward_args(shape, X, topk_idx, topk_w, expert_off, perm, inv_perm, route_state, W_gu, W_d,
+                               A_g, B_g, A_u, B_u, A_d, B_d, Y);
+  if (st != MOE_OK) return st;
+  const moe_shape& s = *shape;
   // saved: gu, h and the low-rank products; ws: the expert outputs o (and, for inference, the rest)
   const size_t need_saved = fwd_layout(s, nullptr, nullptr, false);
   const size_t need_inter = saved ? o_bytes(s) : fwd_layout(s, nullptr, nullptr, true);
@@ -619,7 +632,9 @@ moe_status moe_lora_forward_noalloc(const moe_shape* shape, const void* X, const
                                     const void* W_d, const void* A_g, const void* B_g, const void* A_u,
                                     const void* B_u, const void* A_d, const void* B_d, void* Y,
                                     void* stream) {
-  moe_status st = check_shape(shape);
+  // arguments first: a call that is refused makes no runtime call at all
+  moe_status st = forward_args(shape, X, topk_idx, topk_w, expert_off, perm, inv_perm, route_state, W_gu, W_d,
+                               A_g, B_g, A_u, B_u, A_d, B_d, Y);
   if (st != MOE_OK) return st;
   const size_t need = moe_fwd_ws_bytes(shape, 0);
   if (need > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
