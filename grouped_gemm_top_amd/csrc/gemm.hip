@@ -13,6 +13,7 @@
 // and as a reference for the MFMA kernels.
 #include "gemm.h"
 #include <algorithm>
+#include <climits>
 #include <type_traits>
 
 namespace moe {
@@ -1231,12 +1232,25 @@ __global__ void gm_simt(GemmArgs a, int b_layout, int total_rows_bound) {
   const T* Ar = (const T*)a.A + src * a.lda;
   const T* Bg = (const T*)a.B + (long)e * a.bstride;
   const T* Bug = DUAL ? (const T*)a.Bu + (long)e * a.bstride : nullptr;
-  float acc0 = 0.0f, acc1 = 0.0f;
-  for (int k = 0; k < a.K; k++) {
-    const float x = to_f(Ar[k]);
-    acc0 += x * opv(Bg, b_layout, a.ldb, jj, k);
-    if (DUAL) acc1 += x * opv(Bug, b_layout, a.ldb, jj, k);
+  // four running sums over blocks of four K steps (the steps past the last whole block go to the first),
+  // added together at the end in that order, so that the loads of four steps are in flight together
+  float p0[4] = {0.0f, 0.0f, 0.0f, 0.0f}, p1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  int k = 0;
+  for (; k + 4 <= a.K; k += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const float x = to_f(Ar[k + u]);
+      p0[u] += x * opv(Bg, b_layout, a.ldb, jj, k + u);
+      if (DUAL) p1[u] += x * opv(Bug, b_layout, a.ldb, jj, k + u);
+    }
   }
+  for (; k < a.K; k++) {
+    const float x = to_f(Ar[k]);
+    p0[0] += x * opv(Bg, b_layout, a.ldb, jj, k);
+    if (DUAL) p1[0] += x * opv(Bug, b_layout, a.ldb, jj, k);
+  }
+  float acc0 = ((p0[0] + p0[1]) + p0[2]) + p0[3];
+  float acc1 = ((p1[0] + p1[1]) + p1[2]) + p1[3];
   if (a.tail != TAIL_NONE) {
     const int r2 = a.r2a;
     const T* TAr = (const T*)a.TA + (long)row * a.lda2;
@@ -1283,26 +1297,53 @@ __global__ void gm_simt(GemmArgs a, int b_layout, int total_rows_bound) {
   }
 }
 
+// K-grouped products on plain SIMT threads (fp32 layers and the reference mode): every job of a launch in
+// one grid. Block b belongs to job j when L.tiles_pre[j] <= b < L.tiles_pre[j + 1]; within the job, blocks
+// run over (group, output row, 64-column block), one thread per output element. Each thread reduces its
+// group's rows with four running sums over blocks of four rows (the last rows, past the last whole block,
+// go to the first sum), added together at the end in that order.
 template <typename T>
-__global__ void gk_simt(GemmArgs a) {
-  if (blockIdx.z >= (unsigned)a.G) {  // the second problem of a batched launch (groups G..2G-1)
-    a.A = a.bA;
-    a.B = a.bB;
-    a.C = a.bC;
+__global__ __launch_bounds__(64) void gk_simt(const GkLaunch L) {
+  const int b = blockIdx.x;
+  int j = 0, jbase = 0;
+#pragma unroll
+  for (int i = 1; i < kGkMaxJobs; i++) {  // (constant indices: see gk_job)
+    if (i < L.njobs && b >= L.tiles_pre[i]) {
+      j = i;
+      jbase = L.tiles_pre[i];
+    }
   }
-  const int e = (int)blockIdx.z - (blockIdx.z >= (unsigned)a.G ? a.G : 0), row = blockIdx.y;
-  int col = blockIdx.x * blockDim.x + threadIdx.x;
+  const GkJob a = gk_job(L.jobs, j);
+  const GemmArgs& g0 = L.jobs.job[0];  // the grouping, shared by every job
+  const int nb = (a.N + 63) / 64;
+  int local = b - jbase;
+  const int cb = local % nb;
+  local /= nb;
+  const int row = local % a.M, e = local / a.M;
+  int col = cb * 64 + (int)threadIdx.x;
   if (col >= a.N) return;
-  const int kb = a.goff[e], ke = a.goff[e + 1];
-  float acc = 0.0f;
-  for (int i = kb; i < ke; i++) {
+  const int kb = g0.goff[e], ke = g0.goff[e + 1];
+  const T* A = (const T*)a.A;
+  const T* B = (const T*)a.B;
+  auto term = [&](int i) {
     const long src = a.arow ? (long)(a.arow[i] / a.arow_div) : (long)i;
-    acc += to_f(((const T*)a.A)[src * a.lda + row]) * to_f(((const T*)a.B)[(long)i * a.ldb + col]);
+    return to_f(A[src * a.lda + row]) * to_f(B[(long)i * a.ldb + col]);
+  };
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  int i = kb;
+  for (; i + 4 <= ke; i += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; u++) acc[u] += term(i + u);
   }
+  for (; i < ke; i++) acc[0] += term(i);
+  const float v = ((acc[0] + acc[1]) + acc[2]) + acc[3];
   float* C = (float*)a.C;
-  if (a.C1 && col >= a.nsplit) { C = (float*)a.C1; col -= a.nsplit; }
+  if (a.C1 && col >= a.nsplit) {
+    C = (float*)a.C1;
+    col -= a.nsplit;
+  }
   C += (long)e * a.cstride;
-  C[a.ctrans ? (long)col * a.ldc + row : (long)row * a.ldc + col] = a.scale * acc;
+  C[a.ctrans ? (long)col * a.ldc + row : (long)row * a.ldc + col] = a.scale * v;
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -1512,17 +1553,23 @@ hipError_t gemm_gk_launch(const GemmArgs* jobs, int njobs, int dtype, int refere
       return hipErrorInvalidValue;
   }
   if (a0.G <= 0) return hipSuccess;
-  if (dtype == 0 || reference) {
-    for (int i = 0; i < njobs; i++) {
-      const GemmArgs& a = jobs[i];
-      if (a.M <= 0 || a.N <= 0) continue;
-      dim3 grid((a.N + 63) / 64, a.M, a.G);
-      if (dtype == 0) hipLaunchKernelGGL(gk_simt<float>, grid, dim3(64), 0, stream, a);
-      else hipLaunchKernelGGL(gk_simt<bf16_t>, grid, dim3(64), 0, stream, a);
-      const hipError_t err = hipGetLastError();
-      if (err != hipSuccess) return err;
+  if (dtype == 0 || reference) {  // every job in one launch of the SIMT kernel
+    GkLaunch L;
+    L.njobs = njobs;
+    L.tiles_pre[0] = 0;
+    long pre = 0;
+    for (int i = 0; i < kGkMaxJobs; i++) {
+      const GemmArgs& a = jobs[i < njobs ? i : 0];
+      L.jobs.job[i] = a;
+      if (i < njobs && a.M > 0 && a.N > 0) pre += (long)((a.N + 63) / 64) * a.M * a.G;
+      if (pre > INT_MAX) return hipErrorInvalidValue;
+      L.tiles_pre[i + 1] = (int)pre;
     }
-    return hipSuccess;
+    L.tiles_all = L.tiles_pre[njobs];
+    if (L.tiles_all <= 0) return hipSuccess;
+    if (dtype == 0) hipLaunchKernelGGL(gk_simt<float>, dim3((unsigned)L.tiles_all), dim3(64), 0, stream, L);
+    else hipLaunchKernelGGL(gk_simt<bf16_t>, dim3((unsigned)L.tiles_all), dim3(64), 0, stream, L);
+    return hipGetLastError();
   }
   // output rows = the wide dimension (m or n), output columns = the LoRA rank side
   constexpr int WM = 4, WN = 1, TM = 1, TN = 1;
